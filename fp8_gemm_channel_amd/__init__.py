@@ -1,0 +1,156 @@
+"""Python binding of libfp8g.so, the MI355X (gfx950) scaled FP8 GEMM.
+
+    y[m,n] = bf16_rne( (sum_k x[m,k] * w[n,k]) * scale[n] )
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in include/fp8g.h.  PyTorch supplies device memory and the current
+stream.  If libfp8g.so is missing this module raises ImportError; there is no
+fallback implementation.
+
+Entry points (same names as the C ABI):
+    fp8_gemm_scaled(x, w, scale, y, M, N, K, stream)        raw pointers
+    fp8_gemm_scaled_ex(..., path, variant, split_k, stream)  forced plan
+    fp8_gemm_plan(M, N, K) / fp8_gemm_plan_ex(...)           host-only planner
+    fp8_gemm_strerror(status), fp8_gemm_last_error()
+and the tensor-level convenience wrapper
+    fp8_gemm(x, w, scale, *, out=None, path=0, variant=0, split_k=0) -> y
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libfp8g.so")
+
+FP8G_OK = 0
+FP8G_ERR_INVALID_ARG = 1
+FP8G_ERR_UNSUPPORTED = 2
+FP8G_ERR_HIP = 3
+
+PATH_NONE, PATH_ZERO, PATH_MAIN, PATH_SPLITK = 0, 1, 2, 3
+PATH_NAMES = {PATH_NONE: "none", PATH_ZERO: "zero", PATH_MAIN: "main", PATH_SPLITK: "splitk"}
+
+#: Every symbol include/fp8g.h declares.
+EXPORTED_SYMBOLS = ("fp8_gemm_scaled", "fp8_gemm_scaled_ex", "fp8_gemm_plan", "fp8_gemm_plan_ex",
+                    "fp8_gemm_strerror", "fp8_gemm_last_error")
+
+
+class Plan(ctypes.Structure):
+    """Mirror of struct fp8g_plan."""
+
+    _fields_ = [("path", ctypes.c_int32), ("variant", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("k_slice", ctypes.c_int64), ("group_m", ctypes.c_int32), ("k_tail", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["path_name"] = PATH_NAMES.get(self.path, "?")
+        return d
+
+
+class Fp8gError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{fp8_gemm_strerror(status)}: {detail}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime with the same SONAME (libamdhip64.so.7).
+    # Importing torch first makes the loader bind libfp8g.so to that runtime
+    # instead of loading a second HIP/HSA runtime, which would not see the GPU.
+    import torch  # noqa: F401
+
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is not built; run `python -m fp8_gemm_channel_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIBRARY)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.fp8_gemm_scaled.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.fp8_gemm_scaled.restype = ctypes.c_int
+    lib.fp8_gemm_scaled_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    lib.fp8_gemm_scaled_ex.restype = ctypes.c_int
+    lib.fp8_gemm_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
+    lib.fp8_gemm_plan.restype = ctypes.c_int
+    lib.fp8_gemm_plan_ex.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(Plan)]
+    lib.fp8_gemm_plan_ex.restype = ctypes.c_int
+    lib.fp8_gemm_strerror.argtypes = [ctypes.c_int]
+    lib.fp8_gemm_strerror.restype = ctypes.c_char_p
+    lib.fp8_gemm_last_error.argtypes = []
+    lib.fp8_gemm_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+# ------------------------------------------------------------ raw C-ABI calls --
+def fp8_gemm_scaled(x: int, w: int, scale: int, y: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    """Direct call of the C entry point with device addresses; returns the status."""
+    return _lib.fp8_gemm_scaled(x, w, scale, y, M, N, K, stream)
+
+
+def fp8_gemm_scaled_ex(x: int, w: int, scale: int, y: int, M: int, N: int, K: int,
+                       path: int = 0, variant: int = 0, split_k: int = 0, stream: int = 0) -> int:
+    return _lib.fp8_gemm_scaled_ex(x, w, scale, y, M, N, K, path, variant, split_k, stream)
+
+
+def fp8_gemm_plan(M: int, N: int, K: int) -> dict:
+    return fp8_gemm_plan_ex(M, N, K)
+
+
+def fp8_gemm_plan_ex(M: int, N: int, K: int, path: int = 0, variant: int = 0, split_k: int = 0) -> dict:
+    p = Plan()
+    st = _lib.fp8_gemm_plan_ex(M, N, K, path, variant, split_k, ctypes.byref(p))
+    if st != FP8G_OK:
+        raise Fp8gError(st, fp8_gemm_last_error())
+    return p.as_dict()
+
+
+def fp8_gemm_strerror(status: int) -> str:
+    return _lib.fp8_gemm_strerror(status).decode()
+
+
+def fp8_gemm_last_error() -> str:
+    return _lib.fp8_gemm_last_error().decode()
+
+
+# ------------------------------------------------------------- tensor wrapper --
+def fp8_gemm(x, w, scale, *, out=None, path: int = 0, variant: int = 0, split_k: int = 0, stream=None):
+    """y = bf16((x @ w^T) * scale) on the GPU; returns a new [M, N] bfloat16 tensor
+    (or writes `out`).  x: [M,K], w: [N,K] float8_e4m3fn (or uint8 codes);
+    scale: [N] float32; all contiguous on the same CUDA/HIP device."""
+    import torch
+
+    def codes(t, name):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError(f"{name} must be float8_e4m3fn (or uint8 E4M3 codes), got {t.dtype}")
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 2-d tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+        return t
+
+    x = codes(x, "x")
+    w = codes(w, "w")
+    if scale.dtype != torch.float32 or scale.dim() != 1 or not scale.is_contiguous() or not scale.is_cuda:
+        raise TypeError("scale must be a contiguous 1-d float32 GPU tensor")
+    M, K = x.shape
+    N, K2 = w.shape
+    if K2 != K or scale.numel() != N:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w {tuple(w.shape)}, scale {tuple(scale.shape)}")
+    if not (x.device == w.device == scale.device):
+        raise ValueError("x, w and scale must be on the same device")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] bfloat16 tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        st = _lib.fp8_gemm_scaled_ex(x.data_ptr(), w.data_ptr(), scale.data_ptr(), out.data_ptr(),
+                                     M, N, K, path, variant, split_k, stream.cuda_stream)
+    if st != FP8G_OK:
+        raise Fp8gError(st, fp8_gemm_last_error())
+    return out

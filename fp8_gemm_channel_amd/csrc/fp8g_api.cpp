@@ -1,0 +1,224 @@
+// fp8g_api.cpp -- C ABI of libfp8g.so: argument checks, the launch planner and
+// the entry points declared in include/fp8g.h.
+//
+// The planner picks a path by the M regime, as the pages' kernels do: the
+// decode-shaped M (a handful of rows) is memory-bound and runs as split-K over
+// the streamed weight ("Claude Fable 5", Triton split-K cell, for M <= 64;
+// "Kimi K3 (256k)", SM90 WGMMA and SM120 cells, skinny split-K paths), and
+// everything else runs as one tiled MFMA kernel whose tile shrinks for small
+// problems so the launch still fills the chip.  Configurations are fixed per
+// shape class, never tuned at run time ("GLM-5.2", B200 TMA Triton cell and
+// single-Triton-kernel cell: pinned per-regime configs).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fp8g.h"
+#include "fp8g_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(FP8G_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+constexpr int kNumCUs = 256;          // MI355X compute units
+constexpr int kSkinnyMaxM = 64;       // skinny path handles M <= 64
+constexpr int kMaxSplit = 64;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_dims(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return fail(FP8G_ERR_INVALID_ARG, "negative dimension (M=%lld N=%lld K=%lld)",
+                                           (long long)M, (long long)N, (long long)K);
+  if (M > FP8G_MAX_MN || N > FP8G_MAX_MN)
+    return fail(FP8G_ERR_INVALID_ARG, "M or N above %lld", (long long)FP8G_MAX_MN);
+  if (K > FP8G_MAX_K) return fail(FP8G_ERR_INVALID_ARG, "K=%lld above %lld", (long long)K, (long long)FP8G_MAX_K);
+  return FP8G_OK;
+}
+
+// Main-path configuration for (M, N) when not forced: the largest tile whose
+// grid still gives every compute unit a workgroup.
+int auto_main_variant(int64_t M, int64_t N) {
+  if (cdiv(M, 256) * cdiv(N, 256) >= kNumCUs) return 1;
+  if (cdiv(M, 128) * cdiv(N, 128) >= kNumCUs / 2) return 2;
+  return 3;
+}
+
+int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, int32_t split_k, fp8g_plan *p) {
+  if (!p) return fail(FP8G_ERR_INVALID_ARG, "plan output pointer is null");
+  int st = check_dims(M, N, K);
+  if (st) return st;
+  memset(p, 0, sizeof *p);
+  p->split_k = 1;
+  p->k_slice = K;
+  if (path != 0 && path != FP8G_PATH_MAIN && path != FP8G_PATH_SPLITK)
+    return fail(FP8G_ERR_INVALID_ARG, "unknown path override %d", path);
+  if (split_k < 0 || split_k > kMaxSplit) return fail(FP8G_ERR_INVALID_ARG, "split_k=%d outside 0..%d", split_k, kMaxSplit);
+  if (variant < 0) return fail(FP8G_ERR_INVALID_ARG, "negative variant %d", variant);
+  if (M == 0 || N == 0) {
+    p->path = FP8G_PATH_NONE;
+    return FP8G_OK;
+  }
+  if (K == 0) {
+    p->path = FP8G_PATH_ZERO;
+    p->grid = 1;
+    return FP8G_OK;
+  }
+  if (path == 0) path = (M <= kSkinnyMaxM) ? FP8G_PATH_SPLITK : FP8G_PATH_MAIN;
+  if (path == FP8G_PATH_SPLITK) {
+    if (M > kSkinnyMaxM) return fail(FP8G_ERR_INVALID_ARG, "split-K path needs M <= %d (M=%lld)", kSkinnyMaxM, (long long)M);
+    if (variant == 0) variant = 1;
+    const fp8g::SkinnyConfig *c = fp8g::skinny_config(variant);
+    if (!c) return fail(FP8G_ERR_INVALID_ARG, "unknown split-K variant %d", variant);
+    const int64_t tile_n = fp8g::skinny_tile_n(*c);
+    const int64_t col_blocks = cdiv(N, tile_n);
+    const int64_t chunk = fp8g::skinny_chunk_bytes();
+    int64_t S = split_k;
+    if (S == 0) {
+      // Enough workgroups to cover every compute unit twice, while each slice
+      // keeps at least 1 KiB of K.
+      S = 1;
+      while (S < kMaxSplit && col_blocks * S < 2 * kNumCUs && K / (2 * S) >= 1024) S *= 2;
+    }
+    int64_t k_slice = cdiv(cdiv(K, S), chunk) * chunk;
+    S = cdiv(K, k_slice);  // no empty slices
+    p->path = FP8G_PATH_SPLITK;
+    p->variant = variant;
+    p->tile_m = M > 32 ? 64 : 32;
+    p->tile_n = (int32_t)tile_n;
+    p->tile_k = (int32_t)chunk;
+    p->split_k = (int32_t)S;
+    p->k_slice = k_slice;
+    p->k_tail = (K % chunk) != 0;
+    p->grid = col_blocks * S;
+    p->workspace_bytes = S > 1 ? S * M * N * (int64_t)sizeof(float) : 0;
+    return FP8G_OK;
+  }
+  if (split_k > 1) return fail(FP8G_ERR_INVALID_ARG, "split_k applies to the split-K path only");
+  if (variant == 0) variant = auto_main_variant(M, N);
+  const fp8g::MainConfig *c = fp8g::main_config(variant);
+  if (!c) return fail(FP8G_ERR_INVALID_ARG, "unknown main variant %d", variant);
+  const int64_t tiles_m = cdiv(M, c->bm), tiles_n = cdiv(N, c->bn);
+  if (tiles_m * tiles_n > INT32_MAX) return fail(FP8G_ERR_UNSUPPORTED, "too many tiles");
+  p->path = FP8G_PATH_MAIN;
+  p->variant = variant;
+  p->tile_m = c->bm;
+  p->tile_n = c->bn;
+  p->tile_k = c->bk;
+  p->group_m = (int32_t)(tiles_m < 8 ? tiles_m : 8);
+  p->k_tail = (K % c->bk) != 0;
+  p->grid = tiles_m * tiles_n;
+  return FP8G_OK;
+}
+
+bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+int run(const void *x, const void *w, const float *scale, void *y, int64_t M, int64_t N, int64_t K, int32_t path,
+        int32_t variant, int32_t split_k, void *stream_ptr) {
+  g_last_error.clear();
+  fp8g_plan p;
+  int st = plan_impl(M, N, K, path, variant, split_k, &p);
+  if (st) return st;
+  if (p.path == FP8G_PATH_NONE) return FP8G_OK;
+  if (!y) return fail(FP8G_ERR_INVALID_ARG, "y is null");
+  if (!scale) return fail(FP8G_ERR_INVALID_ARG, "scale is null");
+  if (K > 0 && (!x || !w)) return fail(FP8G_ERR_INVALID_ARG, "x or w is null");
+  if ((uintptr_t)scale % 4) return fail(FP8G_ERR_INVALID_ARG, "scale is not 4-byte aligned");
+  if ((uintptr_t)y % 2) return fail(FP8G_ERR_INVALID_ARG, "y is not 2-byte aligned");
+  const size_t ybytes = (size_t)M * (size_t)N * 2;
+  if (overlaps(y, ybytes, x, (size_t)M * (size_t)K) || overlaps(y, ybytes, w, (size_t)N * (size_t)K) ||
+      overlaps(y, ybytes, scale, (size_t)N * 4))
+    return fail(FP8G_ERR_INVALID_ARG, "y overlaps an input");
+
+  hipStream_t stream = (hipStream_t)stream_ptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+
+  const bool vec = (N % 4 == 0) && ((uintptr_t)y % 8 == 0);
+  if (p.path == FP8G_PATH_ZERO) {
+    e = fp8g::launch_zero((uint16_t *)y, M * N, stream);
+    return e == hipSuccess ? FP8G_OK : hip_fail(e, "zero-fill launch");
+  }
+  if (p.path == FP8G_PATH_MAIN) {
+    fp8g::MainLaunch l{(const uint8_t *)x, (const uint8_t *)w, scale, (uint16_t *)y, (int)M, (int)N, (int)K,
+                       (int)cdiv(M, p.tile_m), (int)cdiv(N, p.tile_n), p.group_m, p.variant, p.k_tail != 0, vec};
+    e = fp8g::launch_main(l, stream);
+    return e == hipSuccess ? FP8G_OK : hip_fail(e, "main kernel launch");
+  }
+  // split-K
+  float *partials = nullptr;
+  if (p.split_k > 1) {
+    e = hipMallocAsync((void **)&partials, (size_t)p.workspace_bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(split-K partials)");
+  }
+  fp8g::SkinnyLaunch l{(const uint8_t *)x, (const uint8_t *)w, scale, (uint16_t *)y, partials, (int)M, (int)N, (int)K,
+                       (int)p.k_slice, p.split_k, p.variant, vec};
+  e = fp8g::launch_skinny(l, stream);
+  if (partials) {
+    hipError_t f = hipFreeAsync(partials, stream);
+    if (e == hipSuccess && f != hipSuccess) return hip_fail(f, "hipFreeAsync(split-K partials)");
+  }
+  return e == hipSuccess ? FP8G_OK : hip_fail(e, "split-K kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y, int64_t M, int64_t N, int64_t K,
+                    void *stream) {
+  return run(x, w, scale, y, M, N, K, 0, 0, 0, stream);
+}
+
+int fp8_gemm_scaled_ex(const void *x, const void *w, const float *scale, void *y, int64_t M, int64_t N, int64_t K,
+                       int32_t path, int32_t variant, int32_t split_k, void *stream) {
+  return run(x, w, scale, y, M, N, K, path, variant, split_k, stream);
+}
+
+int fp8_gemm_plan(int64_t M, int64_t N, int64_t K, fp8g_plan *out) {
+  g_last_error.clear();
+  return plan_impl(M, N, K, 0, 0, 0, out);
+}
+
+int fp8_gemm_plan_ex(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, int32_t split_k,
+                     fp8g_plan *out) {
+  g_last_error.clear();
+  return plan_impl(M, N, K, path, variant, split_k, out);
+}
+
+const char *fp8_gemm_strerror(int status) {
+  switch (status) {
+    case FP8G_OK: return "success";
+    case FP8G_ERR_INVALID_ARG: return "invalid argument";
+    case FP8G_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FP8G_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *fp8_gemm_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// fp8g_internal.h -- declarations shared by the host API (fp8g_api.cpp) and the
+// kernel launchers (fp8g_kernels.hip) of libfp8g.so.  Not installed, not part
+// of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8g {
+
+// One launch of the main (tiled MFMA) kernel.
+struct MainLaunch {
+  const uint8_t *x;
+  const uint8_t *w;
+  const float *scale;
+  uint16_t *y;
+  int M, N, K;
+  int tiles_m, tiles_n, group_m;
+  int variant;   // main-path configuration id
+  bool k_tail;   // K % tile_k != 0
+  bool vec;      // y rows allow 8-byte stores (N % 4 == 0, y 8-byte aligned)
+};
+
+// One launch of the skinny split-K kernel (+ the reduce kernel when S > 1).
+struct SkinnyLaunch {
+  const uint8_t *x;
+  const uint8_t *w;
+  const float *scale;
+  uint16_t *y;
+  float *partials;  // [S, M, N] fp32, only when S > 1
+  int M, N, K;
+  int k_slice, S;
+  int variant;      // skinny configuration id
+  bool vec;         // N % 4 == 0 and y 8-byte aligned
+};
+
+// Kernel-side tile geometry of each configuration id (also used by the planner).
+struct MainConfig {
+  int id, bm, bn, bk, stages;
+};
+struct SkinnyConfig {
+  int id, waves_k;  // waves splitting K inside a workgroup; 4 / waves_k along N
+};
+
+const MainConfig *main_config(int id);      // nullptr if unknown
+const SkinnyConfig *skinny_config(int id);  // nullptr if unknown
+int skinny_tile_n(const SkinnyConfig &c);   // output columns per workgroup
+int skinny_chunk_bytes();                   // K granularity of one wave iteration
+
+hipError_t launch_main(const MainLaunch &l, hipStream_t stream);
+hipError_t launch_skinny(const SkinnyLaunch &l, hipStream_t stream);
+hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream);
+
+}  // namespace fp8g

@@ -1,0 +1,129 @@
+/*
+ * fp8g.h -- C ABI of the MI355X (gfx950) scaled FP8 GEMM library (libfp8g.so).
+ *
+ * The operation (one definition, used by every entry point):
+ *
+ *     y[m,n] = bf16_rne( (sum_{k<K} x[m,k] * w[n,k]) * scale[n] )
+ *
+ *   x     [M,K]  FP8 E4M3 (OCP, no infinities; torch.float8_e4m3fn) codes,
+ *                row-major, row stride K bytes ("activation")
+ *   w     [N,K]  FP8 E4M3 codes, row-major, row stride K bytes ("weight":
+ *                one row per output channel n)
+ *   scale [N]    fp32, per-output-channel dequantisation factor
+ *   y     [M,N]  bf16 bit patterns, row-major, row stride N elements
+ *
+ * The products are summed by the gfx950 f8f6f4 matrix cores into fp32
+ * accumulators; the scale multiplies the finished fp32 sum once, and the result
+ * is rounded to bf16, to nearest, ties to even.  Sources on the pages
+ * (kernelbench.com model pages, cells named by the kernel they audit):
+ *   - fp8 x fp8 products, fp32 accumulation, bf16 output:
+ *     "DeepSeek V4 Flash (0731)", CUTLASS 3.x SM90 fp8 GEMM cell.
+ *   - the live per-output-channel scale is applied in the epilogue, before the
+ *     bf16 store: "Kimi K3 (256k)", SM120 warp-specialised FP8 GEMM cell.
+ *   - every call reads the live operands and writes a fresh output; nothing is
+ *     cached between calls: "Claude Fable 5", Triton split-K cell;
+ *     "Qwen 3.8 Max", stale odd-K pad-cache cell (what goes wrong otherwise).
+ *   - skinny M runs as split-K with fp32 partials and a separate
+ *     reduce/scale/cast step: "Claude Fable 5", Triton split-K cell;
+ *     "Kimi K3 (256k)", SM120 cell (skinny path with a scaled finalize kernel).
+ *   - K need not be a multiple of any tile size: the pages zero-pad copies of
+ *     the operands ("Kimi K3 (256k)", SM100 persistent-TMA Triton cell: zero
+ *     bytes add nothing to the dot); this library masks the K tail inside the
+ *     kernel instead and never copies an operand.
+ *
+ * Ownership and threading: the caller owns every buffer.  The library keeps no
+ * state between calls and has no globals besides a thread-local copy of the
+ * last error message.  Calls are asynchronous: they enqueue kernels on
+ * `stream` (a hipStream_t; NULL is the default stream) and return without
+ * synchronising.  Buffers must stay valid until that work has finished.
+ */
+#ifndef FP8G_H
+#define FP8G_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define FP8G_OK 0
+#define FP8G_ERR_INVALID_ARG 1 /* rejected before any HIP call; nothing enqueued */
+#define FP8G_ERR_UNSUPPORTED 2 /* valid arguments outside what this build handles */
+#define FP8G_ERR_HIP 3         /* a HIP call failed (no device, launch, allocation) */
+
+/* Largest supported K (bytes per operand row).  Kernels address a tile of up
+ * to 256 rows through 32-bit buffer offsets. */
+#define FP8G_MAX_K ((int64_t)16777215)
+/* Largest supported M and N. */
+#define FP8G_MAX_MN ((int64_t)2147483647)
+
+/* Execution paths a plan can choose. */
+#define FP8G_PATH_NONE 0   /* M == 0 or N == 0: nothing to do */
+#define FP8G_PATH_ZERO 1   /* K == 0: y is filled with +0 (the empty sum) */
+#define FP8G_PATH_MAIN 2   /* tiled MFMA kernel, fused scale/bf16 epilogue */
+#define FP8G_PATH_SPLITK 3 /* skinny M: split-K partial kernel, then the
+                              reduce/scale/cast kernel when split_k > 1 */
+
+/* A launch plan.  Pure host integer arithmetic; computing one makes no HIP call. */
+typedef struct fp8g_plan {
+    int32_t path;           /* FP8G_PATH_* */
+    int32_t variant;        /* kernel configuration id within the path */
+    int32_t tile_m;         /* rows of y per workgroup tile */
+    int32_t tile_n;         /* columns of y per workgroup tile */
+    int32_t tile_k;         /* K bytes per pipeline step */
+    int32_t split_k;        /* K slices (splitk path); 1 otherwise */
+    int64_t k_slice;        /* K bytes per slice (splitk path); K otherwise */
+    int32_t group_m;        /* tile-raster group height (main path) */
+    int32_t k_tail;         /* 1 if K is not a multiple of the K step */
+    int64_t grid;           /* workgroups of the first kernel */
+    int64_t workspace_bytes;/* fp32 partials the call allocates (split_k > 1) */
+} fp8g_plan;
+
+/* y = bf16_rne((x . w^T) * scale), as defined above.
+ *   x, w, scale, y : device pointers.  x and w need no alignment.  scale must
+ *                    be 4-byte aligned, y 2-byte aligned.  y must not overlap
+ *                    x, w or scale.  y is fully overwritten.
+ *   M, N, K        : 0 <= M, N <= FP8G_MAX_MN, 0 <= K <= FP8G_MAX_K.
+ *                    M == 0 or N == 0 enqueues nothing; K == 0 writes +0.
+ *   stream         : hipStream_t, or NULL for the default stream.
+ * Returns FP8G_OK, FP8G_ERR_INVALID_ARG (bad sizes, null pointers with non-zero
+ * extent, misaligned scale/y, overlapping output), or FP8G_ERR_HIP (no device,
+ * launch failure, or failure to allocate split-K partials; those are
+ * allocated stream-ordered with hipMallocAsync and freed with hipFreeAsync on
+ * `stream` inside the call). */
+int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y,
+                    int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Same operation with parts of the plan forced, for tests and tuning.  Each
+ * override is 0 for "let the planner choose":
+ *   path    : FP8G_PATH_MAIN or FP8G_PATH_SPLITK (SPLITK needs M <= 64)
+ *   variant : a configuration id valid for the path (see fp8_gemm_plan_ex)
+ *   split_k : 1..64 K slices (splitk path only)
+ * Invalid overrides give FP8G_ERR_INVALID_ARG.  The result is the same
+ * operation to within fp32 summation order. */
+int fp8_gemm_scaled_ex(const void *x, const void *w, const float *scale, void *y,
+                       int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant,
+                       int32_t split_k, void *stream);
+
+/* The plan fp8_gemm_scaled would use for (M, N, K).  Host-only, no HIP call.
+ * Returns FP8G_OK or FP8G_ERR_INVALID_ARG. */
+int fp8_gemm_plan(int64_t M, int64_t N, int64_t K, fp8g_plan *out);
+
+/* The plan fp8_gemm_scaled_ex would use with the same overrides. */
+int fp8_gemm_plan_ex(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant,
+                     int32_t split_k, fp8g_plan *out);
+
+/* Static description of a status code. */
+const char *fp8_gemm_strerror(int status);
+
+/* Detail of the last failure on the calling thread (argument name, HIP error
+ * string); "" if none.  Valid until the next call on the same thread. */
+const char *fp8_gemm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8G_H */

@@ -1,0 +1,131 @@
+"""The C-ABI library: it loads, exports what include/fp8g.h declares, plans the
+five benchmark shapes as intended and rejects bad arguments before any HIP
+call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_gemm_channel_amd as fg
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fp8g.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8_gemm_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fg.LIBRARY)
+    names = declared_functions()
+    assert names, "no declarations found"
+    assert set(names) == set(fg.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/fp8g.h but not exported"
+
+
+def test_strerror_is_static_and_total():
+    assert fg.fp8_gemm_strerror(0) == "success"
+    assert fg.fp8_gemm_strerror(1) == "invalid argument"
+    assert fg.fp8_gemm_strerror(3) == "HIP runtime error"
+    assert fg.fp8_gemm_strerror(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("wl", synth.WORKLOADS, ids=lambda w: w.name)
+def test_plan_of_benchmark_shapes(wl):
+    p = fg.fp8_gemm_plan(wl.M, wl.N, wl.K)
+    if wl.M <= 64:
+        assert p["path_name"] == "splitk"
+        assert p["split_k"] >= 1 and p["k_slice"] * p["split_k"] >= wl.K
+        assert (p["split_k"] - 1) * p["k_slice"] < wl.K, "no empty slice"
+        assert p["k_slice"] % 128 == 0
+        assert p["workspace_bytes"] == (p["split_k"] * wl.M * wl.N * 4 if p["split_k"] > 1 else 0)
+    else:
+        assert p["path_name"] == "main"
+        assert p["grid"] == -(-wl.M // p["tile_m"]) * -(-wl.N // p["tile_n"])
+        assert p["k_tail"] == (wl.K % p["tile_k"] != 0)
+    if wl.M >= 4096:
+        assert (p["tile_m"], p["tile_n"]) == (256, 256) and p["grid"] >= 256
+    if wl.name == "odd-k-4127":
+        assert p["k_tail"] == 1
+
+
+def test_plan_special_extents():
+    assert fg.fp8_gemm_plan(0, 5, 7)["path_name"] == "none"
+    assert fg.fp8_gemm_plan(5, 0, 7)["path_name"] == "none"
+    assert fg.fp8_gemm_plan(5, 6, 0)["path_name"] == "zero"
+    p = fg.fp8_gemm_plan(1, 1, 1)
+    assert p["path_name"] == "splitk" and p["split_k"] == 1 and p["k_tail"] == 1
+    p = fg.fp8_gemm_plan(65, 1, 1)
+    assert p["path_name"] == "main" and p["k_tail"] == 1
+
+
+def test_plan_overrides():
+    p = fg.fp8_gemm_plan_ex(32, 12288, 4096, fg.PATH_SPLITK, 1, 4)
+    assert p["split_k"] == 4 and p["k_slice"] == 1024 and p["workspace_bytes"] == 4 * 32 * 12288 * 4
+    p = fg.fp8_gemm_plan_ex(32, 4096, 4096, fg.PATH_MAIN, 2, 0)
+    assert p["path_name"] == "main" and p["tile_m"] == 128
+    # split_k larger than the number of 128-byte chunks collapses to non-empty slices
+    p = fg.fp8_gemm_plan_ex(8, 100, 300, fg.PATH_SPLITK, 0, 8)
+    assert p["split_k"] == 3 and p["k_slice"] == 128
+
+
+@pytest.mark.parametrize("args", [
+    (-1, 4, 4), (4, -1, 4), (4, 4, -1), (4, 4, (1 << 24)), (2**31, 4, 4),
+])
+def test_plan_rejects_bad_dims(args):
+    with pytest.raises(fg.Fp8gError) as e:
+        fg.fp8_gemm_plan(*args)
+    assert e.value.status == fg.FP8G_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(path=7), dict(path=fg.PATH_SPLITK, M=65), dict(variant=99), dict(split_k=65),
+    dict(split_k=-1), dict(path=fg.PATH_MAIN, split_k=2), dict(path=fg.PATH_SPLITK, variant=9),
+])
+def test_plan_rejects_bad_overrides(kw):
+    M = kw.pop("M", 32)
+    with pytest.raises(fg.Fp8gError) as e:
+        fg.fp8_gemm_plan_ex(M, 256, 256, kw.get("path", 0), kw.get("variant", 0), kw.get("split_k", 0))
+    assert e.value.status == fg.FP8G_ERR_INVALID_ARG
+
+
+# Argument checks happen before any HIP call, so these use host addresses that
+# are never dereferenced.
+FAKE = 1 << 20
+
+
+@pytest.mark.parametrize("case,detail", [
+    (dict(y=0), "y is null"),
+    (dict(scale=0), "scale is null"),
+    (dict(x=0), "x or w is null"),
+    (dict(w=0), "x or w is null"),
+    (dict(scale=FAKE * 40 + 2), "4-byte"),
+    (dict(y=FAKE * 40 + 1), "2-byte"),
+    (dict(y=FAKE * 2), "overlaps"),
+    (dict(M=-3), "negative"),
+])
+def test_scaled_rejects_bad_arguments_without_hip(case, detail):
+    a = dict(x=FAKE * 2, w=FAKE * 4, scale=FAKE * 6, y=FAKE * 8, M=16, N=16, K=64)
+    a.update(case)
+    st = fg.fp8_gemm_scaled(a["x"], a["w"], a["scale"], a["y"], a["M"], a["N"], a["K"], 0)
+    assert st == fg.FP8G_ERR_INVALID_ARG
+    assert detail in fg.fp8_gemm_last_error()
+
+
+def test_empty_extent_is_a_no_op_even_with_null_pointers():
+    assert fg.fp8_gemm_scaled(0, 0, 0, 0, 0, 16, 16, 0) == fg.FP8G_OK
+    assert fg.fp8_gemm_scaled(0, 0, 0, 0, 16, 0, 16, 0) == fg.FP8G_OK
+
+
+def test_no_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; this checks the GPU-less error path")
+    st = fg.fp8_gemm_scaled(FAKE * 2, FAKE * 4, FAKE * 6, FAKE * 8, 16, 16, 64, 0)
+    assert st == fg.FP8G_ERR_HIP
+    assert "hipGetDevice" in fg.fp8_gemm_last_error()

@@ -1,0 +1,93 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, element by element, within 1e-2 + 1e-2 * |ref|.
+
+Sizes the oracle finishes in seconds are compared in full; they span several
+tiles and ragged tails on every path and configuration.  The five benchmark
+shapes run with the default plan (the launch configuration bench.py times);
+the large ones are compared on sampled outputs that the oracle computes one
+by one, always including full rows and columns at the tile edges.
+"""
+import numpy as np
+import pytest
+
+import fp8_gemm_channel_amd as fg
+import oracle
+import synth
+from tests.gpu_util import compare, run, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_case(M, N, K, seed=42, **kw):
+    x, w, s = synth.fp8_inputs(M, N, K, seed=seed)
+    say(f"full M={M} N={N} K={K} seed={seed} {kw}")
+    got = run(x, w, s, **kw)
+    ref = oracle.gemm_scaled(x, w, s)
+    return compare(got, ref, f"M={M} N={N} K={K} {kw}")
+
+
+# ------------------------------------------------- main path, every variant --
+MAIN_SHAPES = [(300, 520, 4127), (257, 129, 200), (128, 128, 128), (65, 70, 33), (520, 264, 1000)]
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3, 4])
+@pytest.mark.parametrize("shape", MAIN_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_main_variants_full(variant, shape):
+    _full_case(*shape, path=fg.PATH_MAIN, variant=variant)
+
+
+# ------------------------------------------- split-K path, forced splits ------
+@pytest.mark.parametrize("split_k", [1, 2, 3, 4, 7])
+@pytest.mark.parametrize("M", [1, 31, 32, 33, 64])
+def test_splitk_full(M, split_k):
+    _full_case(M, 1000, 4127, path=fg.PATH_SPLITK, split_k=split_k)
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_splitk_variants(variant):
+    _full_case(40, 777, 3000, path=fg.PATH_SPLITK, variant=variant, split_k=3)
+    _full_case(32, 1024, 4096, path=fg.PATH_SPLITK, variant=variant, split_k=1)
+
+
+# ---------------------------------------------------- the benchmark shapes ----
+def _sampled(x, w, s, got, seed, count=6000, edges=()):
+    M, N = got.shape
+    mi, ni = synth.sample_positions(M, N, count, seed)
+    rows = [r for r in edges if r < M]
+    cols = [c for c in edges if c < N]
+    for r in rows:                           # full rows
+        mi = np.concatenate([mi, np.full(N, r)])
+        ni = np.concatenate([ni, np.arange(N)])
+    for c in cols:                           # full columns
+        mi = np.concatenate([mi, np.arange(M)])
+        ni = np.concatenate([ni, np.full(M, c)])
+    ref = oracle.gemm_scaled_at(x, w, s, mi, ni)
+    return compare(got[mi, ni], ref, f"sampled {M}x{N}")
+
+
+@pytest.mark.parametrize("wl", synth.WORKLOADS, ids=lambda w: w.name)
+def test_benchmark_shape(wl):
+    x, w, s = synth.fp8_inputs(wl.M, wl.N, wl.K, seed=42)
+    plan = fg.fp8_gemm_plan(wl.M, wl.N, wl.K)
+    say(f"{wl.name} default plan {plan}")
+    got = run(x, w, s)
+    if wl.M * wl.N * wl.K <= 10**11:
+        compare(got, oracle.gemm_scaled(x, w, s), wl.name)
+    else:
+        # first/last rows and columns of tiles, plus random positions
+        t = 256
+        edges = (0, t - 1, t, wl.M - 1, wl.N - 1)
+        _sampled(x, w, s, got, seed=7, edges=edges)
+
+
+@pytest.mark.parametrize("seed", [123, 456])
+@pytest.mark.parametrize("name", ["square-256", "decode-m32", "odd-k-4127"])
+def test_benchmark_shape_other_seeds(name, seed):
+    wl = synth.WORKLOAD_BY_NAME[name]
+    x, w, s = synth.fp8_inputs(wl.M, wl.N, wl.K, seed=seed)
+    say(f"{name} seed={seed}")
+    got = run(x, w, s)
+    if wl.M * wl.N * wl.K <= 10**11:
+        compare(got, oracle.gemm_scaled(x, w, s), name)
+    else:
+        _sampled(x, w, s, got, seed=seed, edges=(0, 255, 256, wl.M - 1))
