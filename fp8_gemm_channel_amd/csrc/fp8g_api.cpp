@@ -85,30 +85,49 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
   if (path == 0) path = (M <= kSkinnyMaxM) ? FP8G_PATH_SPLITK : FP8G_PATH_MAIN;
   if (path == FP8G_PATH_SPLITK) {
     if (M > kSkinnyMaxM) return fail(FP8G_ERR_INVALID_ARG, "split-K path needs M <= %d (M=%lld)", kSkinnyMaxM, (long long)M);
-    if (variant == 0) variant = 1;
-    const fp8g::SkinnyConfig *c = fp8g::skinny_config(variant);
-    if (!c) return fail(FP8G_ERR_INVALID_ARG, "unknown split-K variant %d", variant);
-    const int64_t tile_n = fp8g::skinny_tile_n(*c);
-    const int64_t col_blocks = cdiv(N, tile_n);
+    const int max_rb = fp8g::skinny_max_row_blocks((int)M);
+    if (variant > max_rb) return fail(FP8G_ERR_INVALID_ARG, "split-K variant %d needs M <= %d", variant, variant <= 4 ? 32 : 16);
     const int64_t chunk = fp8g::skinny_chunk_bytes();
-    int64_t S = split_k;
-    if (S == 0) {
-      // Enough workgroups to cover every compute unit twice, while each slice
-      // keeps at least 1 KiB of K.
-      S = 1;
-      while (S < kMaxSplit && col_blocks * S < 2 * kNumCUs && K / (2 * S) >= 1024) S *= 2;
+    const int64_t nchunks = cdiv(K, chunk);
+    const int64_t m_rows = M <= 16 ? 16 : (M <= 32 ? 32 : 64);  // x rows staged per chunk
+    // Choose rows per workgroup (16 * rb) and the number of K slices S by a
+    // bandwidth model: workgroups run in rounds of one per compute unit; a round
+    // costs the w bytes one workgroup streams plus a quarter of its x bytes (x
+    // is re-read from L2); S > 1 adds the partials round trip and a second
+    // launch (about 2 us of one CU's share of HBM bandwidth, ~48 KiB).
+    int64_t best_cost = -1, best_rb = 1, best_S = 1;
+    for (int rb = 1; rb <= max_rb; ++rb) {
+      if (variant != 0 && rb != variant) continue;
+      const int64_t nb = cdiv(N, 16 * rb);
+      for (int64_t S0 = 1; S0 <= kMaxSplit; S0 *= 2) {
+        int64_t S = split_k ? split_k : S0;
+        if (split_k && S0 > 1) break;
+        const int64_t k_slice = cdiv(cdiv(K, S), chunk) * chunk;
+        S = cdiv(K, k_slice);
+        const int64_t rounds = cdiv(nb * S, kNumCUs);
+        int64_t cost = rounds * (16 * rb * k_slice + m_rows * k_slice / 4);
+        if (S > 1) cost += 48 * 1024 + (2 * S * M * N * 4 + M * N * 2) / kNumCUs;
+        if (best_cost < 0 || cost < best_cost) {
+          best_cost = cost;
+          best_rb = rb;
+          best_S = S;
+        }
+        if (S >= nchunks) break;
+      }
     }
-    int64_t k_slice = cdiv(cdiv(K, S), chunk) * chunk;
-    S = cdiv(K, k_slice);  // no empty slices
+    const fp8g::SkinnyConfig *c = fp8g::skinny_config((int)best_rb);
+    if (!c) return fail(FP8G_ERR_INVALID_ARG, "unknown split-K variant %d", variant);
+    const int64_t k_slice = cdiv(cdiv(K, best_S), chunk) * chunk;
+    const int64_t S = cdiv(K, k_slice);  // no empty slices
     p->path = FP8G_PATH_SPLITK;
-    p->variant = variant;
-    p->tile_m = M > 32 ? 64 : 32;
-    p->tile_n = (int32_t)tile_n;
+    p->variant = c->id;
+    p->tile_m = (int32_t)m_rows;
+    p->tile_n = fp8g::skinny_tile_n(*c);
     p->tile_k = (int32_t)chunk;
     p->split_k = (int32_t)S;
     p->k_slice = k_slice;
     p->k_tail = (K % chunk) != 0;
-    p->grid = col_blocks * S;
+    p->grid = cdiv(N, p->tile_n) * S;
     p->workspace_bytes = S > 1 ? S * M * N * (int64_t)sizeof(float) : 0;
     return FP8G_OK;
   }

@@ -39,12 +39,13 @@ struct MainConfig {
   int id, bm, bn, bk, stages;
 };
 struct SkinnyConfig {
-  int id, waves_k;  // waves splitting K inside a workgroup; 4 / waves_k along N
+  int id, row_blocks;  // w rows per workgroup = 16 * row_blocks
 };
 
 const MainConfig *main_config(int id);      // nullptr if unknown
 const SkinnyConfig *skinny_config(int id);  // nullptr if unknown
 int skinny_tile_n(const SkinnyConfig &c);   // output columns per workgroup
+int skinny_max_row_blocks(int M);           // LDS limit on row_blocks for this M
 int skinny_chunk_bytes();                   // K granularity of one wave iteration
 
 hipError_t launch_main(const MainLaunch &l, hipStream_t stream);

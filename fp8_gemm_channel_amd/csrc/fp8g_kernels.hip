@@ -45,6 +45,7 @@ namespace fp8g {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 // LLVM's raw buffer intrinsics, taking the 128-bit descriptor as <4 x i32>.
 __device__ v4i llvm_buffer_load_v4i32(v4i rsrc, uint32_t voffset, uint32_t soffset, int aux)
@@ -155,23 +156,54 @@ struct MainArgs {
   int tiles_m, tiles_n, group_m;
 };
 
+// Scheduling pattern for NM MFMAs and NR LDS reads spread evenly: MFMA q is
+// followed by reads [q*NR/NM, (q+1)*NR/NM).
+template <int Q, int NM, int NR>
+__device__ __forceinline__ void interleave_mfma_reads() {
+  if constexpr (Q < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr ((Q + 1) * NR / NM - Q * NR / NM > 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, (Q + 1) * NR / NM - Q * NR / NM, 0);
+    interleave_mfma_reads<Q + 1, NM, NR>();
+  }
+}
+
+// Software pipeline of one K step (BK bytes, BK/64 MFMA sub-steps):
+//
+//     wait for this wave's DMA of step k+1, workgroup barrier
+//     LDS-DMA of step k+STAGES-1 into the buffer step k-1 used
+//     MFMAs of step k (operands in registers F[k&1]), interleaved with the LDS
+//     reads of step k+1's operands into F[(k+1)&1]
+//
+// The barrier publishes step k+1 (every wave's DMA has landed) and retires the
+// buffer of step k-1 (every wave read its operands before the barrier).
+// With 8 waves per workgroup two waves share each SIMD, so one wave's MFMAs
+// cover the other's barrier and LDS waits; a single wave per SIMD can neither
+// keep the matrix pipe full nor keep enough LDS reads in flight (measured on
+// MI355X: ~4.0-4.5 vs ~4.8 PFLOP/s for back-to-back MFMAs, ~110 vs ~200
+// B/clk/CU for 16-byte LDS reads).
 template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool KTAIL, bool VEC>
 __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) {
   constexpr int NWAVES = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
   constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 blocks per wave
+  constexpr int SUB = BK / 64;               // MFMA sub-steps per K step
   constexpr int CH = BK / 16;                // 16-byte chunks per row
   constexpr int ROWS_PER_KB = 1024 / BK;     // rows in one 1 KiB DMA block
   constexpr int STAGE_BYTES = (BM + BN) * BK;
   constexpr int BLOCKS = STAGE_BYTES / 1024;
   constexpr int DPW = BLOCKS / NWAVES;       // DMA instructions per wave per stage
   constexpr int W_DPW = (BN / ROWS_PER_KB) / NWAVES;  // of which fill w rows
+  constexpr int NMFMA = SUB * FN * FM;       // MFMAs per wave per step
+  constexpr int NREAD = SUB * (FN + FM) * 2; // 16-byte LDS reads per wave per step
   static_assert(BK == 64 || BK == 128, "BK");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
   static_assert(BLOCKS % NWAVES == 0 && (BN / ROWS_PER_KB) % NWAVES == 0, "DMA split");
-  static_assert(STAGES >= 2 && (STAGES - 2) * DPW < 64, "pipeline depth");
+  static_assert(STAGES >= 3 && (STAGES - 2) * DPW < 64, "vmcnt range");
+  static_assert(BN <= 256, "one DMA instruction stages the tile's scales");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+  // Stage ring, then the tile's BN scales.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES + 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -201,26 +233,31 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   const v4i rsrc_x = make_rsrc(a.x + (size_t)m0 * K, (uint32_t)rows_x * (uint32_t)K);
   const v4i rsrc_w = make_rsrc(a.w + (size_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
 
-  // Per-lane source offsets (without the K step) for each DMA instruction.
-  // Instruction t of this wave fills 1 KiB block b = t * NWAVES + wave.
-  uint32_t src_off[DPW];
-  uint32_t src_chunk[DPW];  // byte offset of the logical chunk within the K step
-  {
-    const int rsub = lane / CH, p = lane % CH;
-#pragma unroll
-    for (int t = 0; t < DPW; ++t) {
-      const int b = t * NWAVES + wave;
-      const int R = b * ROWS_PER_KB + rsub;
-      const int r = (t < W_DPW) ? R : R - BN;
-      const int c = p ^ swz<BK>(r);
-      src_chunk[t] = (uint32_t)c * 16u;
-      src_off[t] = (uint32_t)r * (uint32_t)K + src_chunk[t];
-    }
-  }
+  const int g = lane >> 5, lr = lane & 31;
   const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+  const uint32_t scale_lds = smem_base + STAGES * STAGE_BYTES;
+  // The tile's scales scale[n0 .. n0+BN) go to LDS now (wave 0, one DMA; columns
+  // past N read as zero), so the epilogue does not wait on global memory.  This
+  // is wave 0's oldest vector-memory operation, so its first stage wait covers
+  // it, and every barrier after that publishes it.
+  if (wave == 0) {
+    const v4i rsrc_s = make_rsrc(a.scale + n0, (uint32_t)(a.N - n0) * 4u);
+    dma16(rsrc_s, scale_lds, (uint32_t)lane * 16u, 0u);
+  }
+
+  // Lane's tile row and logical chunk in DMA instruction t, which fills 1 KiB
+  // block t*NWAVES + wave of a stage (w rows first, then x rows).
+  auto dma_row = [&](int t) __attribute__((always_inline)) {
+    const int R = (t * NWAVES + wave) * ROWS_PER_KB + lane / CH;
+    return (t < W_DPW) ? R : R - BN;
+  };
+  auto dma_chunk = [&](int t) __attribute__((always_inline)) { return (lane % CH) ^ swz<BK>(dma_row(t)); };
+  uint32_t src_off[DPW];  // source offsets without the K step
+#pragma unroll
+  for (int t = 0; t < DPW; ++t) src_off[t] = (uint32_t)dma_row(t) * (uint32_t)K + (uint32_t)dma_chunk(t) * 16u;
 
   // Full K step kt -> stage buffer `st` via LDS-DMA.
-  auto issue_full = [&](int kt, int st) {
+  auto issue_full = [&](int kt, int st) __attribute__((always_inline)) {
     const uint32_t k0 = (uint32_t)kt * BK;
     const uint32_t sb = smem_base + (uint32_t)st * STAGE_BYTES;
 #pragma unroll
@@ -231,23 +268,49 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   };
   // Last, partial K step -> stage buffer `st` through registers, bytes at or
   // past K zeroed.  Same block/lane mapping as the DMA path.
-  auto issue_tail = [&](int kt, int st) {
+  auto issue_tail = [&](int kt, int st) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     uint8_t *sb = smem + st * STAGE_BYTES;
 #pragma unroll
     for (int t = 0; t < DPW; ++t) {
-      const int valid = K - (k0 + (int)src_chunk[t]);
+      const int valid = K - (k0 + 16 * dma_chunk(t));
       const uint4 v = load16_masked(t < W_DPW ? rsrc_w : rsrc_x, src_off[t] + (uint32_t)k0, valid);
       *(uint4 *)(sb + (t * NWAVES + wave) * 1024 + lane * 16) = v;
     }
   };
+  const int nk_full = K / BK;
+  const int nk = nk_full + (KTAIL ? 1 : 0);
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    if (kt < nk_full) issue_full(kt, kt % STAGES);
+    else if (KTAIL && kt == nk_full) issue_tail(kt, kt % STAGES);
+  };
 
-  // Fragment read offsets.  Lane l reads row (l % 32) of each 32-row block and
-  // the two chunks 4j + 2(l/32) + {0,1} of 64-byte sub-step j.
-  const int g = lane >> 5, lr = lane & 31;
+  // Fragment reads.  Lane l reads row (l % 32) of each 32-row block and the two
+  // chunks 4j + 2(l/32) + {0,1} of 64-byte sub-step j.
   const int aw_row = wave_n * TN + lr;  // w row of block 0 (block i adds 32 i rows)
   const int bx_row = wave_m * TM + lr;  // x row of block 0
   const int sa = swz<BK>(aw_row), sbx = swz<BK>(bx_row);  // 32 i leaves the swizzle unchanged
+
+  v8i fa[2][SUB][FN], fb[2][SUB][FM];
+  // LDS read number q of a step (q in [0, NREAD)): per sub-step j, first the
+  // FN w blocks then the FM x blocks, low then high 16 bytes.
+  auto read_one = [&](int st, int q, v8i (&af)[SUB][FN], v8i (&bf)[SUB][FM]) __attribute__((always_inline)) {
+    const int j = q / ((FN + FM) * 2), rest = q % ((FN + FM) * 2);
+    const int blk = rest / 2, half = rest % 2;
+    const int c = 4 * j + 2 * g + half;
+    const uint8_t *sw_ = smem + st * STAGE_BYTES;
+    if (blk < FN) {
+      const uint8_t *row = sw_ + (aw_row + 32 * blk) * BK;
+      const uint4 v = *(const uint4 *)(row + ((c ^ sa) << 4));
+      af[j][blk][4 * half + 0] = (int)v.x; af[j][blk][4 * half + 1] = (int)v.y;
+      af[j][blk][4 * half + 2] = (int)v.z; af[j][blk][4 * half + 3] = (int)v.w;
+    } else {
+      const uint8_t *row = sw_ + BN * BK + (bx_row + 32 * (blk - FN)) * BK;
+      const uint4 v = *(const uint4 *)(row + ((c ^ sbx) << 4));
+      bf[j][blk - FN][4 * half + 0] = (int)v.x; bf[j][blk - FN][4 * half + 1] = (int)v.y;
+      bf[j][blk - FN][4 * half + 2] = (int)v.z; bf[j][blk - FN][4 * half + 3] = (int)v.w;
+    }
+  };
 
   v16f acc[FN][FM];
 #pragma unroll
@@ -257,89 +320,76 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  auto compute = [&](int st) {
-    const uint8_t *sw_ = smem + st * STAGE_BYTES;
-    const uint8_t *sx_ = sw_ + BN * BK;
+  // Prologue: DMA of steps 0 .. STAGES-2, then step 0's operands.
 #pragma unroll
-    for (int j = 0; j < BK / 64; ++j) {
-      const int c0 = 4 * j + 2 * g;
-      v8i af[FN], bf[FM];
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const uint8_t *row = sw_ + (aw_row + 32 * i) * BK;
-        const uint4 lo = *(const uint4 *)(row + ((c0 ^ sa) << 4));
-        const uint4 hi = *(const uint4 *)(row + (((c0 + 1) ^ sa) << 4));
-        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int jm = 0; jm < FM; ++jm) {
-        const uint8_t *row = sx_ + (bx_row + 32 * jm) * BK;
-        const uint4 lo = *(const uint4 *)(row + ((c0 ^ sbx) << 4));
-        const uint4 hi = *(const uint4 *)(row + (((c0 + 1) ^ sbx) << 4));
-        bf[jm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int jm = 0; jm < FM; ++jm) acc[i][jm] = mfma32(af[i], bf[jm], acc[i][jm]);
-    }
-  };
-
-  const int nk_full = K / BK;
-  const int nk = nk_full + (KTAIL ? 1 : 0);
-
-  // Prologue: fill the first STAGES-1 buffers.
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {
-    if (s < nk_full) issue_full(s, s);
-    else if (KTAIL && s == nk_full) issue_tail(s, s);
+  for (int s = 0; s < STAGES - 1; ++s) issue(s);
+  {
+    const int ahead = min(STAGES - 2, nk - 1);
+    if (ahead >= 2) vm_wait<2 * DPW>();
+    else if (ahead == 1) vm_wait<DPW>();
+    else vm_wait<0>();
   }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NREAD; ++q) read_one(0, q, fa[0], fb[0]);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // Wait until this wave's DMA for step kt has landed.  Stages issued after
-    // kt may stay in flight.  (When the register-loaded tail stage has been
-    // issued, the compiler has already waited for all earlier vector memory
-    // operations, which complete in order, so the count below never
-    // under-waits.)
-    const int ahead = min(STAGES - 2, nk - 1 - kt);
-    if constexpr (STAGES >= 4) {
+  // Two steps per trip so the register buffers F[0] / F[1] are compile-time.
+  auto step = [&](const int kt, const int cur) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    // own DMA of step kt+1 must have landed; later stages may stay in flight
+    const int ahead = min(STAGES - 3, nk - 2 - kt);
+    if constexpr (STAGES >= 5) {
       if (ahead >= 2) vm_wait<2 * DPW>();
       else if (ahead == 1) vm_wait<DPW>();
       else vm_wait<0>();
-    } else if constexpr (STAGES == 3) {
+    } else if constexpr (STAGES == 4) {
       if (ahead >= 1) vm_wait<DPW>();
       else vm_wait<0>();
     } else {
       vm_wait<0>();
     }
-    // Every wave's part of step kt is in LDS, and every wave has finished
-    // reading the buffer of step kt-1, which is refilled next.
     __syncthreads();
-    const int kn = kt + STAGES - 1;
-    if (kn < nk_full) issue_full(kn, kn % STAGES);
-    else if (KTAIL && kn == nk_full) issue_tail(kn, kn % STAGES);
-    compute(kt % STAGES);
+    issue(kt + STAGES - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool more = kt + 1 < nk;
+    const int st = (kt + 1) % STAGES;
+#pragma unroll
+    for (int q = 0; q < NMFMA; ++q) {
+      const int j = q / (FN * FM), i = (q / FM) % FN, jm = q % FM;
+      acc[i][jm] = mfma32(fa[cur][j][i], fb[cur][j][jm], acc[i][jm]);
+      if (more) {
+#pragma unroll
+        for (int r = q * NREAD / NMFMA; r < (q + 1) * NREAD / NMFMA; ++r) read_one(st, r, fa[cur ^ 1], fb[cur ^ 1]);
+      }
+    }
+    interleave_mfma_reads<0, NMFMA, NREAD>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, 0);
+    step(kt + 1, 1);
   }
+  if (kt < nk) step(kt, 0);
 
   // Epilogue: y[m, n..n+3] = bf16(acc * scale[n..n+3]).
-  const v4i rsrc_s = make_rsrc(a.scale, (uint32_t)a.N * 4u);
+  const float *s_lds = (const float *)(smem + STAGES * STAGE_BYTES);
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
-      const int n = n0 + wave_n * TN + 32 * i + 8 * qd + 4 * g;
-      float s[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] = llvm_buffer_load_f32(rsrc_s, (uint32_t)(n + e) * 4u, 0, 0);
+      const int nl = wave_n * TN + 32 * i + 8 * qd + 4 * g;
+      const int n = n0 + nl;
+      const float4 sc = *(const float4 *)(s_lds + nl);
 #pragma unroll
       for (int jm = 0; jm < FM; ++jm) {
         const int m = m0 + wave_m * TM + 32 * jm + lr;
         if (m >= a.M) continue;
         uint16_t *yr = a.y + (size_t)m * a.N;
-        const uint32_t b0 = bf16_rne(acc[i][jm][4 * qd + 0] * s[0]);
-        const uint32_t b1 = bf16_rne(acc[i][jm][4 * qd + 1] * s[1]);
-        const uint32_t b2 = bf16_rne(acc[i][jm][4 * qd + 2] * s[2]);
-        const uint32_t b3 = bf16_rne(acc[i][jm][4 * qd + 3] * s[3]);
+        const uint32_t b0 = bf16_rne(acc[i][jm][4 * qd + 0] * sc.x);
+        const uint32_t b1 = bf16_rne(acc[i][jm][4 * qd + 1] * sc.y);
+        const uint32_t b2 = bf16_rne(acc[i][jm][4 * qd + 2] * sc.z);
+        const uint32_t b3 = bf16_rne(acc[i][jm][4 * qd + 3] * sc.w);
         if (VEC) {
           if (n < a.N) *(uint2 *)(yr + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
         } else {
@@ -355,19 +405,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
 
 // ---------------------------------------------------------------- skinny path
 //
-// M <= 64.  The workgroup's four waves are arranged 4/WK along n (32 w rows
-// each) by WK along K.  Each wave streams its w rows and the x rows straight
-// from global memory into MFMA operand registers (no LDS staging: w is read
-// exactly once, x is small and stays in L2), U 128-byte K chunks per
-// iteration.  Lane l reads 64 contiguous bytes of its row per chunk; MFMA j of
-// the chunk consumes bytes [32 j, 32 j + 32) of them, which is the same
-// (lane, byte) -> k map for both operands.
+// M <= 64 (decode-shaped): the time is the stream of w through HBM.  A workgroup
+// owns R = 16*RB rows of w (output columns) and one K slice.  Its four waves take
+// the slice's 128-byte K chunks round-robin (wave v: chunks v, v+4, v+8, ...), so
+// together they read every w row front to back.  Each wave streams its chunks --
+// R rows of w and 16*MB rows of x, 128 bytes each -- into a private ring of D LDS
+// slots with LDS-DMA, one 1 KiB instruction per 8 rows, and multiplies them with
+// V_MFMA_F32_16X16X128_F8F6F4 (A = 16 w rows, B = 16 x rows).  w is loaded with
+// the non-temporal policy (read once; on gfx950 this roughly doubles streaming
+// read bandwidth), x without it (every workgroup re-reads x, so it should stay in
+// L2).  No barrier is needed in the K loop because no wave reads another wave's
+// slots; completion is tracked with vmcnt.  At the end the four per-wave sums are
+// added through LDS in wave order, so results are deterministic.
 //
-// blockIdx.y selects the K slice [s * k_slice, min(K, (s+1) * k_slice)).  With
-// one slice the kernel applies the scale and writes bf16 y directly; with
-// several it writes unscaled fp32 partials P[s, m, n] that the reduce kernel
-// sums in slice order.  Waves sharing a column block add their accumulators
-// through LDS in wave order, so results are deterministic.
+// MFMA 16x16x128 layout (gfx950, checked on the hardware): operand lane l supplies
+// row l % 16 and the 32 bytes of K-group l / 16; accumulator lane l, element e is
+// row 4*(l/16) + e, column l % 16.  Rows here are w rows (n), columns x rows (m).
+//
+// blockIdx.y selects the K slice [s * k_slice, min(K, (s+1) * k_slice)).  With one
+// slice the kernel scales and writes bf16 y; with several it writes unscaled fp32
+// partials P[s, m, n] that the reduce kernel adds in slice order.
 struct SkinnyArgs {
   const uint8_t *x;
   const uint8_t *w;
@@ -376,138 +433,188 @@ struct SkinnyArgs {
   float *P;
   int M, N, K;
   int k_slice;
+  int vec;  // y rows allow 8-byte stores / P rows 16-byte stores (N % 4 == 0)
 };
 
-constexpr int kSkinnyU = 4;  // 128-byte chunks per wave iteration
+template <int RB, int MB>
+struct SkinnyShape {
+  static constexpr int R = 16 * RB;        // w rows per workgroup
+  static constexpr int MX = 16 * MB;       // x rows staged per chunk
+  static constexpr int ROWS = R + MX;
+  static constexpr int SLOT = ROWS * 128;  // bytes per ring slot
+  static constexpr int OPS = ROWS / 8;     // 1 KiB DMA instructions per chunk
+  static constexpr int D = 3;              // ring depth (chunks in flight per wave)
+  static constexpr int WAVE_LDS = D * SLOT;
+  static_assert(4 * WAVE_LDS <= 160 * 1024, "LDS");
+  static_assert((D - 1) * OPS < 64, "vmcnt range");
+};
 
-template <int MB, int WK, bool PARTIAL, bool VEC>
-__global__ __launch_bounds__(256) void fp8g_splitk_partial_kernel(SkinnyArgs a) {
-  constexpr int WN = 4 / WK;
-  constexpr int U = kSkinnyU;
-  static_assert(WK == 1 || WK == 2 || WK == 4, "WK");
-  __shared__ float red[(WK > 1) ? (WK - 1) * WN * MB * 16 * 64 : 1];
+// 128-byte rows, 16-row MFMA reads: chunk c of row r lives at position c ^ swz16(r);
+// every 8 consecutive rows use 8 different positions, every 16 rows 16 different
+// (bank half, position) pairs.
+__device__ __forceinline__ int swz16(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave % WN, wk = wave / WN;
-  const int g = lane >> 5, lr = lane & 31;
+__device__ __forceinline__ void dma16_nt(v4i rsrc, uint32_t lds_base, uint32_t voffset, uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) / lgkmcnt(0) as compiler memory barriers: LDS reads of data
+// written by LDS-DMA must not be moved above the wait that covers the DMA.
+template <int N>
+__device__ __forceinline__ void vm_wait_fence() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void lgkm_wait_fence() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
+__device__ __forceinline__ v4f mfma16(const v8i &a, const v8i &b, const v4f &c) {
+  // Zero scale operands select the unscaled V_MFMA_F32_16X16X128_F8F6F4.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <int RB, int MB>
+__global__ __launch_bounds__(256, 1) void fp8g_splitk_partial_kernel(SkinnyArgs a) {
+  using S = SkinnyShape<RB, MB>;
+  constexpr int R = S::R, OPS = S::OPS, D = S::D, SLOT = S::SLOT, W_OPS = R / 8;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * S::WAVE_LDS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int K = a.K;
-
-  const int nw0 = blockIdx.x * (32 * WN) + wn * 32;
-  const int rows_w = max(0, min(32, a.N - nw0));
+  const int n0 = blockIdx.x * R;
+  const int rows_w = min(R, a.N - n0);
   const int s = blockIdx.y;
   const int kbeg = s * a.k_slice;
   const int kend = min(K, kbeg + a.k_slice);
+  const int nch = (kend - kbeg + 127) >> 7;
+  const int my = nch > wave ? (nch - wave + 3) >> 2 : 0;  // chunks of this wave
 
-  const v4i rsrc_w = make_rsrc(a.w + (size_t)min(nw0, a.N) * K, (uint32_t)rows_w * (uint32_t)K);
+  const v4i rsrc_w = make_rsrc(a.w + (size_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
   const v4i rsrc_x = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)K);
-  const uint32_t w_off = (uint32_t)lr * (uint32_t)K + 64u * g;
-  uint32_t x_off[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) x_off[mb] = (uint32_t)(lr + 32 * mb) * (uint32_t)K + 64u * g;
 
-  v16f acc[MB];
+  // DMA instruction t moves rows 8t .. 8t+7 of a slot (w rows, then x rows).
+  uint32_t src_off[OPS], src_chunk[OPS];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[mb][e] = 0.0f;
+  for (int t = 0; t < OPS; ++t) {
+    const int row = 8 * t + (lane >> 3);
+    const int r = t < W_OPS ? row : row - R;
+    const int c = (lane & 7) ^ swz16(r);
+    src_chunk[t] = (uint32_t)c * 16u;
+    src_off[t] = (uint32_t)r * (uint32_t)K + src_chunk[t];
+  }
+  const uint32_t ring_base =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem + (uint32_t)wave * S::WAVE_LDS;
+  uint8_t *ring = smem + wave * S::WAVE_LDS;
 
-  const int step = WK * U * 128;
-  for (int kc = kbeg + wk * U * 128; kc < kend; kc += step) {
-    uint4 wv[U][4], xv[MB][U][4];
-    if (kc + U * 128 <= kend) {
+  // Local chunk j (global chunk wave + 4j) -> slot j % D.
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const int kc = kbeg + ((wave + 4 * j) << 7);
+    const int slot = j % D;
+    if (kc + 128 <= kend) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const uint32_t ko = (uint32_t)(kc + u * 128 + 16 * h);
-          wv[u][h] = as_u4(llvm_buffer_load_v4i32(rsrc_w, w_off + ko, 0, 0));
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) xv[mb][u][h] = as_u4(llvm_buffer_load_v4i32(rsrc_x, x_off[mb] + ko, 0, 0));
-        }
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int kb = kc + u * 128 + 64 * g + 16 * h;  // this lane's chunk start
-          const int valid = kend - kb;
-          const uint32_t ko = (uint32_t)(kc + u * 128 + 16 * h);
-          wv[u][h] = load16_masked(rsrc_w, w_off + ko, valid);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) xv[mb][u][h] = load16_masked(rsrc_x, x_off[mb] + ko, valid);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint4 a0 = wv[u][2 * j], a1 = wv[u][2 * j + 1];
-        const v8i af = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const uint4 b0 = xv[mb][u][2 * j], b1 = xv[mb][u][2 * j + 1];
-          const v8i bf = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-          acc[mb] = mfma32(af, bf, acc[mb]);
-        }
+      for (int t = 0; t < OPS; ++t) {
+        const uint32_t lds = ring_base + (uint32_t)(slot * SLOT + t * 1024);
+        if (t < W_OPS) dma16_nt(rsrc_w, lds, src_off[t], (uint32_t)kc);
+        else dma16(rsrc_x, lds, src_off[t], (uint32_t)kc);
       }
-  }
-
-  if constexpr (WK > 1) {
-    if (wk > 0) {
+    } else {
+      // the last chunk of K: bytes at or past K are zero
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) red[((((wk - 1) * WN + wn) * MB + mb) * 16 + e) * 64 + lane] = acc[mb][e];
+      for (int t = 0; t < OPS; ++t) {
+        const uint4 v = load16_masked(t < W_OPS ? rsrc_w : rsrc_x, src_off[t] + (uint32_t)kc,
+                                      kend - (kc + (int)src_chunk[t]));
+        *(uint4 *)(ring + slot * SLOT + t * 1024 + lane * 16) = v;
+      }
     }
-    __syncthreads();
-    if (wk > 0) return;
-#pragma unroll
-    for (int o = 1; o < WK; ++o)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[mb][e] += red[((((o - 1) * WN + wn) * MB + mb) * 16 + e) * 64 + lane];
-  }
+  };
 
-  const v4i rsrc_s = make_rsrc(a.scale, (uint32_t)a.N * 4u);
+  v4f acc[RB][MB];
 #pragma unroll
-  for (int qd = 0; qd < 4; ++qd) {
-    const int n = nw0 + 8 * qd + 4 * g;
-    float sc[4];
-    if (!PARTIAL) {
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sc[e] = llvm_buffer_load_f32(rsrc_s, (uint32_t)(n + e) * 4u, 0, 0);
+    for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int g = lane >> 4, lr = lane & 15;
+  const int sw = swz16(lr);  // 16 rb and 16 mb leave the swizzle unchanged
+  const int c0 = (2 * g) ^ sw, c1 = (2 * g + 1) ^ sw;
+
+  for (int j = 0; j < D && j < my; ++j) issue(j);
+  for (int j = 0; j < my; ++j) {
+    const int ahead = min(D - 1, my - 1 - j);  // chunks issued after j
+    if (ahead >= 2) vm_wait_fence<2 * OPS>();
+    else if (ahead == 1) vm_wait_fence<OPS>();
+    else vm_wait_fence<0>();
+    const uint8_t *sl = ring + (j % D) * SLOT;
+    v8i af[RB], bf[MB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint8_t *row = sl + (16 * rb + lr) * 128;
+      const uint4 lo = *(const uint4 *)(row + (c0 << 4)), hi = *(const uint4 *)(row + (c1 << 4));
+      af[rb] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int m = 32 * mb + lr;
-      if (m >= a.M) continue;
-      const float v0 = acc[mb][4 * qd + 0], v1 = acc[mb][4 * qd + 1];
-      const float v2 = acc[mb][4 * qd + 2], v3 = acc[mb][4 * qd + 3];
-      if (PARTIAL) {
-        float *pr = a.P + ((size_t)s * a.M + m) * a.N;
-        if (VEC) {
-          if (n < a.N) *(float4 *)(pr + n) = make_float4(v0, v1, v2, v3);
-        } else {
-          if (n + 0 < a.N) pr[n + 0] = v0;
-          if (n + 1 < a.N) pr[n + 1] = v1;
-          if (n + 2 < a.N) pr[n + 2] = v2;
-          if (n + 3 < a.N) pr[n + 3] = v3;
-        }
+      const uint8_t *row = sl + (R + 16 * mb + lr) * 128;
+      const uint4 lo = *(const uint4 *)(row + (c0 << 4)), hi = *(const uint4 *)(row + (c1 << 4));
+      bf[mb] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    if (j + D < my) {
+      lgkm_wait_fence();  // this slot's reads are done before it is refilled
+      issue(j + D);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = mfma16(af[rb], bf[mb], acc[rb][mb]);
+  }
+
+  // Add the four waves' sums in wave order; wave v finishes blocks v, v+4, ...
+  __syncthreads();
+  float *red = (float *)smem;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[(((wave * RB + rb) * MB + mb) * 4 + e) * 64 + lane] = acc[rb][mb][e];
+  __syncthreads();
+  const v4i rsrc_s = make_rsrc(a.scale, (uint32_t)a.N * 4u);
+  for (int b = wave; b < RB * MB; b += 4) {
+    const int rb = b / MB, mb = b % MB;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float t = red[((b) * 4 + e) * 64 + lane];
+#pragma unroll
+      for (int o = 1; o < 4; ++o) t += red[((o * RB * MB + b) * 4 + e) * 64 + lane];
+      v[e] = t;
+    }
+    const int n = n0 + 16 * rb + 4 * g;
+    const int m = 16 * mb + lr;
+    if (m >= a.M) continue;
+    if (gridDim.y > 1) {
+      float *pr = a.P + ((size_t)s * a.M + m) * a.N;
+      if (a.vec) {
+        if (n < a.N) *(float4 *)(pr + n) = make_float4(v[0], v[1], v[2], v[3]);
       } else {
-        uint16_t *yr = a.y + (size_t)m * a.N;
-        const uint32_t b0 = bf16_rne(v0 * sc[0]), b1 = bf16_rne(v1 * sc[1]);
-        const uint32_t b2 = bf16_rne(v2 * sc[2]), b3 = bf16_rne(v3 * sc[3]);
-        if (VEC) {
-          if (n < a.N) *(uint2 *)(yr + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-        } else {
-          if (n + 0 < a.N) yr[n + 0] = (uint16_t)b0;
-          if (n + 1 < a.N) yr[n + 1] = (uint16_t)b1;
-          if (n + 2 < a.N) yr[n + 2] = (uint16_t)b2;
-          if (n + 3 < a.N) yr[n + 3] = (uint16_t)b3;
-        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) pr[n + e] = v[e];
+      }
+    } else {
+      uint16_t *yr = a.y + (size_t)m * a.N;
+      uint32_t bits[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bits[e] = bf16_rne(v[e] * llvm_buffer_load_f32(rsrc_s, (uint32_t)(n + e) * 4u, 0, 0));
+      if (a.vec) {
+        if (n < a.N) *(uint2 *)(yr + n) = make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) yr[n + e] = (uint16_t)bits[e];
       }
     }
   }
@@ -553,15 +660,14 @@ __global__ __launch_bounds__(256) void fp8g_zero_kernel(uint16_t *__restrict__ y
 
 // ------------------------------------------------------------------ launchers
 static const MainConfig kMainConfigs[] = {
-    {1, 256, 256, 128, 2},
-    {2, 128, 128, 128, 2},
-    {3, 64, 64, 128, 2},
-    {4, 256, 256, 64, 4},
+    {1, 256, 256, 64, 4},  // 8 waves, wave tile 64 (m) x 128 (n)
+    {2, 128, 128, 64, 4},  // 4 waves, two workgroups per CU
+    {3, 64, 64, 128, 3},   // 4 waves, small problems
+    {4, 256, 256, 64, 4},  // 8 waves, wave tile 128 (m) x 64 (n)
+    {5, 256, 256, 64, 4},  // 4 waves, one per SIMD
 };
 static const SkinnyConfig kSkinnyConfigs[] = {
-    {1, 4},
-    {2, 2},
-    {3, 1},
+    {1, 1}, {2, 2}, {3, 3}, {4, 4}, {5, 5},
 };
 
 const MainConfig *main_config(int id) {
@@ -574,7 +680,8 @@ const SkinnyConfig *skinny_config(int id) {
     if (c.id == id) return &c;
   return nullptr;
 }
-int skinny_tile_n(const SkinnyConfig &c) { return 32 * (4 / c.waves_k); }
+int skinny_tile_n(const SkinnyConfig &c) { return 16 * c.row_blocks; }
+int skinny_max_row_blocks(int M) { return M <= 16 ? 5 : (M <= 32 ? 4 : 2); }
 int skinny_chunk_bytes() { return 128; }
 
 template <int BM, int BN, int BK, int STAGES, int WM, int WN>
@@ -593,29 +700,22 @@ static hipError_t launch_main_cfg(const MainLaunch &l, hipStream_t stream) {
 
 hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
   switch (l.variant) {
-    case 1: return launch_main_cfg<256, 256, 128, 2, 2, 2>(l, stream);
-    case 2: return launch_main_cfg<128, 128, 128, 2, 2, 2>(l, stream);
-    case 3: return launch_main_cfg<64, 64, 128, 2, 2, 2>(l, stream);
-    case 4: return launch_main_cfg<256, 256, 64, 4, 2, 2>(l, stream);
+    case 1: return launch_main_cfg<256, 256, 64, 4, 4, 2>(l, stream);
+    case 2: return launch_main_cfg<128, 128, 64, 4, 2, 2>(l, stream);
+    case 3: return launch_main_cfg<64, 64, 128, 3, 2, 2>(l, stream);
+    case 4: return launch_main_cfg<256, 256, 64, 4, 2, 4>(l, stream);
+    case 5: return launch_main_cfg<256, 256, 64, 4, 2, 2>(l, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int MB, int WK>
+template <int RB, int MB>
 static hipError_t launch_skinny_cfg(const SkinnyLaunch &l, hipStream_t stream) {
-  SkinnyArgs a{l.x, l.w, l.scale, l.y, l.partials, l.M, l.N, l.K, l.k_slice};
-  constexpr int tile_n = 32 * (4 / WK);
-  const dim3 grid((unsigned)((l.N + tile_n - 1) / tile_n), (unsigned)l.S), block(256);
-  const bool partial = l.S > 1;
-  if (partial) {
-    if (l.N % 4 == 0) fp8g_splitk_partial_kernel<MB, WK, true, true><<<grid, block, 0, stream>>>(a);
-    else fp8g_splitk_partial_kernel<MB, WK, true, false><<<grid, block, 0, stream>>>(a);
-  } else {
-    if (l.vec) fp8g_splitk_partial_kernel<MB, WK, false, true><<<grid, block, 0, stream>>>(a);
-    else fp8g_splitk_partial_kernel<MB, WK, false, false><<<grid, block, 0, stream>>>(a);
-  }
+  SkinnyArgs a{l.x, l.w, l.scale, l.y, l.partials, l.M, l.N, l.K, l.k_slice, l.N % 4 == 0 && (l.S > 1 || l.vec)};
+  const dim3 grid((unsigned)((l.N + 16 * RB - 1) / (16 * RB)), (unsigned)l.S), block(256);
+  fp8g_splitk_partial_kernel<RB, MB><<<grid, block, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !partial) return e;
+  if (e != hipSuccess || l.S == 1) return e;
   const int64_t threads = (int64_t)l.M * ((l.N + 3) / 4);
   const dim3 rgrid((unsigned)((threads + 255) / 256));
   if (l.vec) fp8g_splitk_reduce_kernel<true><<<rgrid, block, 0, stream>>>(l.partials, l.scale, l.y, l.M, l.N, l.S);
@@ -623,14 +723,23 @@ static hipError_t launch_skinny_cfg(const SkinnyLaunch &l, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_skinny(const SkinnyLaunch &l, hipStream_t stream) {
-  const bool two = l.M > 32;
+template <int MB>
+static hipError_t launch_skinny_mb(const SkinnyLaunch &l, hipStream_t stream) {
   switch (l.variant) {
-    case 1: return two ? launch_skinny_cfg<2, 4>(l, stream) : launch_skinny_cfg<1, 4>(l, stream);
-    case 2: return two ? launch_skinny_cfg<2, 2>(l, stream) : launch_skinny_cfg<1, 2>(l, stream);
-    case 3: return two ? launch_skinny_cfg<2, 1>(l, stream) : launch_skinny_cfg<1, 1>(l, stream);
-    default: return hipErrorInvalidValue;
+    case 1: return launch_skinny_cfg<1, MB>(l, stream);
+    case 2: return launch_skinny_cfg<2, MB>(l, stream);
+    case 3: if constexpr (MB <= 2) return launch_skinny_cfg<3, MB>(l, stream); else break;
+    case 4: if constexpr (MB <= 2) return launch_skinny_cfg<4, MB>(l, stream); else break;
+    case 5: if constexpr (MB == 1) return launch_skinny_cfg<5, MB>(l, stream); else break;
+    default: break;
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_skinny(const SkinnyLaunch &l, hipStream_t stream) {
+  if (l.M <= 16) return launch_skinny_mb<1>(l, stream);
+  if (l.M <= 32) return launch_skinny_mb<2>(l, stream);
+  return launch_skinny_mb<4>(l, stream);
 }
 
 hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream) {

@@ -43,10 +43,15 @@ def test_splitk_full(M, split_k):
     _full_case(M, 1000, 4127, path=fg.PATH_SPLITK, split_k=split_k)
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
 def test_splitk_variants(variant):
-    _full_case(40, 777, 3000, path=fg.PATH_SPLITK, variant=variant, split_k=3)
-    _full_case(32, 1024, 4096, path=fg.PATH_SPLITK, variant=variant, split_k=1)
+    """Every rows-per-workgroup configuration (16 * variant rows), with and
+    without split-K, for each x-row staging width the variant supports."""
+    if variant <= 2:
+        _full_case(40, 777, 3000, path=fg.PATH_SPLITK, variant=variant, split_k=3)
+    if variant <= 4:
+        _full_case(32, 1024, 4096, path=fg.PATH_SPLITK, variant=variant, split_k=1)
+    _full_case(16, 1000, 4127, path=fg.PATH_SPLITK, variant=variant, split_k=2)
 
 
 # ---------------------------------------------------- the benchmark shapes ----
