@@ -51,6 +51,34 @@ def bound_of(wl) -> str:
     return "mfma" if wl.flops / (PEAK_FP8_TFLOPS * 1e12) >= wl.bytes / (PEAK_HBM_GBPS * 1e9) else "hbm"
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "fp8_gemm_channel_amd", "csrc", "fp8g_kernels.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_main_kernel_square-8192_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None when the summary is missing, covers another
+    workload, or was taken on a different kernel source."""
+    try:
+        fields = {}
+        with open(TRAFFIC_SUMMARY) as f:
+            for line in f:
+                if line.startswith("- ") and ":" in line:
+                    k, v = line[2:].split(":", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("workload") != workload or fields.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return int(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(workloads, inputs, budget_fma: float) -> dict:
     """The CPU oracle on a bounded sample of each shape's outputs: per shape,
     as many output elements (seeded positions) as fit `budget_fma` products.
@@ -99,6 +127,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=4e10, help="oracle products per shape")
     ap.add_argument("--only", default="", help="comma-separated workload names (default: all five)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (3 times); used to "
+                         "calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE against a kernel of known traffic")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -115,6 +146,15 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 3}), flush=True)
+        return 0
 
     workloads = [w for w in synth.WORKLOADS if not args.only or w.name in args.only.split(",")]
     inputs, dev_bufs = {}, {}
@@ -183,7 +223,7 @@ def main() -> int:
                 "peak": PEAK_FP8_TFLOPS if bound_of(dom) == "mfma" else PEAK_HBM_GBPS,
                 "unit": "TFLOP/s" if bound_of(dom) == "mfma" else "GB/s",
                 "avg_launch_us": round(dom_t * 1e6, 2),
-                "traffic": None}
+                "traffic": measured_traffic(dom.name)}
     roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
 
     cpu = None
