@@ -73,7 +73,7 @@ __device__ __forceinline__ uint4 as_u4(v4i v) {
 
 // 16 bytes at `off`, of which only the first `valid` (< 16) may be read; the
 // rest are zero.  Byte loads: each one is range-checked on its own.
-__device__ __noinline__ uint4 load16_partial(v4i rsrc, uint32_t off, int valid) {
+__device__ __forceinline__ uint4 load16_partial(v4i rsrc, uint32_t off, int valid) {
   uint32_t d[4] = {0u, 0u, 0u, 0u};
   for (int j = 0; j < valid; ++j) {
     uint32_t b = (uint8_t)llvm_buffer_load_i8(rsrc, off + j, 0, 0);
@@ -168,15 +168,19 @@ __device__ __forceinline__ void interleave_mfma_reads() {
   }
 }
 
-// Software pipeline of one K step (BK bytes, BK/64 MFMA sub-steps):
+// Software pipeline.  A K step is BK bytes (one stage buffer), worked as BK/64
+// MFMA sub-steps; F[u & 1] holds the operands of sub-step u.  Sub-step u:
 //
-//     wait for this wave's DMA of step k+1, workgroup barrier
-//     LDS-DMA of step k+STAGES-1 into the buffer step k-1 used
-//     MFMAs of step k (operands in registers F[k&1]), interleaved with the LDS
-//     reads of step k+1's operands into F[(k+1)&1]
+//     [last sub-step of step s only] wait for this wave's DMA of step s+1,
+//         workgroup barrier, LDS-DMA of step s+DIST into a retired buffer
+//     MFMAs of sub-step u (operands in F[u & 1]), interleaved with the LDS
+//     reads of sub-step u+1's operands into F[(u+1) & 1]
 //
-// The barrier publishes step k+1 (every wave's DMA has landed) and retires the
-// buffer of step k-1 (every wave read its operands before the barrier).
+// The barrier publishes step s+1 (every wave's DMA has landed) and retires the
+// buffer of step s (every wave has read its operands).  BK = 128 halves the
+// barriers and has each DMA instruction fetch 8 rows x 128 bytes instead of
+// 16 rows x 64 bytes, which the global-to-LDS path serves faster (measured on
+// MI355X: ~7% on 4096^3 and 8192^3).
 // With 8 waves per workgroup two waves share each SIMD, so one wave's MFMAs
 // cover the other's barrier and LDS waits; a single wave per SIMD can neither
 // keep the matrix pipe full nor keep enough LDS reads in flight (measured on
@@ -194,12 +198,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   constexpr int BLOCKS = STAGE_BYTES / 1024;
   constexpr int DPW = BLOCKS / NWAVES;       // DMA instructions per wave per stage
   constexpr int W_DPW = (BN / ROWS_PER_KB) / NWAVES;  // of which fill w rows
-  constexpr int NMFMA = SUB * FN * FM;       // MFMAs per wave per step
-  constexpr int NREAD = SUB * (FN + FM) * 2; // 16-byte LDS reads per wave per step
+  constexpr int NMFMA = FN * FM;             // MFMAs per wave per 64-byte sub-step
+  constexpr int NREAD = (FN + FM) * 2;       // 16-byte LDS reads per wave per sub-step
+  // Prefetch distance in steps.  BK = 64: step k+STAGES-1 goes into the buffer
+  // retired one barrier earlier (issuing one step further ahead measured no
+  // faster).  BK = 128: step k+STAGES goes into the buffer of step k itself,
+  // which a step's last sub-step retires.
+  constexpr int DIST = SUB == 1 ? STAGES - 1 : STAGES;
   static_assert(BK == 64 || BK == 128, "BK");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
   static_assert(BLOCKS % NWAVES == 0 && (BN / ROWS_PER_KB) % NWAVES == 0, "DMA split");
-  static_assert(STAGES >= 3 && (STAGES - 2) * DPW < 64, "vmcnt range");
+  static_assert(DIST >= 2 && DIST <= 5 && (DIST - 1) * DPW < 64, "vmcnt range");
   static_assert(BN <= 256, "one DMA instruction stages the tile's scales");
 
   // Stage ring, then the tile's BN scales.
@@ -230,8 +239,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   const int K = a.K;
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
-  const v4i rsrc_x = make_rsrc(a.x + (size_t)m0 * K, (uint32_t)rows_x * (uint32_t)K);
-  const v4i rsrc_w = make_rsrc(a.w + (size_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
+  // A tile's rows form one range of at most 256 * (2^24 - 1) bytes, so an
+  // offset equal to it never wraps 32 bits; rows past M / N read zero.
+  const uint32_t range_x = (uint32_t)rows_x * (uint32_t)K, range_w = (uint32_t)rows_w * (uint32_t)K;
 
   const int g = lane >> 5, lr = lane & 31;
   const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
@@ -245,41 +255,70 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
     dma16(rsrc_s, scale_lds, (uint32_t)lane * 16u, 0u);
   }
 
-  // Lane's tile row and logical chunk in DMA instruction t, which fills 1 KiB
-  // block t*NWAVES + wave of a stage (w rows first, then x rows).
-  auto dma_row = [&](int t) __attribute__((always_inline)) {
-    const int R = (t * NWAVES + wave) * ROWS_PER_KB + lane / CH;
-    return (t < W_DPW) ? R : R - BN;
-  };
-  auto dma_chunk = [&](int t) __attribute__((always_inline)) { return (lane % CH) ^ swz<BK>(dma_row(t)); };
-  uint32_t src_off[DPW];  // source offsets without the K step
+  // DMA instruction t of a wave fills 1 KiB block t*NWAVES + wave of a stage
+  // (w rows first, then x rows): ROWS_PER_KB rows of BK bytes, lane l taking
+  // row l / CH of the block and logical chunk (l % CH) ^ swz(row).  Blocks
+  // start at multiples of ROWS_PER_KB rows and NWAVES is even, so the row bits
+  // the swizzle reads are the same in every block: each lane has one source
+  // offset relative to its block and one chunk for all t, and block t gets
+  // its own descriptor (base moved to the block's first row, range cut to
+  // match, so rows past M / N still read zero).
+  static_assert(NWAVES % 2 == 0 && BN % 16 == 0, "block-invariant swizzle");
+  const int dma_lrow = wave * ROWS_PER_KB + lane / CH;  // row within block t = 0
+  const int dma_chunk = (lane % CH) ^ swz<BK>(dma_lrow);
+  const uint32_t lane_off = (uint32_t)dma_lrow * (uint32_t)K + (uint32_t)dma_chunk * 16u;
+  const uint32_t blk_stride = (uint32_t)(NWAVES * ROWS_PER_KB) * (uint32_t)K;
+  v4i rs[DPW];
 #pragma unroll
-  for (int t = 0; t < DPW; ++t) src_off[t] = (uint32_t)dma_row(t) * (uint32_t)K + (uint32_t)dma_chunk(t) * 16u;
+  for (int t = 0; t < DPW; ++t) {
+    const int tt = t < W_DPW ? t : t - W_DPW;
+    const uint32_t range = t < W_DPW ? range_w : range_x;
+    const uint32_t skip = (uint32_t)tt * blk_stride;  // < 256 * K: no wrap
+    const uint8_t *base = t < W_DPW ? a.w + (size_t)n0 * K : a.x + (size_t)m0 * K;
+    rs[t] = make_rsrc(base + skip, range > skip ? range - skip : 0u);
+  }
+
+  const int nk_full_c = K / BK;  // K steps that lie entirely before K
 
   // Full K step kt -> stage buffer `st` via LDS-DMA.
   auto issue_full = [&](int kt, int st) __attribute__((always_inline)) {
     const uint32_t k0 = (uint32_t)kt * BK;
     const uint32_t sb = smem_base + (uint32_t)st * STAGE_BYTES;
 #pragma unroll
-    for (int t = 0; t < DPW; ++t) {
-      const uint32_t lds = sb + (uint32_t)(t * NWAVES + wave) * 1024u;
-      dma16(t < W_DPW ? rsrc_w : rsrc_x, lds, src_off[t], k0);
-    }
+    for (int t = 0; t < DPW; ++t) dma16(rs[t], sb + (uint32_t)(t * NWAVES + wave) * 1024u, lane_off, k0);
   };
-  // Last, partial K step -> stage buffer `st` through registers, bytes at or
-  // past K zeroed.  Same block/lane mapping as the DMA path.
+  // Last, partial K step (k0 + BK > K) -> stage buffer `st`, also by LDS-DMA:
+  // chunks entirely before K load as usual, chunks at or past K are pointed out
+  // of range and land as zeros, and the one chunk per row that straddles K is
+  // zeroed the same way here and rebuilt later by fix_tail.
   auto issue_tail = [&](int kt, int st) __attribute__((always_inline)) {
     const int k0 = kt * BK;
-    uint8_t *sb = smem + st * STAGE_BYTES;
+    const uint32_t sb = smem_base + (uint32_t)st * STAGE_BYTES;
+    const int valid = K - (k0 + 16 * dma_chunk);
+    // range_w / range_x bound every block's cut range from above
+    const uint32_t off_w = valid >= 16 ? lane_off + (uint32_t)k0 : range_w;
+    const uint32_t off_x = valid >= 16 ? lane_off + (uint32_t)k0 : range_x;
 #pragma unroll
-    for (int t = 0; t < DPW; ++t) {
-      const int valid = K - (k0 + 16 * dma_chunk(t));
-      const uint4 v = load16_masked(t < W_DPW ? rsrc_w : rsrc_x, src_off[t] + (uint32_t)k0, valid);
-      *(uint4 *)(sb + (t * NWAVES + wave) * 1024 + lane * 16) = v;
+    for (int t = 0; t < DPW; ++t) dma16(rs[t], sb + (uint32_t)(t * NWAVES + wave) * 1024u, t < W_DPW ? off_w : off_x, 0u);
+  };
+  // Rebuild the straddling chunks of the tail stage with byte loads (each byte
+  // range-checked on its own), bytes at or past K zero.  Called once every DMA
+  // of the tail stage has landed and before the barrier that publishes it; the
+  // barrier's LDS wait covers these writes.
+  auto fix_tail = [&](int st) __attribute__((always_inline)) {
+    const int k0 = nk_full_c * BK;
+    uint8_t *sb = smem + st * STAGE_BYTES;
+    const int valid = K - (k0 + 16 * dma_chunk);
+    if (valid > 0 && valid < 16) {
+#pragma unroll
+      for (int t = 0; t < DPW; ++t) {
+        const uint4 v = load16_partial(rs[t], lane_off + (uint32_t)k0, valid);
+        *(uint4 *)(sb + (t * NWAVES + wave) * 1024 + lane * 16) = v;
+      }
     }
   };
-  const int nk_full = K / BK;
-  const int nk = nk_full + (KTAIL ? 1 : 0);
+  const int nk = nk_full_c + (KTAIL ? 1 : 0);
+  const int nk_full = nk_full_c;
   auto issue = [&](int kt) __attribute__((always_inline)) {
     if (kt < nk_full) issue_full(kt, kt % STAGES);
     else if (KTAIL && kt == nk_full) issue_tail(kt, kt % STAGES);
@@ -291,24 +330,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   const int bx_row = wave_m * TM + lr;  // x row of block 0
   const int sa = swz<BK>(aw_row), sbx = swz<BK>(bx_row);  // 32 i leaves the swizzle unchanged
 
-  v8i fa[2][SUB][FN], fb[2][SUB][FM];
-  // LDS read number q of a step (q in [0, NREAD)): per sub-step j, first the
-  // FN w blocks then the FM x blocks, low then high 16 bytes.
-  auto read_one = [&](int st, int q, v8i (&af)[SUB][FN], v8i (&bf)[SUB][FM]) __attribute__((always_inline)) {
-    const int j = q / ((FN + FM) * 2), rest = q % ((FN + FM) * 2);
-    const int blk = rest / 2, half = rest % 2;
+  // Operand registers of two sub-steps: F[u & 1] holds sub-step u.
+  v8i fa[2][FN], fb[2][FM];
+  // LDS read number q (q in [0, NREAD)) of sub-step j of stage `st`: low then
+  // high 16 bytes of each block, blocks in the order the MFMAs first use them
+  // (w block 0, all FM x blocks, then w blocks 1 .. FN-1).
+  auto read_one = [&](int st, int j, int q, v8i (&af)[FN], v8i (&bf)[FM]) __attribute__((always_inline)) {
+    const int ord = q / 2, half = q % 2;
+    const int blk = ord == 0 ? 0 : (ord <= FM ? FN + ord - 1 : ord - FM);
     const int c = 4 * j + 2 * g + half;
     const uint8_t *sw_ = smem + st * STAGE_BYTES;
     if (blk < FN) {
       const uint8_t *row = sw_ + (aw_row + 32 * blk) * BK;
       const uint4 v = *(const uint4 *)(row + ((c ^ sa) << 4));
-      af[j][blk][4 * half + 0] = (int)v.x; af[j][blk][4 * half + 1] = (int)v.y;
-      af[j][blk][4 * half + 2] = (int)v.z; af[j][blk][4 * half + 3] = (int)v.w;
+      af[blk][4 * half + 0] = (int)v.x; af[blk][4 * half + 1] = (int)v.y;
+      af[blk][4 * half + 2] = (int)v.z; af[blk][4 * half + 3] = (int)v.w;
     } else {
       const uint8_t *row = sw_ + BN * BK + (bx_row + 32 * (blk - FN)) * BK;
       const uint4 v = *(const uint4 *)(row + ((c ^ sbx) << 4));
-      bf[j][blk - FN][4 * half + 0] = (int)v.x; bf[j][blk - FN][4 * half + 1] = (int)v.y;
-      bf[j][blk - FN][4 * half + 2] = (int)v.z; bf[j][blk - FN][4 * half + 3] = (int)v.w;
+      bf[blk - FN][4 * half + 0] = (int)v.x; bf[blk - FN][4 * half + 1] = (int)v.y;
+      bf[blk - FN][4 * half + 2] = (int)v.z; bf[blk - FN][4 * half + 3] = (int)v.w;
     }
   };
 
@@ -320,58 +361,78 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Prologue: DMA of steps 0 .. STAGES-2, then step 0's operands.
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue(s);
-  {
-    const int ahead = min(STAGES - 2, nk - 1);
-    if (ahead >= 2) vm_wait<2 * DPW>();
+  // Wait until this wave's DMA of a step has landed while the `ahead` (<= 4)
+  // steps issued after it may stay in flight (vmcnt completes in order).
+  auto wait_ahead = [&](int ahead) __attribute__((always_inline)) {
+    if (ahead >= 4) vm_wait<4 * DPW>();
+    else if (ahead == 3) vm_wait<3 * DPW>();
+    else if (ahead == 2) vm_wait<2 * DPW>();
     else if (ahead == 1) vm_wait<DPW>();
     else vm_wait<0>();
+  };
+
+  // Prologue: DMA of steps 0 .. DIST-1, then sub-step 0's operands.
+#pragma unroll
+  for (int s = 0; s < DIST; ++s) issue(s);
+  wait_ahead(min(DIST - 1, nk - 1));
+  if (KTAIL && nk_full == 0) {  // the tail is step 0: every DMA issued so far has landed
+    vm_wait<0>();
+    fix_tail(0);
   }
   __syncthreads();
 #pragma unroll
-  for (int q = 0; q < NREAD; ++q) read_one(0, q, fa[0], fb[0]);
+  for (int q = 0; q < NREAD; ++q) read_one(0, 0, q, fa[0], fb[0]);
 
-  // Two steps per trip so the register buffers F[0] / F[1] are compile-time.
-  auto step = [&](const int kt, const int cur) __attribute__((always_inline)) {
+  // Sub-step u (step s = u / SUB, part j = u % SUB): MFMAs on F[cur],
+  // interleaved with the reads of sub-step u+1 into F[cur ^ 1].  The last
+  // sub-step of a step is a boundary: before it, step s+1 must be published.
+  const int nsub = nk * SUB;
+  auto substep = [&](const int u, const int cur, const bool boundary) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    // own DMA of step kt+1 must have landed; later stages may stay in flight
-    const int ahead = min(STAGES - 3, nk - 2 - kt);
-    if constexpr (STAGES >= 5) {
-      if (ahead >= 2) vm_wait<2 * DPW>();
-      else if (ahead == 1) vm_wait<DPW>();
-      else vm_wait<0>();
-    } else if constexpr (STAGES == 4) {
-      if (ahead >= 1) vm_wait<DPW>();
-      else vm_wait<0>();
-    } else {
-      vm_wait<0>();
+    const int s = u / SUB;
+    if (boundary) {
+      // Own DMA of step s+1 must have landed; steps s+2 .. s+DIST-1 (issued
+      // earlier) may stay in flight.
+      wait_ahead(min(DIST - 2, nk - 2 - s));
+      // step s+1 is the tail: the wait above covered its DMA (nothing is
+      // issued after the tail), so rebuild its straddling chunks before
+      // publishing it
+      if (KTAIL && s + 1 == nk_full) fix_tail((s + 1) % STAGES);
+      // After this barrier every wave has read all operands of step s (the
+      // last of them during the previous sub-step), so its buffer is free;
+      // so is the buffer of step s-1.  Step s+DIST goes into one of them.
+      __syncthreads();
+      issue(s + DIST);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-    issue(kt + STAGES - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    const bool more = kt + 1 < nk;
-    const int st = (kt + 1) % STAGES;
+    const bool more = u + 1 < nsub;
+    const int un = u + 1;
+    const int st = (un / SUB) % STAGES, jn = un % SUB;
 #pragma unroll
     for (int q = 0; q < NMFMA; ++q) {
-      const int j = q / (FN * FM), i = (q / FM) % FN, jm = q % FM;
-      acc[i][jm] = mfma32(fa[cur][j][i], fb[cur][j][jm], acc[i][jm]);
+      const int i = q / FM, jm = q % FM;
+      acc[i][jm] = mfma32(fa[cur][i], fb[cur][jm], acc[i][jm]);
       if (more) {
 #pragma unroll
-        for (int r = q * NREAD / NMFMA; r < (q + 1) * NREAD / NMFMA; ++r) read_one(st, r, fa[cur ^ 1], fb[cur ^ 1]);
+        for (int r = q * NREAD / NMFMA; r < (q + 1) * NREAD / NMFMA; ++r) read_one(st, jn, r, fa[cur ^ 1], fb[cur ^ 1]);
       }
     }
     interleave_mfma_reads<0, NMFMA, NREAD>();
     __builtin_amdgcn_sched_barrier(0);
   };
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, 0);
-    step(kt + 1, 1);
+  if constexpr (SUB == 1) {
+    int u = 0;
+    for (; u + 1 < nsub; u += 2) {
+      substep(u, 0, true);
+      substep(u + 1, 1, true);
+    }
+    if (u < nsub) substep(u, 0, true);
+  } else {
+    for (int s = 0; s < nk; ++s) {
+      substep(2 * s, 0, false);
+      substep(2 * s + 1, 1, true);
+    }
   }
-  if (kt < nk) step(kt, 0);
-
   // Epilogue: y[m, n..n+3] = bf16(acc * scale[n..n+3]).
   const float *s_lds = (const float *)(smem + STAGES * STAGE_BYTES);
 #pragma unroll
@@ -665,6 +726,8 @@ static const MainConfig kMainConfigs[] = {
     {3, 64, 64, 128, 3},   // 4 waves, small problems
     {4, 256, 256, 64, 4},  // 8 waves, wave tile 128 (m) x 64 (n)
     {5, 256, 256, 64, 4},  // 4 waves, one per SIMD
+    {6, 256, 256, 128, 2}, // 8 waves, wave tile 64 (m) x 128 (n), 128-byte K steps
+    {7, 256, 256, 128, 2}, // 8 waves, wave tile 128 (m) x 64 (n), 128-byte K steps
 };
 static const SkinnyConfig kSkinnyConfigs[] = {
     {1, 1}, {2, 2}, {3, 3}, {4, 4}, {5, 5},
@@ -705,6 +768,8 @@ hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
     case 3: return launch_main_cfg<64, 64, 128, 3, 2, 2>(l, stream);
     case 4: return launch_main_cfg<256, 256, 64, 4, 2, 4>(l, stream);
     case 5: return launch_main_cfg<256, 256, 64, 4, 2, 2>(l, stream);
+    case 6: return launch_main_cfg<256, 256, 128, 2, 4, 2>(l, stream);
+    case 7: return launch_main_cfg<256, 256, 128, 2, 2, 4>(l, stream);
     default: return hipErrorInvalidValue;
   }
 }
