@@ -82,10 +82,31 @@ __device__ __forceinline__ uint4 load16_partial(v4i rsrc, uint32_t off, int vali
   return make_uint4(d[0], d[1], d[2], d[3]);
 }
 
-// 16 bytes at `off` with `valid` bytes before the end of the row (any value).
-__device__ __forceinline__ uint4 load16_masked(v4i rsrc, uint32_t off, int valid) {
+// The same for 0 < valid < 16 when the row holds at least 16 bytes up to
+// off + valid (i.e. K >= 16): one 16-byte load that ends at the last valid
+// byte, moved down by 16 - valid bytes (whole dwords first, then the byte
+// remainder with a funnel shift) so the bytes past the row come in as zeros.
+// One memory round trip instead of `valid` dependent byte loads.
+__device__ __forceinline__ uint4 load16_tail(v4i rsrc, uint32_t off, int valid) {
+  const v4i v = llvm_buffer_load_v4i32(rsrc, off + (uint32_t)valid - 16u, 0, 0);
+  const int sh = 16 - valid;  // 1 .. 15
+  const int q = sh >> 2, r = sh & 3;
+  const uint32_t d0 = (uint32_t)v.x, d1 = (uint32_t)v.y, d2 = (uint32_t)v.z, d3 = (uint32_t)v.w;
+  const uint32_t e0 = q == 0 ? d0 : q == 1 ? d1 : q == 2 ? d2 : d3;
+  const uint32_t e1 = q == 0 ? d1 : q == 1 ? d2 : q == 2 ? d3 : 0u;
+  const uint32_t e2 = q == 0 ? d2 : q == 1 ? d3 : 0u;
+  const uint32_t e3 = q == 0 ? d3 : 0u;
+  // alignbyte(hi, lo, r) = low 32 bits of ({hi, lo} >> 8r)
+  return make_uint4(__builtin_amdgcn_alignbyte(e1, e0, r), __builtin_amdgcn_alignbyte(e2, e1, r),
+                    __builtin_amdgcn_alignbyte(e3, e2, r), __builtin_amdgcn_alignbyte(0u, e3, r));
+}
+
+// 16 bytes at `off` with `valid` bytes before the end of the row (any value);
+// K is the row length.
+__device__ __forceinline__ uint4 load16_masked(v4i rsrc, uint32_t off, int valid, int K) {
   if (valid >= 16) return as_u4(llvm_buffer_load_v4i32(rsrc, off, 0, 0));
   if (valid <= 0) return make_uint4(0u, 0u, 0u, 0u);
+  if (K >= 16) return load16_tail(rsrc, off, valid);
   return load16_partial(rsrc, off, valid);
 }
 
@@ -301,8 +322,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
 #pragma unroll
     for (int t = 0; t < DPW; ++t) dma16(rs[t], sb + (uint32_t)(t * NWAVES + wave) * 1024u, t < W_DPW ? off_w : off_x, 0u);
   };
-  // Rebuild the straddling chunks of the tail stage with byte loads (each byte
-  // range-checked on its own), bytes at or past K zero.  Called once every DMA
+  // Rebuild the straddling chunks of the tail stage (one shifted 16-byte load
+  // each, or byte loads when K < 16), bytes at or past K zero.  Called once every DMA
   // of the tail stage has landed and before the barrier that publishes it; the
   // barrier's LDS wait covers these writes.
   auto fix_tail = [&](int st) __attribute__((always_inline)) {
@@ -312,7 +333,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
     if (valid > 0 && valid < 16) {
 #pragma unroll
       for (int t = 0; t < DPW; ++t) {
-        const uint4 v = load16_partial(rs[t], lane_off + (uint32_t)k0, valid);
+        const uint4 v = K >= 16 ? load16_tail(rs[t], lane_off + (uint32_t)k0, valid)
+                                : load16_partial(rs[t], lane_off + (uint32_t)k0, valid);
         *(uint4 *)(sb + (t * NWAVES + wave) * 1024 + lane * 16) = v;
       }
     }
@@ -586,7 +608,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_splitk_partial_kernel(SkinnyArgs 
 #pragma unroll
       for (int t = 0; t < OPS; ++t) {
         const uint4 v = load16_masked(t < W_OPS ? rsrc_w : rsrc_x, src_off[t] + (uint32_t)kc,
-                                      kend - (kc + (int)src_chunk[t]));
+                                      kend - (kc + (int)src_chunk[t]), K);
         *(uint4 *)(ring + slot * SLOT + t * 1024 + lane * 16) = v;
       }
     }
