@@ -182,8 +182,9 @@ int run(const void *x, const void *w, const float *scale, void *y, int64_t M, in
     return e == hipSuccess ? FP8G_OK : hip_fail(e, "zero-fill launch");
   }
   if (p.path == FP8G_PATH_MAIN) {
+    const int ystore = (N % 8 == 0 && (uintptr_t)y % 16 == 0) ? 16 : vec ? 8 : 2;
     fp8g::MainLaunch l{(const uint8_t *)x, (const uint8_t *)w, scale, (uint16_t *)y, (int)M, (int)N, (int)K,
-                       (int)cdiv(M, p.tile_m), (int)cdiv(N, p.tile_n), p.group_m, p.variant, p.k_tail != 0, vec};
+                       (int)cdiv(M, p.tile_m), (int)cdiv(N, p.tile_n), p.group_m, p.variant, p.k_tail != 0, ystore};
     e = fp8g::launch_main(l, stream);
     return e == hipSuccess ? FP8G_OK : hip_fail(e, "main kernel launch");
   }

@@ -18,7 +18,7 @@ struct MainLaunch {
   int tiles_m, tiles_n, group_m;
   int variant;   // main-path configuration id
   bool k_tail;   // K % tile_k != 0
-  bool vec;      // y rows allow 8-byte stores (N % 4 == 0, y 8-byte aligned)
+  int ystore;    // widest y store: 16 (N % 8 == 0, y 16-byte aligned), 8 (N % 4 == 0, y 8-byte aligned) or 2
 };
 
 // One launch of the skinny split-K kernel (+ the reduce kernel when S > 1).

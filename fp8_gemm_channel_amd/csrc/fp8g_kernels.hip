@@ -175,6 +175,7 @@ struct MainArgs {
   uint16_t *y;
   int M, N, K;
   int tiles_m, tiles_n, group_m;
+  int ystore;  // widest y store allowed by N and y's alignment: 16, 8 or 2 bytes
 };
 
 // Scheduling pattern for NM MFMAs and NR LDS reads spread evenly: MFMA q is
@@ -207,7 +208,7 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 // keep the matrix pipe full nor keep enough LDS reads in flight (measured on
 // MI355X: ~4.0-4.5 vs ~4.8 PFLOP/s for back-to-back MFMAs, ~110 vs ~200
 // B/clk/CU for 16-byte LDS reads).
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool KTAIL, bool VEC>
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool KTAIL, bool PP>
 __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) {
   constexpr int NWAVES = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
@@ -402,6 +403,62 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
     fix_tail(0);
   }
   __syncthreads();
+
+  if constexpr (PP) {
+    // Ping-pong schedule.  Waves are dealt to the four SIMDs round-robin, so
+    // waves 0-3 (group 0) and 4-7 (group 1) put one wave of each group on every
+    // SIMD.  The groups alternate between two kinds of phase, separated by
+    // workgroup barriers: a compute phase issues the wave's 8 MFMAs of one K step
+    // back to back from registers; a memory phase reads the next K step's
+    // operands from LDS and issues the wave's LDS-DMA share of the step three
+    // ahead.  While one wave of a SIMD computes, the other one loads, so the
+    // matrix pipe of every SIMD is fed by one wave or the other and a barrier
+    // does not drain it.
+    //
+    //   phase 2k  : group 0 memory(k)            group 1 compute(k-1)
+    //   phase 2k+1: group 0 compute(k)           group 1 memory(k)
+    //
+    // Step k lives in stage k % 4.  Memory(k) issues step k+3 into the stage of
+    // step k-1, which both groups finished reading by the end of phase 2k-1.
+    // The barrier ending phase 2k+1 publishes step k+1: before it every wave
+    // waits for its own DMA of step k+1 (steps k+2 and k+3 may stay in flight).
+    static_assert(SUB == 1 && STAGES == 4 && NWAVES == 8 && DIST == 3, "ping-pong layout");
+    const int grp = wave >> 2;
+    auto mem = [&](int k) __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < NREAD; ++q) read_one(k % STAGES, 0, q, fa[0], fb[0]);
+      issue(k + DIST);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto comp = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < NMFMA; ++q) {
+        const int i = q / FM, jm = q % FM;
+        acc[i][jm] = mfma32(fa[0][i], fb[0][jm], acc[i][jm]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // Both groups run the same body, memory(k) then compute(k); group 1 runs
+    // it one phase later (an extra barrier first, none after its last compute),
+    // so every wave executes the same number of barriers.  The wait that
+    // publishes step k+1 belongs to phase 2k+1, which is group 0's compute and
+    // group 1's memory phase.
+    auto publish = [&](int k) __attribute__((always_inline)) {
+      wait_ahead(min(2, nk - 2 - k));
+      if (KTAIL && k + 1 == nk_full) fix_tail((k + 1) % STAGES);
+    };
+    if (grp == 1) __syncthreads();
+    for (int k = 0; k < nk; ++k) {
+      mem(k);
+      if (grp == 1) publish(k);
+      __syncthreads();
+      comp();
+      if (grp == 0) publish(k);
+      if (grp == 0 || k + 1 < nk) __syncthreads();
+    }
+  } else {
 #pragma unroll
   for (int q = 0; q < NREAD; ++q) read_one(0, 0, q, fa[0], fb[0]);
 
@@ -455,33 +512,58 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
       substep(2 * s + 1, 1, true);
     }
   }
-  // Epilogue: y[m, n..n+3] = bf16(acc * scale[n..n+3]).
+  }  // PP
+
+  // Epilogue: y[m, n..n+3] = bf16(acc * scale[n..n+3]), written through LDS so
+  // that y leaves in whole rows.  A lane's results are four consecutive n of
+  // one m, so stored directly every store instruction would touch 32 rows with
+  // 16 bytes each and every 128-byte line of y would be assembled from eight
+  // partial writes.  Instead the waves put the bf16 tile into the (now idle)
+  // stage buffers -- row pitch 2*BN bytes, 16-byte chunk c of row r at
+  // c ^ (r % CPR), which keeps both the 32-row writes and the row reads nearly
+  // free of bank conflicts -- and then write it out row by row, 16 bytes per
+  // lane, so one store instruction covers whole rows of the tile.
+  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+  constexpr int PITCH = 2 * BN;
+  constexpr int NTHREADS = NWAVES * 64;
+  static_assert(BM * PITCH <= STAGES * STAGE_BYTES, "the bf16 tile fits in the stage buffers");
   const float *s_lds = (const float *)(smem + STAGES * STAGE_BYTES);
+  __syncthreads();  // every wave is done with the stage buffers
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
       const int nl = wave_n * TN + 32 * i + 8 * qd + 4 * g;
-      const int n = n0 + nl;
       const float4 sc = *(const float4 *)(s_lds + nl);
 #pragma unroll
       for (int jm = 0; jm < FM; ++jm) {
-        const int m = m0 + wave_m * TM + 32 * jm + lr;
-        if (m >= a.M) continue;
-        uint16_t *yr = a.y + (size_t)m * a.N;
+        const int ml = wave_m * TM + 32 * jm + lr;
         const uint32_t b0 = bf16_rne(acc[i][jm][4 * qd + 0] * sc.x);
         const uint32_t b1 = bf16_rne(acc[i][jm][4 * qd + 1] * sc.y);
         const uint32_t b2 = bf16_rne(acc[i][jm][4 * qd + 2] * sc.z);
         const uint32_t b3 = bf16_rne(acc[i][jm][4 * qd + 3] * sc.w);
-        if (VEC) {
-          if (n < a.N) *(uint2 *)(yr + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-        } else {
-          if (n + 0 < a.N) yr[n + 0] = (uint16_t)b0;
-          if (n + 1 < a.N) yr[n + 1] = (uint16_t)b1;
-          if (n + 2 < a.N) yr[n + 2] = (uint16_t)b2;
-          if (n + 3 < a.N) yr[n + 3] = (uint16_t)b3;
-        }
+        const int off = ml * PITCH + (((nl >> 3) ^ (ml & (CPR - 1))) << 4) + ((nl & 7) << 1);
+        *(uint2 *)(smem + off) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
       }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < BM * CPR; idx += NTHREADS) {
+    const int r = idx / CPR, c = idx % CPR;
+    const int m = m0 + r, n = n0 + 8 * c;
+    if (m >= a.M || n >= a.N) continue;
+    const uint4 v = *(const uint4 *)(smem + r * PITCH + ((c ^ (r & (CPR - 1))) << 4));
+    uint16_t *dst = a.y + (size_t)m * a.N + n;
+    if (a.ystore == 16) {  // N % 8 == 0 and y 16-byte aligned: the chunk is whole
+      *(uint4 *)dst = v;
+    } else if (a.ystore == 8) {  // N % 4 == 0 and y 8-byte aligned
+      *(uint2 *)dst = make_uint2(v.x, v.y);
+      if (n + 4 < a.N) *(uint2 *)(dst + 4) = make_uint2(v.z, v.w);
+    } else {
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < a.N) dst[e] = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
     }
   }
 }
@@ -750,6 +832,7 @@ static const MainConfig kMainConfigs[] = {
     {5, 256, 256, 64, 4},  // 4 waves, one per SIMD
     {6, 256, 256, 128, 2}, // 8 waves, wave tile 64 (m) x 128 (n), 128-byte K steps
     {7, 256, 256, 128, 2}, // 8 waves, wave tile 128 (m) x 64 (n), 128-byte K steps
+    {9, 256, 256, 64, 4},  // 8 waves in two ping-pong groups, wave tile 64 (m) x 128 (n)
 };
 static const SkinnyConfig kSkinnyConfigs[] = {
     {1, 1}, {2, 2}, {3, 3}, {4, 4}, {5, 5},
@@ -769,17 +852,12 @@ int skinny_tile_n(const SkinnyConfig &c) { return 16 * c.row_blocks; }
 int skinny_max_row_blocks(int M) { return M <= 16 ? 5 : (M <= 32 ? 4 : 2); }
 int skinny_chunk_bytes() { return 128; }
 
-template <int BM, int BN, int BK, int STAGES, int WM, int WN>
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool PP = false>
 static hipError_t launch_main_cfg(const MainLaunch &l, hipStream_t stream) {
-  MainArgs a{l.x, l.w, l.scale, l.y, l.M, l.N, l.K, l.tiles_m, l.tiles_n, l.group_m};
+  MainArgs a{l.x, l.w, l.scale, l.y, l.M, l.N, l.K, l.tiles_m, l.tiles_n, l.group_m, l.ystore};
   const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(WM * WN * 64);
-  if (l.k_tail) {
-    if (l.vec) fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, true, true><<<grid, block, 0, stream>>>(a);
-    else fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, true, false><<<grid, block, 0, stream>>>(a);
-  } else {
-    if (l.vec) fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, false, true><<<grid, block, 0, stream>>>(a);
-    else fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, false, false><<<grid, block, 0, stream>>>(a);
-  }
+  if (l.k_tail) fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, true, PP><<<grid, block, 0, stream>>>(a);
+  else fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, false, PP><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -792,6 +870,7 @@ hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
     case 5: return launch_main_cfg<256, 256, 64, 4, 2, 2>(l, stream);
     case 6: return launch_main_cfg<256, 256, 128, 2, 4, 2>(l, stream);
     case 7: return launch_main_cfg<256, 256, 128, 2, 2, 4>(l, stream);
+    case 9: return launch_main_cfg<256, 256, 64, 4, 4, 2, true>(l, stream);
     default: return hipErrorInvalidValue;
   }
 }
