@@ -39,13 +39,13 @@ struct MainConfig {
   int id, bm, bn, bk, stages;
 };
 struct SkinnyConfig {
-  int id, row_blocks;  // w rows per workgroup = 16 * row_blocks
+  int id, row_blocks;  // w rows per workgroup = 16 * row_blocks; ids >= 11: direct-to-register kernel
 };
 
 const MainConfig *main_config(int id);      // nullptr if unknown
 const SkinnyConfig *skinny_config(int id);  // nullptr if unknown
 int skinny_tile_n(const SkinnyConfig &c);   // output columns per workgroup
-int skinny_max_row_blocks(int M);           // LDS limit on row_blocks for this M
+int skinny_max_row_blocks(int M, bool direct);  // limit on row_blocks for this M and kernel
 int skinny_chunk_bytes();                   // K granularity of one wave iteration
 
 hipError_t launch_main(const MainLaunch &l, hipStream_t stream);

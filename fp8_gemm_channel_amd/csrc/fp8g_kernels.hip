@@ -640,6 +640,61 @@ __device__ __forceinline__ v4f mfma16(const v8i &a, const v8i &b, const v4f &c) 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// End of a skinny workgroup: the four waves' sums are added through LDS (`red`,
+// 4*RB*MB*4*64 floats) in wave order, so the result does not depend on timing;
+// wave v finishes blocks v, v+4, ...  One K slice: scale and bf16 store; several:
+// unscaled fp32 partials P[s, m, n] for the reduce kernel.
+template <int RB, int MB>
+__device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const SkinnyArgs &a, float *red, int n0,
+                                              int s, int wave, int lane) {
+  const int g = lane >> 4, lr = lane & 15;
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[(((wave * RB + rb) * MB + mb) * 4 + e) * 64 + lane] = acc[rb][mb][e];
+  __syncthreads();
+  const v4i rsrc_s = make_rsrc(a.scale, (uint32_t)a.N * 4u);
+  for (int b = wave; b < RB * MB; b += 4) {
+    const int rb = b / MB, mb = b % MB;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float t = red[((b) * 4 + e) * 64 + lane];
+#pragma unroll
+      for (int o = 1; o < 4; ++o) t += red[((o * RB * MB + b) * 4 + e) * 64 + lane];
+      v[e] = t;
+    }
+    const int n = n0 + 16 * rb + 4 * g;
+    const int m = 16 * mb + lr;
+    if (m >= a.M) continue;
+    if (gridDim.y > 1) {
+      float *pr = a.P + ((size_t)s * a.M + m) * a.N;
+      if (a.vec) {
+        if (n < a.N) *(float4 *)(pr + n) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) pr[n + e] = v[e];
+      }
+    } else {
+      uint16_t *yr = a.y + (size_t)m * a.N;
+      uint32_t bits[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bits[e] = bf16_rne(v[e] * llvm_buffer_load_f32(rsrc_s, (uint32_t)(n + e) * 4u, 0, 0));
+      if (a.vec) {
+        if (n < a.N) *(uint2 *)(yr + n) = make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) yr[n + e] = (uint16_t)bits[e];
+      }
+    }
+  }
+}
+
 template <int RB, int MB>
 __global__ __launch_bounds__(256, 1) void fp8g_splitk_partial_kernel(SkinnyArgs a) {
   using S = SkinnyShape<RB, MB>;
@@ -736,53 +791,144 @@ __global__ __launch_bounds__(256, 1) void fp8g_splitk_partial_kernel(SkinnyArgs 
       for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = mfma16(af[rb], bf[mb], acc[rb][mb]);
   }
 
-  // Add the four waves' sums in wave order; wave v finishes blocks v, v+4, ...
-  __syncthreads();
-  float *red = (float *)smem;
+  skinny_finish<RB, MB>(acc, a, (float *)smem, n0, s, wave, lane);
+}
+
+// Direct variant of the skinny kernel: no LDS in the K loop.  Every lane
+// loads its own MFMA operands from global memory straight into registers, so
+// neither w nor x passes through LDS and nothing but the final cross-wave sum
+// needs it.  For V_MFMA_F32_16X16X128_F8F6F4 lane l supplies row l % 16 of a
+// 16-row block and 32 bytes of K.  Any permutation of K inside one MFMA is
+// harmless as long as A and B use the same one, so lane l (r = l % 16,
+// g = l / 16) takes bytes [16g, 16g+16) and [64 + 16g, 64 + 16g + 16) of the
+// 128-byte chunk: the four lanes of a row then read 64 contiguous bytes per
+// load instruction.  Wave v takes chunks v, v+4, v+8, ... of the workgroup's K
+// slice and keeps D chunks in flight (register ring, loads issued D chunks
+// ahead of the MFMAs that use them); w is read with the non-temporal policy,
+// x (re-read by every workgroup, so best kept in L2) without.
+template <int RB, int MB, int D>
+__global__ __launch_bounds__(256, 1) void fp8g_skinny_direct_kernel(SkinnyArgs a) {
+  constexpr int NB = RB + MB;  // 16-row blocks per chunk: RB of w, then MB of x
+  __shared__ __attribute__((aligned(16))) float red[4 * RB * MB * 4 * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = a.K;
+  const int n0 = blockIdx.x * 16 * RB;
+  const int rows_w = min(16 * RB, a.N - n0);
+  const int s = blockIdx.y;
+  const int kbeg = s * a.k_slice;
+  const int kend = min(K, kbeg + a.k_slice);
+  const int nch = (kend - kbeg + 127) >> 7;
+  const int my = nch > wave ? (nch - wave + 3) >> 2 : 0;  // chunks of this wave
+
+  const v4i rsrc_w = make_rsrc(a.w + (size_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
+  const v4i rsrc_x = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)K);
+  const int g = lane >> 4, r = lane & 15;
+  uint32_t off[NB];  // lane's row start + 16g, per block (rows past N or M read as zero)
+#pragma unroll
+  for (int b = 0; b < NB; ++b) off[b] = (uint32_t)(16 * (b < RB ? b : b - RB) + r) * (uint32_t)K + 16u * g;
+
+  // Only the slice's last chunk can end past kend; it belongs to wave
+  // (nch - 1) % 4 as its last chunk.  Its loads are issued before everything
+  // else and it is used last, so the main loop has no tail logic.
+  const bool has_tail = ((kend - kbeg) & 127) != 0 && ((nch - 1) & 3) == wave;
+  const int my_full = my - (has_tail ? 1 : 0);
+
+  // Chunk j of this wave into registers: bb[b][h] = 16 bytes at k = kc + 64h + 16g.
+  // Every load is issued unconditionally: a chunk past the wave's share is
+  // pointed 2^31 bytes past the buffer, beyond its range (rows * K < 2^31), so
+  // it reads zeros without touching memory and its MFMAs add nothing.  With no
+  // load under a branch the compiler can wait for exactly the chunk it needs
+  // (a conditional load would force it to wait for all of them).  The
+  // scheduling barriers keep the loads in chunk order.
+  auto load = [&](int j, v4i (&bb)[NB][2]) __attribute__((always_inline)) {
+    const uint32_t kc = j < my_full ? (uint32_t)(kbeg + ((wave + 4 * j) << 7)) : 0x80000000u;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        bb[b][h] = b < RB ? llvm_buffer_load_v4i32(rsrc_w, off[b] + 64u * h, kc, 2)
+                          : llvm_buffer_load_v4i32(rsrc_x, off[b] + 64u * h, kc, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  v4f acc[RB][MB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const v4i (&bb)[NB][2]) __attribute__((always_inline)) {
+    v8i op[NB];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[(((wave * RB + rb) * MB + mb) * 4 + e) * 64 + lane] = acc[rb][mb][e];
-  __syncthreads();
-  const v4i rsrc_s = make_rsrc(a.scale, (uint32_t)a.N * 4u);
-  for (int b = wave; b < RB * MB; b += 4) {
-    const int rb = b / MB, mb = b % MB;
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float t = red[((b) * 4 + e) * 64 + lane];
-#pragma unroll
-      for (int o = 1; o < 4; ++o) t += red[((o * RB * MB + b) * 4 + e) * 64 + lane];
-      v[e] = t;
+    for (int b = 0; b < NB; ++b) {
+      const v4i lo = bb[b][0], hi = bb[b][1];
+      op[b] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     }
-    const int n = n0 + 16 * rb + 4 * g;
-    const int m = 16 * mb + lr;
-    if (m >= a.M) continue;
-    if (gridDim.y > 1) {
-      float *pr = a.P + ((size_t)s * a.M + m) * a.N;
-      if (a.vec) {
-        if (n < a.N) *(float4 *)(pr + n) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < a.N) pr[n + e] = v[e];
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = mfma16(op[rb], op[RB + mb], acc[rb][mb]);
+  };
+
+  // Tail chunk: a piece with valid bytes 0 < v < 16 is loaded as the 16 bytes
+  // ending at its last valid byte (within its row, since K >= 16) and moved
+  // into place at the end; a piece with none is zeroed there.
+  v4i tail[NB][2];
+  int tvalid[2] = {0, 0};
+  if (has_tail) {
+    const int kc = kbeg + ((wave + 4 * my_full) << 7);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) tvalid[h] = kend - (kc + 64 * h + 16 * g);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int v = tvalid[h];
+        const uint32_t o = off[b] + (uint32_t)(kc + 64 * h) + (uint32_t)(v >= 16 ? 0 : v > 0 ? v - 16 : 0);
+        tail[b][h] = llvm_buffer_load_v4i32(b < RB ? rsrc_w : rsrc_x, o, 0, b < RB ? 2 : 0);
       }
-    } else {
-      uint16_t *yr = a.y + (size_t)m * a.N;
-      uint32_t bits[4];
+  }
+  // D chunks in flight: chunk j lives in slot j % D and is refilled with chunk
+  // j + D right after its MFMAs; the last round issues no refills.
+  v4i buf[D][NB][2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bits[e] = bf16_rne(v[e] * llvm_buffer_load_f32(rsrc_s, (uint32_t)(n + e) * 4u, 0, 0));
-      if (a.vec) {
-        if (n < a.N) *(uint2 *)(yr + n) = make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
-      } else {
+  for (int d = 0; d < D; ++d) load(d, buf[d]);
+  const int rounds = (my_full + D - 1) / D;
+  for (int rd = 0; rd + 1 < rounds; ++rd) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < a.N) yr[n + e] = (uint16_t)bits[e];
-      }
+    for (int d = 0; d < D; ++d) {
+      mma(buf[d]);
+      load(rd * D + d + D, buf[d]);
     }
   }
+#pragma unroll
+  for (int d = 0; d < D; ++d) mma(buf[d]);
+  if (has_tail) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int v = tvalid[h];
+        if (v >= 16) continue;
+        if (v <= 0) {
+          tail[b][h] = v4i{0, 0, 0, 0};
+          continue;
+        }
+        const int sh = 16 - v, q = sh >> 2, r8 = sh & 3;
+        const uint32_t d0 = (uint32_t)tail[b][h].x, d1 = (uint32_t)tail[b][h].y;
+        const uint32_t d2 = (uint32_t)tail[b][h].z, d3 = (uint32_t)tail[b][h].w;
+        const uint32_t e0 = q == 0 ? d0 : q == 1 ? d1 : q == 2 ? d2 : d3;
+        const uint32_t e1 = q == 0 ? d1 : q == 1 ? d2 : q == 2 ? d3 : 0u;
+        const uint32_t e2 = q == 0 ? d2 : q == 1 ? d3 : 0u;
+        const uint32_t e3 = q == 0 ? d3 : 0u;
+        tail[b][h] = v4i{(int)__builtin_amdgcn_alignbyte(e1, e0, r8), (int)__builtin_amdgcn_alignbyte(e2, e1, r8),
+                         (int)__builtin_amdgcn_alignbyte(e3, e2, r8), (int)__builtin_amdgcn_alignbyte(0u, e3, r8)};
+      }
+    mma(tail);
+  }
+  skinny_finish<RB, MB>(acc, a, red, n0, s, wave, lane);
 }
 
 // y[m, n..n+3] = bf16((sum_{s<S} P[s, m, n..n+3]) * scale[n..n+3]), slices
@@ -834,8 +980,9 @@ static const MainConfig kMainConfigs[] = {
     {7, 256, 256, 128, 2}, // 8 waves, wave tile 128 (m) x 64 (n), 128-byte K steps
     {9, 256, 256, 64, 4},  // 8 waves in two ping-pong groups, wave tile 64 (m) x 128 (n)
 };
+// ids 1-5: LDS-ring kernel, 11-15: direct-to-register kernel; 16 * row_blocks w rows per workgroup
 static const SkinnyConfig kSkinnyConfigs[] = {
-    {1, 1}, {2, 2}, {3, 3}, {4, 4}, {5, 5},
+    {1, 1}, {2, 2}, {3, 3}, {4, 4}, {5, 5}, {11, 1}, {12, 2}, {13, 3}, {14, 4}, {15, 5},
 };
 
 const MainConfig *main_config(int id) {
@@ -849,7 +996,10 @@ const SkinnyConfig *skinny_config(int id) {
   return nullptr;
 }
 int skinny_tile_n(const SkinnyConfig &c) { return 16 * c.row_blocks; }
-int skinny_max_row_blocks(int M) { return M <= 16 ? 5 : (M <= 32 ? 4 : 2); }
+int skinny_max_row_blocks(int M, bool direct) {
+  if (direct) return 5;  // register ring: (RB + MB) * 8 * 4 VGPRs of operands
+  return M <= 16 ? 5 : (M <= 32 ? 4 : 2);  // LDS ring of the other kernel
+}
 int skinny_chunk_bytes() { return 128; }
 
 template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool PP = false>
@@ -875,11 +1025,12 @@ hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
   }
 }
 
-template <int RB, int MB>
+template <int RB, int MB, bool DIRECT>
 static hipError_t launch_skinny_cfg(const SkinnyLaunch &l, hipStream_t stream) {
   SkinnyArgs a{l.x, l.w, l.scale, l.y, l.partials, l.M, l.N, l.K, l.k_slice, l.N % 4 == 0 && (l.S > 1 || l.vec)};
   const dim3 grid((unsigned)((l.N + 16 * RB - 1) / (16 * RB)), (unsigned)l.S), block(256);
-  fp8g_splitk_partial_kernel<RB, MB><<<grid, block, 0, stream>>>(a);
+  if constexpr (DIRECT) fp8g_skinny_direct_kernel<RB, MB, 4><<<grid, block, 0, stream>>>(a);
+  else fp8g_splitk_partial_kernel<RB, MB><<<grid, block, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.S == 1) return e;
   const int64_t threads = (int64_t)l.M * ((l.N + 3) / 4);
@@ -892,11 +1043,16 @@ static hipError_t launch_skinny_cfg(const SkinnyLaunch &l, hipStream_t stream) {
 template <int MB>
 static hipError_t launch_skinny_mb(const SkinnyLaunch &l, hipStream_t stream) {
   switch (l.variant) {
-    case 1: return launch_skinny_cfg<1, MB>(l, stream);
-    case 2: return launch_skinny_cfg<2, MB>(l, stream);
-    case 3: if constexpr (MB <= 2) return launch_skinny_cfg<3, MB>(l, stream); else break;
-    case 4: if constexpr (MB <= 2) return launch_skinny_cfg<4, MB>(l, stream); else break;
-    case 5: if constexpr (MB == 1) return launch_skinny_cfg<5, MB>(l, stream); else break;
+    case 1: return launch_skinny_cfg<1, MB, false>(l, stream);
+    case 2: return launch_skinny_cfg<2, MB, false>(l, stream);
+    case 3: if constexpr (MB <= 2) return launch_skinny_cfg<3, MB, false>(l, stream); else break;
+    case 4: if constexpr (MB <= 2) return launch_skinny_cfg<4, MB, false>(l, stream); else break;
+    case 5: if constexpr (MB == 1) return launch_skinny_cfg<5, MB, false>(l, stream); else break;
+    case 11: return launch_skinny_cfg<1, MB, true>(l, stream);
+    case 12: return launch_skinny_cfg<2, MB, true>(l, stream);
+    case 13: return launch_skinny_cfg<3, MB, true>(l, stream);
+    case 14: return launch_skinny_cfg<4, MB, true>(l, stream);
+    case 15: return launch_skinny_cfg<5, MB, true>(l, stream);
     default: break;
   }
   return hipErrorInvalidValue;

@@ -45,13 +45,26 @@ def test_splitk_full(M, split_k):
 
 @pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
 def test_splitk_variants(variant):
-    """Every rows-per-workgroup configuration (16 * variant rows), with and
-    without split-K, for each x-row staging width the variant supports."""
+    """Every rows-per-workgroup configuration of the LDS-ring kernel (16 *
+    variant rows), with and without split-K, for each x-row staging width the
+    variant supports."""
     if variant <= 2:
         _full_case(40, 777, 3000, path=fg.PATH_SPLITK, variant=variant, split_k=3)
     if variant <= 4:
         _full_case(32, 1024, 4096, path=fg.PATH_SPLITK, variant=variant, split_k=1)
     _full_case(16, 1000, 4127, path=fg.PATH_SPLITK, variant=variant, split_k=2)
+
+
+@pytest.mark.parametrize("variant", [11, 12, 13, 14, 15])
+@pytest.mark.parametrize("M", [1, 16, 17, 32, 40, 64])
+def test_splitk_direct_variants(variant, M):
+    """The direct-to-register kernel (16 * (variant - 10) rows per workgroup)
+    for every x-row block count, with ragged N, a K tail whose last chunk has
+    pieces with 0, 1..15 and 16 valid bytes, and 1..3 K slices."""
+    _full_case(M, 777, 3000, path=fg.PATH_SPLITK, variant=variant, split_k=3)
+    _full_case(M, 1024, 4096, path=fg.PATH_SPLITK, variant=variant, split_k=1)
+    _full_case(M, 1000, 4127, path=fg.PATH_SPLITK, variant=variant, split_k=2)
+    _full_case(M, 264, 600, path=fg.PATH_SPLITK, variant=variant, split_k=1)
 
 
 # ---------------------------------------------------- the benchmark shapes ----
