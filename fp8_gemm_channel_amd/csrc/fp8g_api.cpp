@@ -57,7 +57,7 @@ int check_dims(int64_t M, int64_t N, int64_t K) {
 // Main-path configuration for (M, N) when not forced: the largest tile whose
 // grid still gives every compute unit a workgroup.
 int auto_main_variant(int64_t M, int64_t N) {
-  if (cdiv(M, 256) * cdiv(N, 256) >= kNumCUs) return 6;
+  if (cdiv(M, 256) * cdiv(N, 256) >= kNumCUs) return 10;
   if (cdiv(M, 128) * cdiv(N, 128) >= kNumCUs / 2) return 2;
   return 3;
 }

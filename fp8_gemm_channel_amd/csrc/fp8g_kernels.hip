@@ -190,6 +190,89 @@ __device__ __forceinline__ void interleave_mfma_reads() {
   }
 }
 
+// Workgroup -> tile.  Workgroup ids are dispatched round-robin over the 8 XCDs
+// (each with its own L2), so first renumber them so that every XCD works on a
+// contiguous range of tiles, then walk that range in groups of group_m tile
+// rows (all tile columns of a group before the next group) so the x rows and
+// w rows a group shares stay in the XCD's L2.
+__device__ __forceinline__ void tile_coords(const MainArgs &a, int &tm, int &tn) {
+  const int total = a.tiles_m * a.tiles_n;
+  const int pid = blockIdx.x;
+  const int xcd = pid & 7, q8 = total >> 3, r8 = total & 7;
+  const int lpid = xcd * q8 + min(xcd, r8) + (pid >> 3);
+  const int per_group = a.group_m * a.tiles_n;
+  const int gid = lpid / per_group;
+  const int first_m = gid * a.group_m;
+  const int gsize = min(a.tiles_m - first_m, a.group_m);
+  const int within = lpid - gid * per_group;
+  tm = first_m + within % gsize;
+  tn = within / gsize;
+}
+
+// Epilogue of the main kernels: y[m, n..n+3] = bf16(acc * scale[n..n+3]) for a
+// BM x BN tile computed by WM x WN waves (wave tile (BM/WM) x (BN/WN) as 32x32
+// blocks), with the tile's scales at s_lds[0 .. BN) and at least 2*BM*BN bytes
+// of LDS at smem that no wave uses any more after the first barrier.
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void main_epilogue(const v16f (&acc)[BN / WN / 32][BM / WM / 32], const MainArgs &a,
+                                              uint8_t *smem, const float *s_lds, int m0, int n0, int wave,
+                                              int lane) {
+  constexpr int NWAVES = WM * WN, TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  // Epilogue: y[m, n..n+3] = bf16(acc * scale[n..n+3]), written through LDS so
+  // that y leaves in whole rows.  A lane's results are four consecutive n of
+  // one m, so stored directly every store instruction would touch 32 rows with
+  // 16 bytes each and every 128-byte line of y would be assembled from eight
+  // partial writes.  Instead the waves put the bf16 tile into the (now idle)
+  // stage buffers -- row pitch 2*BN bytes, 16-byte chunk c of row r at
+  // c ^ (r % CPR), which keeps both the 32-row writes and the row reads nearly
+  // free of bank conflicts -- and then write it out row by row, 16 bytes per
+  // lane, so one store instruction covers whole rows of the tile.
+  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+  constexpr int PITCH = 2 * BN;
+  constexpr int NTHREADS = NWAVES * 64;
+  const int tid = threadIdx.x;
+  const int g = lane >> 5, lr = lane & 31;
+  const int wave_m = wave % WM, wave_n = wave / WM;
+  __syncthreads();  // every wave is done with the stage buffers (and s_lds is published)
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int nl = wave_n * TN + 32 * i + 8 * qd + 4 * g;
+      const float4 sc = *(const float4 *)(s_lds + nl);
+#pragma unroll
+      for (int jm = 0; jm < FM; ++jm) {
+        const int ml = wave_m * TM + 32 * jm + lr;
+        const uint32_t b0 = bf16_rne(acc[i][jm][4 * qd + 0] * sc.x);
+        const uint32_t b1 = bf16_rne(acc[i][jm][4 * qd + 1] * sc.y);
+        const uint32_t b2 = bf16_rne(acc[i][jm][4 * qd + 2] * sc.z);
+        const uint32_t b3 = bf16_rne(acc[i][jm][4 * qd + 3] * sc.w);
+        const int off = ml * PITCH + (((nl >> 3) ^ (ml & (CPR - 1))) << 4) + ((nl & 7) << 1);
+        *(uint2 *)(smem + off) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < BM * CPR; idx += NTHREADS) {
+    const int r = idx / CPR, c = idx % CPR;
+    const int m = m0 + r, n = n0 + 8 * c;
+    if (m >= a.M || n >= a.N) continue;
+    const uint4 v = *(const uint4 *)(smem + r * PITCH + ((c ^ (r & (CPR - 1))) << 4));
+    uint16_t *dst = a.y + (size_t)m * a.N + n;
+    if (a.ystore == 16) {  // N % 8 == 0 and y 16-byte aligned: the chunk is whole
+      *(uint4 *)dst = v;
+    } else if (a.ystore == 8) {  // N % 4 == 0 and y 8-byte aligned
+      *(uint2 *)dst = make_uint2(v.x, v.y);
+      if (n + 4 < a.N) *(uint2 *)(dst + 4) = make_uint2(v.z, v.w);
+    } else {
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < a.N) dst[e] = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
 // Software pipeline.  A K step is BK bytes (one stage buffer), worked as BK/64
 // MFMA sub-steps; F[u & 1] holds the operands of sub-step u.  Sub-step u:
 //
@@ -241,22 +324,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_m = wave % WM, wave_n = wave / WM;
 
-  // Workgroup -> tile.  Workgroup ids are dispatched round-robin over the 8
-  // XCDs (each with its own L2), so first renumber them so that every XCD works
-  // on a contiguous range of tiles, then walk that range in groups of group_m
-  // tile rows (all tile columns of a group before the next group) so the x rows
-  // and w rows a group shares stay in the XCD's L2.
-  const int total = a.tiles_m * a.tiles_n;
-  const int pid = blockIdx.x;
-  const int xcd = pid & 7, q8 = total >> 3, r8 = total & 7;
-  const int lpid = xcd * q8 + min(xcd, r8) + (pid >> 3);
-  const int per_group = a.group_m * a.tiles_n;
-  const int gid = lpid / per_group;
-  const int first_m = gid * a.group_m;
-  const int gsize = min(a.tiles_m - first_m, a.group_m);
-  const int within = lpid - gid * per_group;
-  const int tm = first_m + within % gsize;
-  const int tn = within / gsize;
+  int tm, tn;
+  tile_coords(a, tm, tn);
 
   const int K = a.K;
   const int m0 = tm * BM, n0 = tn * BN;
@@ -514,58 +583,211 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   }
   }  // PP
 
-  // Epilogue: y[m, n..n+3] = bf16(acc * scale[n..n+3]), written through LDS so
-  // that y leaves in whole rows.  A lane's results are four consecutive n of
-  // one m, so stored directly every store instruction would touch 32 rows with
-  // 16 bytes each and every 128-byte line of y would be assembled from eight
-  // partial writes.  Instead the waves put the bf16 tile into the (now idle)
-  // stage buffers -- row pitch 2*BN bytes, 16-byte chunk c of row r at
-  // c ^ (r % CPR), which keeps both the 32-row writes and the row reads nearly
-  // free of bank conflicts -- and then write it out row by row, 16 bytes per
-  // lane, so one store instruction covers whole rows of the tile.
-  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
-  constexpr int PITCH = 2 * BN;
-  constexpr int NTHREADS = NWAVES * 64;
-  static_assert(BM * PITCH <= STAGES * STAGE_BYTES, "the bf16 tile fits in the stage buffers");
-  const float *s_lds = (const float *)(smem + STAGES * STAGE_BYTES);
-  __syncthreads();  // every wave is done with the stage buffers
+  static_assert(2 * BM * BN <= STAGES * STAGE_BYTES, "the bf16 tile fits in the stage buffers");
+  main_epilogue<BM, BN, WM, WN>(acc, a, smem, (const float *)(smem + STAGES * STAGE_BYTES), m0, n0, wave, lane);
+}
+
+// ------------------------------------------------- main path, five LDS slots
+//
+// 256 x 256 tiles, 128-byte K steps, 8 waves with 64 (m) x 128 (n) wave tiles,
+// as variant 6 of the kernel above, but with a deeper feed.  Measured on
+// MI355X, the global-to-LDS copy of a K step (64 KiB per workgroup, 64 LDS-DMA
+// instructions) is limited by how fast the compute unit accepts DMA
+// instructions (about one per 20-25 cycles): issued in one burst after the
+// barrier, the second wave of every SIMD stalls for ~1400 cycles before it can
+// issue its MFMAs.  Spreading the instructions over the step needs them to be
+// issued earlier, i.e. more buffering than two 64 KiB stages in 160 KiB of LDS.
+//
+// So a stage is split in halves: LDS holds five 32 KiB slots, each one K step
+// of either the tile's w rows or its x rows -- w of step k in slot k % 2, x of
+// step k in slot 2 + k % 3.  x (whose rows are shared by fewer of the tiles an
+// XCD runs at once, so it misses L2 more often) is fetched two steps ahead and
+// w one step ahead, and every DMA instruction is issued between two MFMAs, so
+// no wave waits long for the instruction queue.  The epilogue's
+// scales no longer fit in LDS during the K loop: thread t < 256 keeps
+// scale[n0 + t] in a register and writes it to LDS after the loop.
+template <bool KTAIL>
+__global__ __launch_bounds__(512, 1) void fp8g_main5_kernel(MainArgs a) {
+  constexpr int BM = 256, BN = 256, BK = 128, WM = 4, WN = 2, NWAVES = 8;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr int CH = BK / 16, ROWS_PER_KB = 1024 / BK;
+  constexpr int SLOT = 256 * BK;                         // one half step: 256 rows x 128 bytes
+  constexpr int HDPW = SLOT / 1024 / NWAVES;             // DMA instructions per wave per half step (4)
+  constexpr int NMFMA = FN * FM, NREAD = (FN + FM) * 2;  // per wave per 64-byte sub-step
+  static_assert(HDPW == 4 && NMFMA == 8, "x DMAs are spread two per sub-step, after MFMAs 1 and 5");
+  static_assert(2 * BM * BN + BN * 4 <= 5 * SLOT, "epilogue tile and scales fit");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * SLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_m = wave % WM, wave_n = wave / WM;
+  int tm, tn;
+  tile_coords(a, tm, tn);
+  const int K = a.K;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
+  const uint32_t range_x = (uint32_t)rows_x * (uint32_t)K, range_w = (uint32_t)rows_w * (uint32_t)K;
+  const int g = lane >> 5, lr = lane & 31;
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+
+  // The epilogue's scale for column n0 + tid (zero past N); the load is the
+  // oldest vector-memory operation, so every DMA wait below also covers it.
+  float my_scale = 0.0f;
+  if (tid < BN) my_scale = llvm_buffer_load_f32(make_rsrc(a.scale + n0, (uint32_t)(a.N - n0) * 4u), (uint32_t)tid * 4u, 0, 0);
+
+  // DMA instruction t (0..3) of a wave fills 1 KiB block t*8 + wave of a half
+  // step: 8 rows of 128 bytes, lane l taking row l / 8 and logical chunk
+  // (l % 8) ^ swz(row); descriptor t starts at the block's first row (rows past
+  // M / N read zero).
+  const int dma_lrow = wave * ROWS_PER_KB + lane / CH;
+  const int dma_chunk = (lane % CH) ^ swz<BK>(dma_lrow);
+  const uint32_t lane_off = (uint32_t)dma_lrow * (uint32_t)K + (uint32_t)dma_chunk * 16u;
+  const uint32_t blk_stride = (uint32_t)(NWAVES * ROWS_PER_KB) * (uint32_t)K;
+  v4i rw[HDPW], rx[HDPW];
 #pragma unroll
-  for (int i = 0; i < FN; ++i) {
+  for (int t = 0; t < HDPW; ++t) {
+    const uint32_t skip = (uint32_t)t * blk_stride;
+    rw[t] = make_rsrc(a.w + (size_t)n0 * K + skip, range_w > skip ? range_w - skip : 0u);
+    rx[t] = make_rsrc(a.x + (size_t)m0 * K + skip, range_x > skip ? range_x - skip : 0u);
+  }
+  const int nk_full = K / BK;
+  const int nk = nk_full + (KTAIL ? 1 : 0);
+  auto slot_w = [&](int k) __attribute__((always_inline)) { return (uint32_t)((k & 1) * SLOT); };
+  auto slot_x = [&](int k) __attribute__((always_inline)) { return (uint32_t)((2 + k % 3) * SLOT); };
+
+  // DMA instruction t of step kt's w (or x) half; the tail step points chunks
+  // at or past K out of range (zeros) and fix_tail rebuilds the straddling one.
+  auto dma_half = [&](const v4i &rs, uint32_t range, uint32_t slot, int kt, int t) __attribute__((always_inline)) {
+    const uint32_t lds = smem_base + slot + (uint32_t)(t * NWAVES + wave) * 1024u;
+    if (kt < nk_full) {
+      dma16(rs, lds, lane_off, (uint32_t)kt * BK);
+    } else if (KTAIL && kt == nk_full) {
+      const int valid = K - (kt * BK + 16 * dma_chunk);
+      dma16(rs, lds, valid >= 16 ? lane_off + (uint32_t)(kt * BK) : range, 0u);
+    }
+  };
+  auto issue_w = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int nl = wave_n * TN + 32 * i + 8 * qd + 4 * g;
-      const float4 sc = *(const float4 *)(s_lds + nl);
+    for (int t = 0; t < HDPW; ++t) dma_half(rw[t], range_w, slot_w(kt), kt, t);
+  };
+  auto issue_x = [&](int kt, int t) __attribute__((always_inline)) { dma_half(rx[t], range_x, slot_x(kt), kt, t); };
+  auto fix_tail = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * BK;
+    const int valid = K - (k0 + 16 * dma_chunk);
+    if (valid > 0 && valid < 16) {
 #pragma unroll
-      for (int jm = 0; jm < FM; ++jm) {
-        const int ml = wave_m * TM + 32 * jm + lr;
-        const uint32_t b0 = bf16_rne(acc[i][jm][4 * qd + 0] * sc.x);
-        const uint32_t b1 = bf16_rne(acc[i][jm][4 * qd + 1] * sc.y);
-        const uint32_t b2 = bf16_rne(acc[i][jm][4 * qd + 2] * sc.z);
-        const uint32_t b3 = bf16_rne(acc[i][jm][4 * qd + 3] * sc.w);
-        const int off = ml * PITCH + (((nl >> 3) ^ (ml & (CPR - 1))) << 4) + ((nl & 7) << 1);
-        *(uint2 *)(smem + off) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      for (int t = 0; t < 2 * HDPW; ++t) {  // w blocks, then x blocks, one at a time (runs once)
+        const v4i &rs = t < HDPW ? rw[t % HDPW] : rx[t % HDPW];
+        const uint4 v = K >= 16 ? load16_tail(rs, lane_off + (uint32_t)k0, valid)
+                                : load16_partial(rs, lane_off + (uint32_t)k0, valid);
+        const uint32_t slot = t < HDPW ? slot_w(kt) : slot_x(kt);
+        *(uint4 *)(smem + slot + ((t % HDPW) * NWAVES + wave) * 1024 + lane * 16) = v;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < BM * CPR; idx += NTHREADS) {
-    const int r = idx / CPR, c = idx % CPR;
-    const int m = m0 + r, n = n0 + 8 * c;
-    if (m >= a.M || n >= a.N) continue;
-    const uint4 v = *(const uint4 *)(smem + r * PITCH + ((c ^ (r & (CPR - 1))) << 4));
-    uint16_t *dst = a.y + (size_t)m * a.N + n;
-    if (a.ystore == 16) {  // N % 8 == 0 and y 16-byte aligned: the chunk is whole
-      *(uint4 *)dst = v;
-    } else if (a.ystore == 8) {  // N % 4 == 0 and y 8-byte aligned
-      *(uint2 *)dst = make_uint2(v.x, v.y);
-      if (n + 4 < a.N) *(uint2 *)(dst + 4) = make_uint2(v.z, v.w);
+  };
+
+  // Fragment reads: lane l reads row (l % 32) of each 32-row block, chunks
+  // 4j + 2(l/32) + {0,1} of 64-byte sub-step j; blocks in first-use order.
+  const int aw_row = wave_n * TN + lr, bx_row = wave_m * TM + lr;
+  const int sa = swz<BK>(aw_row), sbx = swz<BK>(bx_row);
+  v8i fa[2][FN], fb[2][FM];
+  auto read_one = [&](int k, int j, int q, v8i (&af)[FN], v8i (&bf)[FM]) __attribute__((always_inline)) {
+    const int ord = q / 2, half = q % 2;
+    const int blk = ord == 0 ? 0 : (ord <= FM ? FN + ord - 1 : ord - FM);
+    const int c = 4 * j + 2 * g + half;
+    if (blk < FN) {
+      const uint8_t *row = smem + slot_w(k) + (aw_row + 32 * blk) * BK;
+      const uint4 v = *(const uint4 *)(row + ((c ^ sa) << 4));
+      af[blk][4 * half + 0] = (int)v.x; af[blk][4 * half + 1] = (int)v.y;
+      af[blk][4 * half + 2] = (int)v.z; af[blk][4 * half + 3] = (int)v.w;
     } else {
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (n + e < a.N) dst[e] = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
+      const uint8_t *row = smem + slot_x(k) + (bx_row + 32 * (blk - FN)) * BK;
+      const uint4 v = *(const uint4 *)(row + ((c ^ sbx) << 4));
+      bf[blk - FN][4 * half + 0] = (int)v.x; bf[blk - FN][4 * half + 1] = (int)v.y;
+      bf[blk - FN][4 * half + 2] = (int)v.z; bf[blk - FN][4 * half + 3] = (int)v.w;
     }
+  };
+
+  v16f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // Prologue: w(0), x(0), x(1), w(1), x(2) -- the steady-state issue order --
+  // then wait for step 0 (what was issued after x(0) may stay in flight).
+  issue_w(0);
+#pragma unroll
+  for (int t = 0; t < HDPW; ++t) issue_x(0, t);
+#pragma unroll
+  for (int t = 0; t < HDPW; ++t) issue_x(1, t);
+  issue_w(1);
+#pragma unroll
+  for (int t = 0; t < HDPW; ++t) issue_x(2, t);
+  if (nk >= 3) vm_wait<3 * HDPW>();
+  else if (nk == 2) vm_wait<2 * HDPW>();
+  else vm_wait<0>();
+  if (KTAIL && nk_full == 0) fix_tail(0);  // K < 128: everything issued has landed
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NREAD; ++q) read_one(0, 0, q, fa[0], fb[0]);
+
+  // Sub-step u = 2s + j of step s.  j = 1 is the boundary: wait for this wave's
+  // DMA of w(s+1) and x(s+1), barrier
+  // (publishes step s+1, retires step s's slots), then, spread over the MFMAs,
+  // w(s+2) into the slot of w(s) and the first half of x(s+3) into the slot of
+  // x(s); sub-step 2s+2 issues the second half of x(s+3).
+  const int nsub = 2 * nk;
+  auto substep = [&](const int u, const int cur) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int s = u >> 1, j = u & 1;
+    if (j == 1) {
+      // This wave's last DMA of w(s+1) came after MFMA 6 of sub-step 2s-1;
+      // after it only x(s+2) instructions 1 (after MFMA 7), 2 and 3 (sub-step
+      // 2s) were issued, so at most 3 may stay in flight.  (At s = 0 the
+      // prologue issued all of x(2) after w(1): waiting for 3 is stricter.)
+      if (s + 2 < nk) vm_wait<HDPW - 1>();
+      else vm_wait<0>();
+      if (KTAIL && s + 1 == nk_full) fix_tail(s + 1);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int xk = j == 1 ? s + 3 : s + 2;  // x step whose DMAs this sub-step spreads
+    const int xt = j == 1 ? 0 : 2;          // ... instructions xt and xt + 1
+    const bool xdma = j == 1 || s >= 1;
+    const bool more = u + 1 < nsub;
+    const int un = u + 1;
+#pragma unroll
+    for (int q = 0; q < NMFMA; ++q) {
+      const int i = q / FM, jm = q % FM;
+      acc[i][jm] = mfma32(fa[cur][i], fb[cur][jm], acc[i][jm]);
+      if (more) {
+#pragma unroll
+        for (int r = q * NREAD / NMFMA; r < (q + 1) * NREAD / NMFMA; ++r)
+          read_one(un >> 1, un & 1, r, fa[cur ^ 1], fb[cur ^ 1]);
+      }
+      // w(s+2) after MFMAs 0, 2, 4, 6 of the boundary sub-step, x after MFMAs 3
+      // and 7 (measured best among the placements tried: a burst of DMA
+      // instructions right after the barrier stalls the issuing waves)
+      if (j == 1 && (q & 1) == 0) dma_half(rw[q >> 1], range_w, slot_w(s + 2), s + 2, q >> 1);
+      if ((q == 3 || q == 7) && xdma) issue_x(xk, xt + (q == 7 ? 1 : 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int s = 0; s < nk; ++s) {
+    substep(2 * s, 0);
+    substep(2 * s + 1, 1);
   }
+
+  // Scales into LDS (past the bf16 tile), published by the epilogue's first barrier.
+  float *s_lds = (float *)(smem + 2 * BM * BN);
+  __syncthreads();  // every wave is done with the slots
+  if (tid < BN) s_lds[tid] = my_scale;
+  main_epilogue<BM, BN, WM, WN>(acc, a, smem, s_lds, m0, n0, wave, lane);
 }
 
 // ---------------------------------------------------------------- skinny path
@@ -979,6 +1201,7 @@ static const MainConfig kMainConfigs[] = {
     {6, 256, 256, 128, 2}, // 8 waves, wave tile 64 (m) x 128 (n), 128-byte K steps
     {7, 256, 256, 128, 2}, // 8 waves, wave tile 128 (m) x 64 (n), 128-byte K steps
     {9, 256, 256, 64, 4},  // 8 waves in two ping-pong groups, wave tile 64 (m) x 128 (n)
+    {10, 256, 256, 128, 2}, // 8 waves, five half-step LDS slots (x two steps ahead)
 };
 // ids 1-5: LDS-ring kernel, 11-15: direct-to-register kernel; 16 * row_blocks w rows per workgroup
 static const SkinnyConfig kSkinnyConfigs[] = {
@@ -1011,6 +1234,14 @@ static hipError_t launch_main_cfg(const MainLaunch &l, hipStream_t stream) {
   return hipGetLastError();
 }
 
+static hipError_t launch_main5(const MainLaunch &l, hipStream_t stream) {
+  MainArgs a{l.x, l.w, l.scale, l.y, l.M, l.N, l.K, l.tiles_m, l.tiles_n, l.group_m, l.ystore};
+  const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(512);
+  if (l.k_tail) fp8g_main5_kernel<true><<<grid, block, 0, stream>>>(a);
+  else fp8g_main5_kernel<false><<<grid, block, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
   switch (l.variant) {
     case 1: return launch_main_cfg<256, 256, 64, 4, 4, 2>(l, stream);
@@ -1021,6 +1252,7 @@ hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
     case 6: return launch_main_cfg<256, 256, 128, 2, 4, 2>(l, stream);
     case 7: return launch_main_cfg<256, 256, 128, 2, 2, 4>(l, stream);
     case 9: return launch_main_cfg<256, 256, 64, 4, 4, 2, true>(l, stream);
+    case 10: return launch_main5(l, stream);
     default: return hipErrorInvalidValue;
   }
 }

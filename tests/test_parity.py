@@ -30,7 +30,7 @@ def _full_case(M, N, K, seed=42, **kw):
 MAIN_SHAPES = [(300, 520, 4127), (257, 129, 200), (128, 128, 128), (65, 70, 33), (520, 264, 1000)]
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 9])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 9, 10])
 @pytest.mark.parametrize("shape", MAIN_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_main_variants_full(variant, shape):
     _full_case(*shape, path=fg.PATH_MAIN, variant=variant)
