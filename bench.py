@@ -52,7 +52,7 @@ def bound_of(wl) -> str:
 
 
 KERNEL_SOURCE = os.path.join(ROOT, "fp8_gemm_channel_amd", "csrc", "fp8g_kernels.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_main_kernel_square-8192_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_main5_kernel_square-8192_traffic.md")
 
 
 def kernel_source_hash() -> str:
@@ -216,7 +216,8 @@ def main() -> int:
     dom_t = float(np.mean(times[dom.name]))
     dom_plan = fg.fp8_gemm_plan(dom.M, dom.N, dom.K)
     roofline = {"bound": bound_of(dom),
-                "kernel": f"fp8g_main_kernel variant {dom_plan['variant']} on {dom.name}"
+                "kernel": f"{'fp8g_main5_kernel' if dom_plan['variant'] == 10 else 'fp8g_main_kernel'} "
+                          f"(main variant {dom_plan['variant']}) on {dom.name}"
                 if dom_plan["path_name"] == "main" else f"{dom_plan['path_name']} on {dom.name}",
                 "achieved": round(dom.flops / dom_t / 1e12, 1) if bound_of(dom) == "mfma"
                 else round(dom.bytes / dom_t / 1e9, 1),
