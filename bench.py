@@ -17,7 +17,7 @@ algorithmic bytes / 8.0 TB/s).  `value` is the geometric mean of the five
 fractions.  `roofline` describes the dominant kernel (the main kernel on the
 8192^3 shape); `cpu_baseline` times the CPU oracle on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
 """
 from __future__ import annotations
 
@@ -121,8 +121,8 @@ def _cpu_model() -> str:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-flush", action="store_true", help="warm-cache timing (no 512 MiB rewrite)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=4e10, help="oracle products per shape")

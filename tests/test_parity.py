@@ -27,7 +27,9 @@ def _full_case(M, N, K, seed=42, **kw):
 
 
 # ------------------------------------------------- main path, every variant --
-MAIN_SHAPES = [(300, 520, 4127), (257, 129, 200), (128, 128, 128), (65, 70, 33), (520, 264, 1000)]
+MAIN_SHAPES = [(300, 520, 4127), (257, 129, 200), (128, 128, 128), (65, 70, 33), (520, 264, 1000),
+               # K below one 16-byte chunk, one chunk + 1, one step + 1 byte, exactly three steps
+               (70, 300, 1), (40, 33, 17), (256, 256, 257), (300, 300, 384)]
 
 
 @pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 9, 10])
