@@ -3,7 +3,7 @@
 One step = one call of each of the five benchmark shapes (square 256^3, square
 4096^3, M=32 decode, odd K = 4127, square 8192^3), which together exercise
 every step of the hot path: the main MFMA kernel with its fused epilogue, the
-masked K tail, and the split-K partial + reduce kernels.  Inputs are seeded
+masked K tail, and the split-K kernel with its in-launch reduction.  Inputs are seeded
 synthetic E4M3 operands (N(0,1) quantised with saturation, scale U[0.005,
 0.02]) already resident in HBM.  Before every GEMM a 512 MiB buffer is
 rewritten (outside the timed events) so no operand is served from the 4 MiB

@@ -13,6 +13,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -23,6 +24,20 @@
 namespace {
 
 thread_local std::string g_last_error;
+// Call ids for the split-K tickets.  A ticket left in the (uninitialized)
+// workspace by an earlier call, or any other stale bytes there, must not look
+// like this call's: ids are a counter passed through the splitmix64 finalizer
+// (a bijection), so consecutive ids differ in about half their 56 bits and no
+// simple pattern (zero, small integers, float bits) is likely to match one.
+std::atomic<unsigned long long> g_call_counter{0};
+
+unsigned long long call_id() {
+  unsigned long long z = g_call_counter.fetch_add(1, std::memory_order_relaxed) + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z & ((1ull << 56) - 1);
+}
 
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char *fmt, ...) {
@@ -44,6 +59,10 @@ constexpr int kSkinnyMaxM = 64;       // skinny path handles M <= 64
 constexpr int kMaxSplit = 64;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Bytes of split-K tickets (one 128-byte line per column tile), padded so the
+// partials that follow start 256-byte aligned.
+int64_t splitk_ticket_bytes(int64_t tiles) { return cdiv(tiles * 8 * fp8g::kTicketStride, 256) * 256; }
 
 int check_dims(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return fail(FP8G_ERR_INVALID_ARG, "negative dimension (M=%lld N=%lld K=%lld)",
@@ -105,8 +124,9 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     // Choose rows per workgroup (16 * rb) and the number of K slices S by a
     // bandwidth model: workgroups run in rounds of one per compute unit; a round
     // costs the w bytes one workgroup streams plus a quarter of its x bytes (x
-    // is re-read from L2); S > 1 adds the partials round trip and a second
-    // launch (about 2 us of one CU's share of HBM bandwidth, ~48 KiB).
+    // is re-read from L2); S > 1 adds the partials round trip and the final
+    // reduction by one workgroup per column tile (about 2 us of one CU's share
+    // of HBM bandwidth, ~48 KiB).
     int64_t best_cost = -1, best_rb = 1, best_S = 1;
     for (int rb = 1; rb <= max_rb; ++rb) {
       if (forced_rb != 0 && rb != forced_rb) continue;
@@ -140,7 +160,11 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     p->k_slice = k_slice;
     p->k_tail = (K % chunk) != 0;
     p->grid = cdiv(N, p->tile_n) * S;
-    p->workspace_bytes = S > 1 ? S * M * N * (int64_t)sizeof(float) : 0;
+    // one ticket line per column tile (padded to 256 bytes), then the fp32
+    // partials, tile-major: [column tile][S][M][tile_n]
+    p->workspace_bytes = S > 1 ? splitk_ticket_bytes(cdiv(N, p->tile_n)) +
+                                     cdiv(N, p->tile_n) * S * M * p->tile_n * (int64_t)sizeof(float)
+                               : 0;
     return FP8G_OK;
   }
   if (split_k > 1) return fail(FP8G_ERR_INVALID_ARG, "split_k applies to the split-K path only");
@@ -201,17 +225,24 @@ int run(const void *x, const void *w, const float *scale, void *y, int64_t M, in
     return e == hipSuccess ? FP8G_OK : hip_fail(e, "main kernel launch");
   }
   // split-K
+  void *ws = nullptr;
   float *partials = nullptr;
+  unsigned long long *tickets = nullptr;
   if (p.split_k > 1) {
-    e = hipMallocAsync((void **)&partials, (size_t)p.workspace_bytes, stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(split-K partials)");
+    e = hipMallocAsync(&ws, (size_t)p.workspace_bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(split-K workspace)");
+    // The workspace is not initialized: a ticket carries the call id, so stale
+    // values are harmless, and every partial is written before it is read.
+    tickets = (unsigned long long *)ws;
+    partials = (float *)((char *)ws + splitk_ticket_bytes(cdiv(N, p.tile_n)));
   }
-  fp8g::SkinnyLaunch l{(const uint8_t *)x, (const uint8_t *)w, scale, (uint16_t *)y, partials, (int)M, (int)N, (int)K,
-                       (int)p.k_slice, p.split_k, p.variant, vec};
+  const unsigned long long epoch = call_id();
+  fp8g::SkinnyLaunch l{(const uint8_t *)x, (const uint8_t *)w, scale, (uint16_t *)y, partials, tickets, epoch,
+                       (int)M, (int)N, (int)K, (int)p.k_slice, p.split_k, p.variant, vec};
   e = fp8g::launch_skinny(l, stream);
-  if (partials) {
-    hipError_t f = hipFreeAsync(partials, stream);
-    if (e == hipSuccess && f != hipSuccess) return hip_fail(f, "hipFreeAsync(split-K partials)");
+  if (ws) {
+    hipError_t f = hipFreeAsync(ws, stream);
+    if (e == hipSuccess && f != hipSuccess) return hip_fail(f, "hipFreeAsync(split-K workspace)");
   }
   return e == hipSuccess ? FP8G_OK : hip_fail(e, "split-K kernel launch");
 }

@@ -21,18 +21,25 @@ struct MainLaunch {
   int ystore;    // widest y store: 16 (N % 8 == 0, y 16-byte aligned), 8 (N % 4 == 0, y 8-byte aligned) or 2
 };
 
-// One launch of the skinny split-K kernel (+ the reduce kernel when S > 1).
+// One launch of the skinny split-K kernel (with S > 1 the last workgroup of each
+// column tile adds the slices' partials and writes y in the same launch).
 struct SkinnyLaunch {
   const uint8_t *x;
   const uint8_t *w;
   const float *scale;
   uint16_t *y;
-  float *partials;  // [S, M, N] fp32, only when S > 1
+  float *partials;  // [column tile][S][M][tile_n] fp32, only when S > 1
+  unsigned long long *tickets;  // one per column tile, kTicketStride apart, only when S > 1 (any initial value)
+  unsigned long long epoch;     // id of this call, < 2^56
   int M, N, K;
   int k_slice, S;
   int variant;      // skinny configuration id
   bool vec;         // N % 4 == 0 and y 8-byte aligned
 };
+
+// Split-K tickets sit one 128-byte cache line apart (in 8-byte units): the
+// atomics of different column tiles then never queue on the same line.
+constexpr int kTicketStride = 16;
 
 // Kernel-side tile geometry of each configuration id (also used by the planner).
 struct MainConfig {

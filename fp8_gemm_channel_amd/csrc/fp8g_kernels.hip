@@ -54,6 +54,12 @@ __device__ char llvm_buffer_load_i8(v4i rsrc, uint32_t voffset, uint32_t soffset
     __asm("llvm.amdgcn.raw.buffer.load.i8");
 __device__ float llvm_buffer_load_f32(v4i rsrc, uint32_t voffset, uint32_t soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.f32");
+__device__ v4f llvm_buffer_load_v4f32(v4i rsrc, uint32_t voffset, uint32_t soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4f32");
+__device__ void llvm_buffer_store_v4f32(v4f data, v4i rsrc, uint32_t voffset, uint32_t soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.v4f32");
+__device__ void llvm_buffer_store_f32(float data, v4i rsrc, uint32_t voffset, uint32_t soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.f32");
 
 // Buffer descriptor: base address, stride 0 (raw), range `bytes`, and the
 // gfx9 data-format word (32-bit elements, bounds-checked raw access).
@@ -811,13 +817,16 @@ __global__ __launch_bounds__(512, 1) void fp8g_main5_kernel(MainArgs a) {
 //
 // blockIdx.y selects the K slice [s * k_slice, min(K, (s+1) * k_slice)).  With one
 // slice the kernel scales and writes bf16 y; with several it writes unscaled fp32
-// partials P[s, m, n] that the reduce kernel adds in slice order.
+// partials that the last workgroup of the column tile adds in slice order
+// (splitk_finish).
 struct SkinnyArgs {
   const uint8_t *x;
   const uint8_t *w;
   const float *scale;
   uint16_t *y;
-  float *P;
+  float *P;                  // fp32 partials [column tile][S][M][16*RB] (S > 1)
+  unsigned long long *tickets;  // one per column tile, kTicketStride apart (S > 1), any initial value
+  unsigned long long epoch;  // this call's id (< 2^56), unique among calls that share tickets
   int M, N, K;
   int k_slice;
   int vec;  // y rows allow 8-byte stores / P rows 16-byte stores (N % 4 == 0)
@@ -862,10 +871,106 @@ __device__ __forceinline__ v4f mfma16(const v8i &a, const v8i &b, const v4f &c) 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// Cache policy of the split-K partials and their readers: device scope (SC1),
+// the encoding the compiler gives agent-scope atomic loads and stores.  Stores
+// write through the XCD's L2 to the device coherence point and loads do not hit
+// stale lines, so the partials pass between XCDs without flushing or
+// invalidating whole caches.
+constexpr int kDeviceScope = 16;
+
+// Split-K with S > 1 slices, in the same launch.  Every workgroup of a column
+// tile has stored its unscaled fp32 partials (tile-major: the tile's S slices
+// of M x 16*RB floats are contiguous); the last of the tile's S workgroups to
+// finish adds them in slice order s = 0, 1, ..., S-1, scales, rounds to bf16 and
+// writes y, so the result does not depend on the order the workgroups ran in.
+// "Last" is decided on a 64-bit ticket per tile holding (call id << 8 | count):
+// a ticket left by another call restarts at count 1, so nothing is zeroed
+// before the launch.  Ordering: each wave waits until its device-scope partial
+// stores are acknowledged, the workgroup meets at a barrier, and only then does
+// one thread take the ticket; the last workgroup reads with device scope after
+// its ticket.  No L2 write-back or invalidate is needed for these accesses.
+template <int RB>
+__device__ __forceinline__ void splitk_finish(const SkinnyArgs &a, int n0, int *flag) {
+  constexpr int R = 16 * RB;
+  const int S = (int)gridDim.y;
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long *t = a.tickets + (size_t)blockIdx.x * kTicketStride;
+    unsigned long long old = __hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long want;
+    for (;;) {
+      want = (old >> 8) == a.epoch ? old + 1 : (a.epoch << 8) | 1ull;
+      if (__hip_atomic_compare_exchange_strong(t, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        break;
+    }
+    *flag = (int)(want & 0xFFull) == S;
+  }
+  __syncthreads();
+  if (!*flag) return;
+  asm volatile("" : : : "memory");
+  const v4i rsrc_p = make_rsrc(a.P + (size_t)blockIdx.x * S * a.M * R, (uint32_t)(S * a.M * R) * 4u);
+  const uint32_t slice_bytes = (uint32_t)(a.M * R) * 4u;
+  constexpr int q4 = R / 4;  // four-column groups in the tile
+  constexpr uint32_t kOut = 0x80000000u;  // past the descriptor's range: reads 0
+  // Each thread sums IT items (four columns of one row), IT * SB loads in flight
+  // at a time; loads that fall past S or past the items read zero and are unused.
+  constexpr int IT = 2, SB = 8;
+  const int items = a.M * q4;
+  const v4i rsrc_s = make_rsrc(a.scale + n0, (uint32_t)min(R, a.N - n0) * 4u);
+  for (int i0 = threadIdx.x; i0 < items; i0 += IT * (int)blockDim.x) {
+    uint32_t off[IT];
+    v4f acc[IT], sc[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int idx = i0 + i * (int)blockDim.x;
+      off[i] = idx < items ? (uint32_t)((idx / q4) * R + 4 * (idx % q4)) * 4u : kOut;
+      // scale of the item's four columns, requested before the partials
+      sc[i] = llvm_buffer_load_v4f32(rsrc_s, idx < items ? (uint32_t)(4 * (idx % q4)) * 4u : kOut, 0, 0);
+      acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int s0 = 0; s0 < S; s0 += SB) {
+      v4f v[IT][SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+#pragma unroll
+        for (int i = 0; i < IT; ++i)
+          v[i][j] = llvm_buffer_load_v4f32(rsrc_p, s0 + j < S ? off[i] + (uint32_t)(s0 + j) * slice_bytes : kOut, 0,
+                                           kDeviceScope);
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+          if (s0 + j >= S) continue;
+          // slice 0 starts the sum (keeps its sign of zero), the others add in order
+          if (s0 + j == 0) acc[i] = v[i][j];
+          else { acc[i].x += v[i][j].x; acc[i].y += v[i][j].y; acc[i].z += v[i][j].z; acc[i].w += v[i][j].w; }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int idx = i0 + i * (int)blockDim.x;
+      if (idx >= items) continue;
+      const int m = idx / q4, n = n0 + 4 * (idx % q4);
+      if (n >= a.N) continue;
+      uint16_t *yr = a.y + (size_t)m * a.N;
+      const uint32_t b0 = bf16_rne(acc[i].x * sc[i].x), b1 = bf16_rne(acc[i].y * sc[i].y);
+      const uint32_t b2 = bf16_rne(acc[i].z * sc[i].z), b3 = bf16_rne(acc[i].w * sc[i].w);
+      if (a.vec) {
+        *(uint2 *)(yr + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      } else {
+        const uint32_t b[4] = {b0, b1, b2, b3};
+        for (int e = 0; e < 4 && n + e < a.N; ++e) yr[n + e] = (uint16_t)b[e];
+      }
+    }
+  }
+}
+
 // End of a skinny workgroup: the four waves' sums are added through LDS (`red`,
 // 4*RB*MB*4*64 floats) in wave order, so the result does not depend on timing;
 // wave v finishes blocks v, v+4, ...  One K slice: scale and bf16 store; several:
-// unscaled fp32 partials P[s, m, n] for the reduce kernel.
+// unscaled fp32 partials, which the column tile's last workgroup adds.
 template <int RB, int MB>
 __device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const SkinnyArgs &a, float *red, int n0,
                                               int s, int wave, int lane) {
@@ -893,14 +998,11 @@ __device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const Sk
     const int m = 16 * mb + lr;
     if (m >= a.M) continue;
     if (gridDim.y > 1) {
-      float *pr = a.P + ((size_t)s * a.M + m) * a.N;
-      if (a.vec) {
-        if (n < a.N) *(float4 *)(pr + n) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < a.N) pr[n + e] = v[e];
-      }
+      // all 16*RB columns of the tile are stored, also those past N (never read)
+      const v4i rsrc_p = make_rsrc(a.P + ((size_t)blockIdx.x * gridDim.y + s) * a.M * (16 * RB),
+                                   (uint32_t)(a.M * 16 * RB) * 4u);
+      llvm_buffer_store_v4f32(v4f{v[0], v[1], v[2], v[3]}, rsrc_p, (uint32_t)(m * 16 * RB + (n - n0)) * 4u, 0,
+                              kDeviceScope);
     } else {
       uint16_t *yr = a.y + (size_t)m * a.N;
       uint32_t bits[4];
@@ -915,6 +1017,7 @@ __device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const Sk
       }
     }
   }
+  if (gridDim.y > 1) splitk_finish<RB>(a, n0, (int *)red);
 }
 
 template <int RB, int MB>
@@ -1153,39 +1256,6 @@ __global__ __launch_bounds__(256, 1) void fp8g_skinny_direct_kernel(SkinnyArgs a
   skinny_finish<RB, MB>(acc, a, red, n0, s, wave, lane);
 }
 
-// y[m, n..n+3] = bf16((sum_{s<S} P[s, m, n..n+3]) * scale[n..n+3]), slices
-// added in order s = 0, 1, ..., S-1.  One thread per four outputs of a row.
-template <bool VEC>
-__global__ __launch_bounds__(256) void fp8g_splitk_reduce_kernel(const float *__restrict__ P,
-                                                                 const float *__restrict__ scale,
-                                                                 uint16_t *__restrict__ y, int M, int N, int S) {
-  const int n4 = (N + 3) / 4;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)M * n4) return;
-  const int m = (int)(idx / n4);
-  const int n = (int)(idx - (int64_t)m * n4) * 4;
-  const size_t plane = (size_t)M * N;
-  const float *p = P + (size_t)m * N + n;
-  uint16_t *yr = y + (size_t)m * N;
-  if (VEC) {
-    float4 acc = *(const float4 *)p;
-    for (int s = 1; s < S; ++s) {
-      const float4 v = *(const float4 *)(p + s * plane);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    // scale is only guaranteed 4-byte aligned
-    const uint32_t b0 = bf16_rne(acc.x * scale[n + 0]), b1 = bf16_rne(acc.y * scale[n + 1]);
-    const uint32_t b2 = bf16_rne(acc.z * scale[n + 2]), b3 = bf16_rne(acc.w * scale[n + 3]);
-    *(uint2 *)(yr + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-  } else {
-    for (int e = 0; e < 4 && n + e < N; ++e) {
-      float acc = p[e];
-      for (int s = 1; s < S; ++s) acc += p[s * plane + e];
-      yr[n + e] = (uint16_t)bf16_rne(acc * scale[n + e]);
-    }
-  }
-}
-
 __global__ __launch_bounds__(256) void fp8g_zero_kernel(uint16_t *__restrict__ y, int64_t count) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = 0;
@@ -1259,16 +1329,10 @@ hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
 
 template <int RB, int MB, bool DIRECT>
 static hipError_t launch_skinny_cfg(const SkinnyLaunch &l, hipStream_t stream) {
-  SkinnyArgs a{l.x, l.w, l.scale, l.y, l.partials, l.M, l.N, l.K, l.k_slice, l.N % 4 == 0 && (l.S > 1 || l.vec)};
+  SkinnyArgs a{l.x, l.w, l.scale, l.y, l.partials, l.tickets, l.epoch, l.M, l.N, l.K, l.k_slice, l.vec};
   const dim3 grid((unsigned)((l.N + 16 * RB - 1) / (16 * RB)), (unsigned)l.S), block(256);
   if constexpr (DIRECT) fp8g_skinny_direct_kernel<RB, MB, 4><<<grid, block, 0, stream>>>(a);
   else fp8g_splitk_partial_kernel<RB, MB><<<grid, block, 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || l.S == 1) return e;
-  const int64_t threads = (int64_t)l.M * ((l.N + 3) / 4);
-  const dim3 rgrid((unsigned)((threads + 255) / 256));
-  if (l.vec) fp8g_splitk_reduce_kernel<true><<<rgrid, block, 0, stream>>>(l.partials, l.scale, l.y, l.M, l.N, l.S);
-  else fp8g_splitk_reduce_kernel<false><<<rgrid, block, 0, stream>>>(l.partials, l.scale, l.y, l.M, l.N, l.S);
   return hipGetLastError();
 }
 

@@ -23,17 +23,18 @@
  *   - every call reads the live operands and writes a fresh output; nothing is
  *     cached between calls: "Claude Fable 5", Triton split-K cell;
  *     "Qwen 3.8 Max", stale odd-K pad-cache cell (what goes wrong otherwise).
- *   - skinny M runs as split-K with fp32 partials and a separate
- *     reduce/scale/cast step: "Claude Fable 5", Triton split-K cell;
- *     "Kimi K3 (256k)", SM120 cell (skinny path with a scaled finalize kernel).
+ *   - skinny M runs as split-K with fp32 partials and a reduce/scale/cast
+ *     step: "Claude Fable 5", Triton split-K cell; "Kimi K3 (256k)", SM120
+ *     cell (skinny path with a scaled finalize kernel).  Here the step runs in
+ *     the same launch, by the last workgroup to finish each column tile.
  *   - K need not be a multiple of any tile size: the pages zero-pad copies of
  *     the operands ("Kimi K3 (256k)", SM100 persistent-TMA Triton cell: zero
  *     bytes add nothing to the dot); this library masks the K tail inside the
  *     kernel instead and never copies an operand.
  *
  * Ownership and threading: the caller owns every buffer.  The library keeps no
- * state between calls and has no globals besides a thread-local copy of the
- * last error message.  Calls are asynchronous: they enqueue kernels on
+ * data between calls; its only globals are a thread-local copy of the last
+ * error message and an atomic call counter (ids for split-K tickets).  Calls are asynchronous: they enqueue kernels on
  * `stream` (a hipStream_t; NULL is the default stream) and return without
  * synchronising.  Buffers must stay valid until that work has finished.
  */
@@ -63,8 +64,9 @@ extern "C" {
 #define FP8G_PATH_NONE 0   /* M == 0 or N == 0: nothing to do */
 #define FP8G_PATH_ZERO 1   /* K == 0: y is filled with +0 (the empty sum) */
 #define FP8G_PATH_MAIN 2   /* tiled MFMA kernel, fused scale/bf16 epilogue */
-#define FP8G_PATH_SPLITK 3 /* skinny M: split-K partial kernel, then the
-                              reduce/scale/cast kernel when split_k > 1 */
+#define FP8G_PATH_SPLITK 3 /* skinny M: one split-K launch; with split_k > 1
+                              the last slice of each column tile to finish
+                              adds the fp32 partials, scales and casts */
 
 /* A launch plan.  Pure host integer arithmetic; computing one makes no HIP call. */
 typedef struct fp8g_plan {
@@ -78,7 +80,8 @@ typedef struct fp8g_plan {
     int32_t group_m;        /* tile-raster group height (main path) */
     int32_t k_tail;         /* 1 if K is not a multiple of the K step */
     int64_t grid;           /* workgroups of the first kernel */
-    int64_t workspace_bytes;/* fp32 partials the call allocates (split_k > 1) */
+    int64_t workspace_bytes;/* per-tile tickets + fp32 partials the call
+                               allocates (split_k > 1) */
 } fp8g_plan;
 
 /* y = bf16_rne((x . w^T) * scale), as defined above.
@@ -90,9 +93,9 @@ typedef struct fp8g_plan {
  *   stream         : hipStream_t, or NULL for the default stream.
  * Returns FP8G_OK, FP8G_ERR_INVALID_ARG (bad sizes, null pointers with non-zero
  * extent, misaligned scale/y, overlapping output), or FP8G_ERR_HIP (no device,
- * launch failure, or failure to allocate split-K partials; those are
+ * launch failure, or failure to allocate the split-K workspace; that is
  * allocated stream-ordered with hipMallocAsync and freed with hipFreeAsync on
- * `stream` inside the call). */
+ * `stream` inside the call, so calls on different streams never share it). */
 int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y,
                     int64_t M, int64_t N, int64_t K, void *stream);
 

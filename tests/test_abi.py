@@ -35,6 +35,13 @@ def test_strerror_is_static_and_total():
     assert fg.fp8_gemm_strerror(12345) == "unknown status"
 
 
+def _splitk_workspace(p, M, N):
+    # one 128-byte ticket line per column tile, padded to 256 bytes, then fp32
+    # partials [column tile][split_k][M][tile_n]
+    tiles = -(-N // p["tile_n"])
+    return -(-tiles * 128 // 256) * 256 + tiles * p["split_k"] * M * p["tile_n"] * 4
+
+
 @pytest.mark.parametrize("wl", synth.WORKLOADS, ids=lambda w: w.name)
 def test_plan_of_benchmark_shapes(wl):
     p = fg.fp8_gemm_plan(wl.M, wl.N, wl.K)
@@ -43,7 +50,7 @@ def test_plan_of_benchmark_shapes(wl):
         assert p["split_k"] >= 1 and p["k_slice"] * p["split_k"] >= wl.K
         assert (p["split_k"] - 1) * p["k_slice"] < wl.K, "no empty slice"
         assert p["k_slice"] % 128 == 0
-        assert p["workspace_bytes"] == (p["split_k"] * wl.M * wl.N * 4 if p["split_k"] > 1 else 0)
+        assert p["workspace_bytes"] == (_splitk_workspace(p, wl.M, wl.N) if p["split_k"] > 1 else 0)
     else:
         assert p["path_name"] == "main"
         assert p["grid"] == -(-wl.M // p["tile_m"]) * -(-wl.N // p["tile_n"])
@@ -66,7 +73,8 @@ def test_plan_special_extents():
 
 def test_plan_overrides():
     p = fg.fp8_gemm_plan_ex(32, 12288, 4096, fg.PATH_SPLITK, 1, 4)
-    assert p["split_k"] == 4 and p["k_slice"] == 1024 and p["workspace_bytes"] == 4 * 32 * 12288 * 4
+    assert p["split_k"] == 4 and p["k_slice"] == 1024
+    assert p["workspace_bytes"] == _splitk_workspace(p, 32, 12288)
     p = fg.fp8_gemm_plan_ex(32, 4096, 4096, fg.PATH_MAIN, 2, 0)
     assert p["path_name"] == "main" and p["tile_m"] == 128
     # split_k larger than the number of 128-byte chunks collapses to non-empty slices

@@ -135,6 +135,31 @@ def test_alternating_k_shapes_share_nothing():
         compare(run(*b), rb, "K=4096")
 
 
+def test_splitk_back_to_back_calls_without_sync():
+    """Split-K calls queued on one stream with no synchronisation between them:
+    each call's last-arriving workgroups must add exactly that call's partials
+    (stream-ordered workspaces may reuse the same memory and its old tickets)."""
+    cases = [((32, 1000, 4127), 4), ((17, 777, 3000), 3), ((32, 1000, 4127), 7), ((64, 264, 600), 2)]
+    data = [synth.fp8_inputs(M, N, K, seed=20 + i) for i, ((M, N, K), _) in enumerate(cases)]
+    dev = [tuple(to_dev(a.astype(np.float32) if a.dtype != np.uint8 else a) for a in d) for d in data]
+    refs = [oracle.gemm_scaled(*d) for d in data]
+    outs = []
+    say("split-K back to back, 5 rounds of 4 shapes")
+    for _ in range(5):
+        for ((M, N, K), S), (xd, wd, sd) in zip(cases, dev):
+            out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            out.view(torch.int16).fill_(-1)
+            fg.fp8_gemm(xd, wd, sd, out=out, path=fg.PATH_SPLITK, split_k=S)
+            outs.append(out)
+    torch.cuda.synchronize()
+    first = [o.view(torch.int16).cpu().numpy().view(np.uint16) for o in outs[:len(cases)]]
+    for i, (f, r) in enumerate(zip(first, refs)):
+        compare(f, r, f"case {i}")
+    for j, o in enumerate(outs[len(cases):]):
+        got = o.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, first[j % len(cases)]), f"call {j + len(cases)} differs"
+
+
 @pytest.mark.parametrize("shape,kw", [
     ((4096, 4096, 4127), {}), ((32, 12288, 4096), {}),
     ((32, 12288, 4096), dict(path=fg.PATH_SPLITK, split_k=4)), ((256, 256, 256), {}),
