@@ -42,7 +42,8 @@ class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("variant", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("k_slice", ctypes.c_int64), ("group_m", ctypes.c_int32), ("k_tail", ctypes.c_int32),
-                ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+                ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("dp_tiles", ctypes.c_int32), ("sk_groups", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         d = {name: getattr(self, name) for name, _ in self._fields_}

@@ -29,6 +29,7 @@ thread_local std::string g_last_error;
 // like this call's: ids are a counter passed through the splitmix64 finalizer
 // (a bijection), so consecutive ids differ in about half their 56 bits and no
 // simple pattern (zero, small integers, float bits) is likely to match one.
+// Ids keep 48 bits: a ticket holds (id << 16 | arrivals).
 std::atomic<unsigned long long> g_call_counter{0};
 
 unsigned long long call_id() {
@@ -36,7 +37,7 @@ unsigned long long call_id() {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
   z ^= z >> 31;
-  return z & ((1ull << 56) - 1);
+  return z & ((1ull << 48) - 1);
 }
 
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -57,6 +58,7 @@ int hip_fail(hipError_t e, const char *what) {
 constexpr int kNumCUs = 256;          // MI355X compute units
 constexpr int kSkinnyMaxM = 64;       // skinny path handles M <= 64
 constexpr int kMaxSplit = 64;
+constexpr int kMaxStreamK = 2048;    // stream-K workgroups (2 partial tiles each must stay below 2 GiB)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -73,15 +75,34 @@ int check_dims(int64_t M, int64_t N, int64_t K) {
   return FP8G_OK;
 }
 
-// Main-path configuration for (M, N) when not forced.  Measured on MI355X
-// (cold cache): 256x256 tiles win as soon as they occupy half the compute
-// units (3072^3: 144 tiles, 49 us against 58 us with 128x128); 128x128 tiles
-// need a full wave to beat 64x64 (256x8192x8192: 128 tiles of 128x128 take
-// 62 us, 512 tiles of 64x64 54 us; 2048^3: 256 tiles, 21.7 against 23.9 us).
-int auto_main_variant(int64_t M, int64_t N) {
-  if (cdiv(M, 256) * cdiv(N, 256) >= kNumCUs / 2) return 10;
-  if (cdiv(M, 128) * cdiv(N, 128) >= kNumCUs) return 2;
-  return 3;
+// Main-path configuration for (M, N, K) when not forced.  Few tiles: 64 x 64
+// (variant 3, several workgroups per compute unit).  Otherwise the cheapest of
+// three tile sizes by  waves of tiles x flops per tile / sustained rate of one
+// compute unit, the rates measured on MI355X with full waves (cold cache):
+// 256 x 256 (variant 10) ~10.4 TFLOP/s (8192^3), 128 x 256 (variant 17) ~7.0
+// (1024 x 8192 x 8192), 128 x 128 with eight waves (variant 18) ~4.9
+// (512 x 8192 x 8192).  On the shapes measured this picks the fastest variant:
+// 4096^3, 8192^3, 3072^3 -> 10; 1024 x 8192^2, 1536 x 4096^2, 512 x 12288 x
+// 4096 -> 17; 512 x 8192^2, 768 x 4096^2, 2048^3 -> 18; 128 x 8192^2 -> 3.
+int auto_main_variant(int64_t M, int64_t N, int64_t K) {
+  if (cdiv(M, 128) * cdiv(N, 128) < kNumCUs / 2) return 3;
+  struct Cand {
+    int variant, bm, bn;
+    double tflops_per_cu;
+  };
+  static const Cand cands[] = {{10, 256, 256, 10.4}, {17, 128, 256, 7.0}, {18, 128, 128, 4.9}};
+  const double kp = (double)cdiv(K, 128) * 128;
+  int best = 10;
+  double best_t = -1;
+  for (const Cand &c : cands) {
+    const int64_t waves = cdiv(cdiv(M, c.bm) * cdiv(N, c.bn), kNumCUs);
+    const double t = (double)waves * 2.0 * c.bm * c.bn * kp / (c.tflops_per_cu * 1e12);
+    if (best_t < 0 || t < best_t) {
+      best_t = t;
+      best = c.variant;
+    }
+  }
+  return best;
 }
 
 int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, int32_t split_k, fp8g_plan *p) {
@@ -93,7 +114,8 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
   p->k_slice = K;
   if (path != 0 && path != FP8G_PATH_MAIN && path != FP8G_PATH_SPLITK)
     return fail(FP8G_ERR_INVALID_ARG, "unknown path override %d", path);
-  if (split_k < 0 || split_k > kMaxSplit) return fail(FP8G_ERR_INVALID_ARG, "split_k=%d outside 0..%d", split_k, kMaxSplit);
+  if (split_k < 0 || split_k > kMaxStreamK)
+    return fail(FP8G_ERR_INVALID_ARG, "split_k=%d outside 0..%d", split_k, kMaxStreamK);
   if (variant < 0) return fail(FP8G_ERR_INVALID_ARG, "negative variant %d", variant);
   if (M == 0 || N == 0) {
     p->path = FP8G_PATH_NONE;
@@ -107,6 +129,8 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
   if (path == 0) path = (M <= kSkinnyMaxM) ? FP8G_PATH_SPLITK : FP8G_PATH_MAIN;
   if (path == FP8G_PATH_SPLITK) {
     if (M > kSkinnyMaxM) return fail(FP8G_ERR_INVALID_ARG, "split-K path needs M <= %d (M=%lld)", kSkinnyMaxM, (long long)M);
+    if (split_k > kMaxSplit)
+      return fail(FP8G_ERR_INVALID_ARG, "split-K path takes split_k 0..%d (split_k=%d)", kMaxSplit, split_k);
     // Variants 1-5 force the LDS-ring kernel with 16 * variant w rows per
     // workgroup, 11-15 the direct-to-register kernel with 16 * (variant - 10);
     // 0 lets the planner choose the rows for the LDS-ring kernel, which streams
@@ -170,8 +194,10 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
                                : 0;
     return FP8G_OK;
   }
-  if (split_k > 1) return fail(FP8G_ERR_INVALID_ARG, "split_k applies to the split-K path only");
-  if (variant == 0) variant = auto_main_variant(M, N);
+  if (variant == 0) variant = auto_main_variant(M, N, K);
+  if (split_k > 1 && variant != 16)
+    return fail(FP8G_ERR_INVALID_ARG, "split_k applies to the split-K path and to main variant 16 only");
+
   const fp8g::MainConfig *c = fp8g::main_config(variant);
   if (!c) return fail(FP8G_ERR_INVALID_ARG, "unknown main variant %d", variant);
   const int64_t tiles_m = cdiv(M, c->bm), tiles_n = cdiv(N, c->bn);
@@ -184,6 +210,23 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
   p->group_m = (int32_t)(tiles_m < 8 ? tiles_m : 8);
   p->k_tail = (K % c->bk) != 0;
   p->grid = tiles_m * tiles_n;
+  p->dp_tiles = (int32_t)(tiles_m * tiles_n);
+  if (variant == 16) {
+    // Stream-K: whole waves of tiles stay one tile per workgroup except the
+    // last, which joins the partial wave; one workgroup per compute unit then
+    // splits the (tile, K step) units of those tiles evenly, so every compute
+    // unit gets between one and two tiles' worth (less than one when the tiles
+    // do not fill a wave).  split_k forces the number of stream-K workgroups.
+    const int64_t T = tiles_m * tiles_n, nk = cdiv(K, c->bk);
+    const int64_t n_dp = T > kNumCUs ? (T / kNumCUs - 1) * kNumCUs : 0;
+    if (T * nk >= INT32_MAX) return fail(FP8G_ERR_UNSUPPORTED, "stream-K needs tiles x K steps below 2^31");
+    int64_t n_sk = split_k > 0 ? split_k : kNumCUs;
+    if (n_sk > (T - n_dp) * nk) n_sk = (T - n_dp) * nk;  // at least one unit each
+    p->dp_tiles = (int32_t)n_dp;
+    p->sk_groups = (int32_t)n_sk;
+    p->grid = n_dp + n_sk;
+    p->workspace_bytes = splitk_ticket_bytes(T - n_dp) + 2 * n_sk * fp8g::kMainPartialBytes;
+  }
   return FP8G_OK;
 }
 
@@ -224,7 +267,25 @@ int run(const void *x, const void *w, const float *scale, void *y, int64_t M, in
     const int ystore = (N % 8 == 0 && (uintptr_t)y % 16 == 0) ? 16 : vec ? 8 : 2;
     fp8g::MainLaunch l{(const uint8_t *)x, (const uint8_t *)w, scale, (uint16_t *)y, (int)M, (int)N, (int)K,
                        (int)cdiv(M, p.tile_m), (int)cdiv(N, p.tile_n), p.group_m, p.variant, p.k_tail != 0, ystore};
+    void *ws = nullptr;
+    if (p.sk_groups > 0) {
+      // tickets for the stream-K tiles, then two partial tiles per stream-K
+      // workgroup; uninitialized (tickets carry the call id, partials are
+      // written before they are read)
+      e = hipMallocAsync(&ws, (size_t)p.workspace_bytes, stream);
+      if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(stream-K workspace)");
+      const int64_t sk_tiles = cdiv(M, p.tile_m) * cdiv(N, p.tile_n) - p.dp_tiles;
+      l.n_dp = p.dp_tiles;
+      l.n_sk = p.sk_groups;
+      l.tickets = (unsigned long long *)ws;
+      l.partials = (float *)((char *)ws + splitk_ticket_bytes(sk_tiles));
+      l.epoch = call_id();
+    }
     e = fp8g::launch_main(l, stream);
+    if (ws) {
+      hipError_t f = hipFreeAsync(ws, stream);
+      if (e == hipSuccess && f != hipSuccess) return hip_fail(f, "hipFreeAsync(stream-K workspace)");
+    }
     return e == hipSuccess ? FP8G_OK : hip_fail(e, "main kernel launch");
   }
   // split-K

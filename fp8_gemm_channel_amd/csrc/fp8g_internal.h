@@ -19,6 +19,11 @@ struct MainLaunch {
   int variant;   // main-path configuration id
   bool k_tail;   // K % tile_k != 0
   int ystore;    // widest y store: 16 (N % 8 == 0, y 16-byte aligned), 8 (N % 4 == 0, y 8-byte aligned) or 2
+  // variant 16 (stream-K) only:
+  int n_dp = 0, n_sk = 0;                 // whole-tile workgroups, stream-K workgroups
+  float *partials = nullptr;              // 2 * n_sk partial tiles of kMainPartialBytes
+  unsigned long long *tickets = nullptr;  // one per stream-K tile, kTicketStride apart (any initial value)
+  unsigned long long epoch = 0;           // id of this call, < 2^48
 };
 
 // One launch of the skinny split-K kernel (with S > 1 the last workgroup of each
@@ -30,7 +35,7 @@ struct SkinnyLaunch {
   uint16_t *y;
   float *partials;  // [column tile][S][M][tile_n] fp32, only when S > 1
   unsigned long long *tickets;  // one per column tile, kTicketStride apart, only when S > 1 (any initial value)
-  unsigned long long epoch;     // id of this call, < 2^56
+  unsigned long long epoch;     // id of this call, < 2^48
   int M, N, K;
   int k_slice, S;
   int variant;      // skinny configuration id
@@ -40,6 +45,8 @@ struct SkinnyLaunch {
 // Split-K tickets sit one 128-byte cache line apart (in 8-byte units): the
 // atomics of different column tiles then never queue on the same line.
 constexpr int kTicketStride = 16;
+// One partial 256 x 256 fp32 tile of the stream-K main kernel.
+constexpr int64_t kMainPartialBytes = 256 * 256 * 4;
 
 // Kernel-side tile geometry of each configuration id (also used by the planner).
 struct MainConfig {

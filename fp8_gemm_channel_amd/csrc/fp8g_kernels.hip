@@ -182,7 +182,42 @@ struct MainArgs {
   int M, N, K;
   int tiles_m, tiles_n, group_m;
   int ystore;  // widest y store allowed by N and y's alignment: 16, 8 or 2 bytes
+  // Stream-K (five-slot kernel only; zero elsewhere).  Workgroups 0 .. n_dp-1
+  // each compute one whole tile, the first n_dp tiles of the raster order; the
+  // n_sk workgroups after them split the (tile, K step) units of the remaining
+  // tiles evenly.
+  int n_dp, n_sk;
+  float *P;                      // 2 partial-tile slots per stream-K workgroup
+  unsigned long long *tickets;   // one per stream-K tile, kTicketStride apart
+  unsigned long long epoch;      // this call's id (< 2^48)
 };
+
+// Cache policy of partial sums that pass between workgroups: device scope
+// (SC1), the encoding the compiler gives agent-scope atomic loads and stores.
+// Stores write through the XCD's L2 to the device coherence point and loads do
+// not hit stale lines, so partials move between XCDs without flushing or
+// invalidating whole caches.
+constexpr int kDeviceScope = 16;
+constexpr uint32_t kOut = 0x80000000u;  // a buffer offset past every descriptor's range: reads 0
+
+// Last-arrival hand-off: every workgroup that contributes to an output tile
+// takes the tile's ticket once, after its partial sums are visible device-wide;
+// the one that brings the count to `target` finishes the tile.  A ticket holds
+// (call id << 16 | arrivals); a ticket left by another call (or any stale
+// bytes) restarts at one arrival, so tickets need no zeroing before a launch.
+// The compare-and-swap loop is lock-free: a failed attempt means another
+// workgroup's succeeded.
+__device__ __forceinline__ bool take_ticket(unsigned long long *t, unsigned long long epoch, int target) {
+  unsigned long long old = __hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned long long want;
+  for (;;) {
+    want = (old >> 16) == epoch ? old + 1 : (epoch << 16) | 1ull;
+    if (__hip_atomic_compare_exchange_strong(t, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      break;
+  }
+  return (int)(want & 0xFFFFull) == target;
+}
 
 // Scheduling pattern for NM MFMAs and NR LDS reads spread evenly: MFMA q is
 // followed by reads [q*NR/NM, (q+1)*NR/NM).
@@ -201,11 +236,11 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 // contiguous range of tiles, then walk that range in groups of group_m tile
 // rows (all tile columns of a group before the next group) so the x rows and
 // w rows a group shares stay in the XCD's L2.
-__device__ __forceinline__ void tile_coords(const MainArgs &a, int &tm, int &tn) {
-  const int total = a.tiles_m * a.tiles_n;
-  const int pid = blockIdx.x;
-  const int xcd = pid & 7, q8 = total >> 3, r8 = total & 7;
-  const int lpid = xcd * q8 + min(xcd, r8) + (pid >> 3);
+__device__ __forceinline__ int xcd_remap(int pid, int count) {
+  const int xcd = pid & 7, q8 = count >> 3, r8 = count & 7;
+  return xcd * q8 + min(xcd, r8) + (pid >> 3);
+}
+__device__ __forceinline__ void raster(const MainArgs &a, int lpid, int &tm, int &tn) {
   const int per_group = a.group_m * a.tiles_n;
   const int gid = lpid / per_group;
   const int first_m = gid * a.group_m;
@@ -213,6 +248,9 @@ __device__ __forceinline__ void tile_coords(const MainArgs &a, int &tm, int &tn)
   const int within = lpid - gid * per_group;
   tm = first_m + within % gsize;
   tn = within / gsize;
+}
+__device__ __forceinline__ void tile_coords(const MainArgs &a, int &tm, int &tn) {
+  raster(a, xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n), tm, tn);
 }
 
 // Epilogue of the main kernels: y[m, n..n+3] = bf16(acc * scale[n..n+3]) for a
@@ -222,7 +260,7 @@ __device__ __forceinline__ void tile_coords(const MainArgs &a, int &tm, int &tn)
 template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void main_epilogue(const v16f (&acc)[BN / WN / 32][BM / WM / 32], const MainArgs &a,
                                               uint8_t *smem, const float *s_lds, int m0, int n0, int wave,
-                                              int lane) {
+                                              int lane, int tid) {
   constexpr int NWAVES = WM * WN, TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   // Epilogue: y[m, n..n+3] = bf16(acc * scale[n..n+3]), written through LDS so
   // that y leaves in whole rows.  A lane's results are four consecutive n of
@@ -236,7 +274,6 @@ __device__ __forceinline__ void main_epilogue(const v16f (&acc)[BN / WN / 32][BM
   constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
   constexpr int PITCH = 2 * BN;
   constexpr int NTHREADS = NWAVES * 64;
-  const int tid = threadIdx.x;
   const int g = lane >> 5, lr = lane & 31;
   const int wave_m = wave % WM, wave_n = wave / WM;
   __syncthreads();  // every wave is done with the stage buffers (and s_lds is published)
@@ -363,7 +400,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   static_assert(NWAVES % 2 == 0 && BN % 16 == 0, "block-invariant swizzle");
   const int dma_lrow = wave * ROWS_PER_KB + lane / CH;  // row within block t = 0
   const int dma_chunk = (lane % CH) ^ swz<BK>(dma_lrow);
-  const uint32_t lane_off = (uint32_t)dma_lrow * (uint32_t)K + (uint32_t)dma_chunk * 16u;
+  const uint32_t laneff = (uint32_t)dma_lrow * (uint32_t)K + (uint32_t)dma_chunk * 16u;
   const uint32_t blk_stride = (uint32_t)(NWAVES * ROWS_PER_KB) * (uint32_t)K;
   v4i rs[DPW];
 #pragma unroll
@@ -382,7 +419,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
     const uint32_t k0 = (uint32_t)kt * BK;
     const uint32_t sb = smem_base + (uint32_t)st * STAGE_BYTES;
 #pragma unroll
-    for (int t = 0; t < DPW; ++t) dma16(rs[t], sb + (uint32_t)(t * NWAVES + wave) * 1024u, lane_off, k0);
+    for (int t = 0; t < DPW; ++t) dma16(rs[t], sb + (uint32_t)(t * NWAVES + wave) * 1024u, laneff, k0);
   };
   // Last, partial K step (k0 + BK > K) -> stage buffer `st`, also by LDS-DMA:
   // chunks entirely before K load as usual, chunks at or past K are pointed out
@@ -393,8 +430,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
     const uint32_t sb = smem_base + (uint32_t)st * STAGE_BYTES;
     const int valid = K - (k0 + 16 * dma_chunk);
     // range_w / range_x bound every block's cut range from above
-    const uint32_t off_w = valid >= 16 ? lane_off + (uint32_t)k0 : range_w;
-    const uint32_t off_x = valid >= 16 ? lane_off + (uint32_t)k0 : range_x;
+    const uint32_t off_w = valid >= 16 ? laneff + (uint32_t)k0 : range_w;
+    const uint32_t off_x = valid >= 16 ? laneff + (uint32_t)k0 : range_x;
 #pragma unroll
     for (int t = 0; t < DPW; ++t) dma16(rs[t], sb + (uint32_t)(t * NWAVES + wave) * 1024u, t < W_DPW ? off_w : off_x, 0u);
   };
@@ -409,8 +446,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
     if (valid > 0 && valid < 16) {
 #pragma unroll
       for (int t = 0; t < DPW; ++t) {
-        const uint4 v = K >= 16 ? load16_tail(rs[t], lane_off + (uint32_t)k0, valid)
-                                : load16_partial(rs[t], lane_off + (uint32_t)k0, valid);
+        const uint4 v = K >= 16 ? load16_tail(rs[t], laneff + (uint32_t)k0, valid)
+                                : load16_partial(rs[t], laneff + (uint32_t)k0, valid);
         *(uint4 *)(sb + (t * NWAVES + wave) * 1024 + lane * 16) = v;
       }
     }
@@ -590,7 +627,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   }  // PP
 
   static_assert(2 * BM * BN <= STAGES * STAGE_BYTES, "the bf16 tile fits in the stage buffers");
-  main_epilogue<BM, BN, WM, WN>(acc, a, smem, (const float *)(smem + STAGES * STAGE_BYTES), m0, n0, wave, lane);
+  main_epilogue<BM, BN, WM, WN>(acc, a, smem, (const float *)(smem + STAGES * STAGE_BYTES), m0, n0, wave, lane,
+                                (int)threadIdx.x);
 }
 
 // ------------------------------------------------- main path, five LDS slots
@@ -612,7 +650,21 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
 // no wave waits long for the instruction queue.  The epilogue's
 // scales no longer fit in LDS during the K loop: thread t < 256 keeps
 // scale[n0 + t] in a register and writes it to LDS after the loop.
-template <bool KTAIL>
+// Stream-K work split (variant 16).  Units are (tile, K step) pairs numbered
+// tile * nk + step over the stream-K tiles only; stream-K workgroup i takes the
+// units [sk_start(i), sk_start(i + 1)).
+// The host keeps every unit number below 2^31.
+__device__ __forceinline__ int sk_start(int i, int units, int n_sk) { return (int)((int64_t)i * units / n_sk); }
+// The stream-K workgroup whose range holds unit u (the largest i with sk_start(i) <= u).
+__device__ __forceinline__ int sk_owner(int u, int units, int n_sk) {
+  return (int)(((int64_t)(u + 1) * n_sk - 1) / units);
+}
+// Bytes of one partial tile: 512 threads x 128 fp32 accumulators, stored in
+// register order (thread t's float4 q at (q * 512 + t) * 16), since only the
+// same thread of another workgroup of this kernel reads it back.
+constexpr uint32_t kPartialBytes = (uint32_t)kMainPartialBytes;
+
+template <bool KTAIL, bool SK>
 __global__ __launch_bounds__(512, 1) void fp8g_main5_kernel(MainArgs a) {
   constexpr int BM = 256, BN = 256, BK = 128, WM = 4, WN = 2, NWAVES = 8;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
@@ -622,178 +674,309 @@ __global__ __launch_bounds__(512, 1) void fp8g_main5_kernel(MainArgs a) {
   constexpr int NMFMA = FN * FM, NREAD = (FN + FM) * 2;  // per wave per 64-byte sub-step
   static_assert(HDPW == 4 && NMFMA == 8, "x DMAs are spread two per sub-step, after MFMAs 1 and 5");
   static_assert(2 * BM * BN + BN * 4 <= 5 * SLOT, "epilogue tile and scales fit");
+  static_assert(FN * FM * 16 == 128 && NWAVES * 64 * 128 * 4 == (int)kPartialBytes, "partial tile layout");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * SLOT];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave_m = wave % WM, wave_n = wave / WM;
-  int tm, tn;
-  tile_coords(a, tm, tn);
   const int K = a.K;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
-  const uint32_t range_x = (uint32_t)rows_x * (uint32_t)K, range_w = (uint32_t)rows_w * (uint32_t)K;
-  const int g = lane >> 5, lr = lane & 31;
   const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
-
-  // The epilogue's scale for column n0 + tid (zero past N); the load is the
-  // oldest vector-memory operation, so every DMA wait below also covers it.
-  float my_scale = 0.0f;
-  if (tid < BN) my_scale = llvm_buffer_load_f32(make_rsrc(a.scale + n0, (uint32_t)(a.N - n0) * 4u), (uint32_t)tid * 4u, 0, 0);
-
-  // DMA instruction t (0..3) of a wave fills 1 KiB block t*8 + wave of a half
-  // step: 8 rows of 128 bytes, lane l taking row l / 8 and logical chunk
-  // (l % 8) ^ swz(row); descriptor t starts at the block's first row (rows past
-  // M / N read zero).
-  const int dma_lrow = wave * ROWS_PER_KB + lane / CH;
-  const int dma_chunk = (lane % CH) ^ swz<BK>(dma_lrow);
-  const uint32_t lane_off = (uint32_t)dma_lrow * (uint32_t)K + (uint32_t)dma_chunk * 16u;
-  const uint32_t blk_stride = (uint32_t)(NWAVES * ROWS_PER_KB) * (uint32_t)K;
-  v4i rw[HDPW], rx[HDPW];
-#pragma unroll
-  for (int t = 0; t < HDPW; ++t) {
-    const uint32_t skip = (uint32_t)t * blk_stride;
-    rw[t] = make_rsrc(a.w + (size_t)n0 * K + skip, range_w > skip ? range_w - skip : 0u);
-    rx[t] = make_rsrc(a.x + (size_t)m0 * K + skip, range_x > skip ? range_x - skip : 0u);
-  }
+  const int total = a.tiles_m * a.tiles_n;
   const int nk_full = K / BK;
-  const int nk = nk_full + (KTAIL ? 1 : 0);
+  const int nk = nk_full + (KTAIL ? 1 : 0);  // K steps of a tile
   auto slot_w = [&](int k) __attribute__((always_inline)) { return (uint32_t)((k & 1) * SLOT); };
   auto slot_x = [&](int k) __attribute__((always_inline)) { return (uint32_t)((2 + k % 3) * SLOT); };
 
-  // DMA instruction t of step kt's w (or x) half; the tail step points chunks
-  // at or past K out of range (zeros) and fix_tail rebuilds the straddling one.
-  auto dma_half = [&](const v4i &rs, uint32_t range, uint32_t slot, int kt, int t) __attribute__((always_inline)) {
-    const uint32_t lds = smem_base + slot + (uint32_t)(t * NWAVES + wave) * 1024u;
-    if (kt < nk_full) {
-      dma16(rs, lds, lane_off, (uint32_t)kt * BK);
-    } else if (KTAIL && kt == nk_full) {
-      const int valid = K - (kt * BK + 16 * dma_chunk);
-      dma16(rs, lds, valid >= 16 ? lane_off + (uint32_t)(kt * BK) : range, 0u);
-    }
-  };
-  auto issue_w = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t = 0; t < HDPW; ++t) dma_half(rw[t], range_w, slot_w(kt), kt, t);
-  };
-  auto issue_x = [&](int kt, int t) __attribute__((always_inline)) { dma_half(rx[t], range_x, slot_x(kt), kt, t); };
-  auto fix_tail = [&](int kt) __attribute__((always_inline)) {
-    const int k0 = kt * BK;
-    const int valid = K - (k0 + 16 * dma_chunk);
-    if (valid > 0 && valid < 16) {
-#pragma unroll
-      for (int t = 0; t < 2 * HDPW; ++t) {  // w blocks, then x blocks, one at a time (runs once)
-        const v4i &rs = t < HDPW ? rw[t % HDPW] : rx[t % HDPW];
-        const uint4 v = K >= 16 ? load16_tail(rs, lane_off + (uint32_t)k0, valid)
-                                : load16_partial(rs, lane_off + (uint32_t)k0, valid);
-        const uint32_t slot = t < HDPW ? slot_w(kt) : slot_x(kt);
-        *(uint4 *)(smem + slot + ((t % HDPW) * NWAVES + wave) * 1024 + lane * 16) = v;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  // Fragment reads: lane l reads row (l % 32) of each 32-row block, chunks
-  // 4j + 2(l/32) + {0,1} of 64-byte sub-step j; blocks in first-use order.
-  const int aw_row = wave_n * TN + lr, bx_row = wave_m * TM + lr;
-  const int sa = swz<BK>(aw_row), sbx = swz<BK>(bx_row);
-  v8i fa[2][FN], fb[2][FM];
-  auto read_one = [&](int k, int j, int q, v8i (&af)[FN], v8i (&bf)[FM]) __attribute__((always_inline)) {
-    const int ord = q / 2, half = q % 2;
-    const int blk = ord == 0 ? 0 : (ord <= FM ? FN + ord - 1 : ord - FM);
-    const int c = 4 * j + 2 * g + half;
-    if (blk < FN) {
-      const uint8_t *row = smem + slot_w(k) + (aw_row + 32 * blk) * BK;
-      const uint4 v = *(const uint4 *)(row + ((c ^ sa) << 4));
-      af[blk][4 * half + 0] = (int)v.x; af[blk][4 * half + 1] = (int)v.y;
-      af[blk][4 * half + 2] = (int)v.z; af[blk][4 * half + 3] = (int)v.w;
-    } else {
-      const uint8_t *row = smem + slot_x(k) + (bx_row + 32 * (blk - FN)) * BK;
-      const uint4 v = *(const uint4 *)(row + ((c ^ sbx) << 4));
-      bf[blk - FN][4 * half + 0] = (int)v.x; bf[blk - FN][4 * half + 1] = (int)v.y;
-      bf[blk - FN][4 * half + 2] = (int)v.z; bf[blk - FN][4 * half + 3] = (int)v.w;
-    }
-  };
-
-  v16f acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // Prologue: w(0), x(0), x(1), w(1), x(2) -- the steady-state issue order --
-  // then wait for step 0 (what was issued after x(0) may stay in flight).
-  issue_w(0);
-#pragma unroll
-  for (int t = 0; t < HDPW; ++t) issue_x(0, t);
-#pragma unroll
-  for (int t = 0; t < HDPW; ++t) issue_x(1, t);
-  issue_w(1);
-#pragma unroll
-  for (int t = 0; t < HDPW; ++t) issue_x(2, t);
-  if (nk >= 3) vm_wait<3 * HDPW>();
-  else if (nk == 2) vm_wait<2 * HDPW>();
-  else vm_wait<0>();
-  if (KTAIL && nk_full == 0) fix_tail(0);  // K < 128: everything issued has landed
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < NREAD; ++q) read_one(0, 0, q, fa[0], fb[0]);
-
-  // Sub-step u = 2s + j of step s.  j = 1 is the boundary: wait for this wave's
-  // DMA of w(s+1) and x(s+1), barrier
-  // (publishes step s+1, retires step s's slots), then, spread over the MFMAs,
-  // w(s+2) into the slot of w(s) and the first half of x(s+3) into the slot of
-  // x(s); sub-step 2s+2 issues the second half of x(s+3).
-  const int nsub = 2 * nk;
-  auto substep = [&](const int u, const int cur) __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-    const int s = u >> 1, j = u & 1;
-    if (j == 1) {
-      // This wave's last DMA of w(s+1) came after MFMA 6 of sub-step 2s-1;
-      // after it only x(s+2) instructions 1 (after MFMA 7), 2 and 3 (sub-step
-      // 2s) were issued, so at most 3 may stay in flight.  (At s = 0 the
-      // prologue issued all of x(2) after w(1): waiting for 3 is stricter.)
-      if (s + 2 < nk) vm_wait<HDPW - 1>();
-      else vm_wait<0>();
-      if (KTAIL && s + 1 == nk_full) fix_tail(s + 1);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const int xk = j == 1 ? s + 3 : s + 2;  // x step whose DMAs this sub-step spreads
-    const int xt = j == 1 ? 0 : 2;          // ... instructions xt and xt + 1
-    const bool xdma = j == 1 || s >= 1;
-    const bool more = u + 1 < nsub;
-    const int un = u + 1;
-#pragma unroll
-    for (int q = 0; q < NMFMA; ++q) {
-      const int i = q / FM, jm = q % FM;
-      acc[i][jm] = mfma32(fa[cur][i], fb[cur][jm], acc[i][jm]);
-      if (more) {
-#pragma unroll
-        for (int r = q * NREAD / NMFMA; r < (q + 1) * NREAD / NMFMA; ++r)
-          read_one(un >> 1, un & 1, r, fa[cur ^ 1], fb[cur ^ 1]);
-      }
-      // w(s+2) after MFMAs 0, 2, 4, 6 of the boundary sub-step, x after MFMAs 3
-      // and 7 (measured best among the placements tried: a burst of DMA
-      // instructions right after the barrier stalls the issuing waves)
-      if (j == 1 && (q & 1) == 0) dma_half(rw[q >> 1], range_w, slot_w(s + 2), s + 2, q >> 1);
-      if ((q == 3 || q == 7) && xdma) issue_x(xk, xt + (q == 7 ? 1 : 0));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  for (int s = 0; s < nk; ++s) {
-    substep(2 * s, 0);
-    substep(2 * s + 1, 1);
+  // This workgroup's units [u0, u1), unit = tile * nk + K step with tiles in
+  // raster order: one whole tile, or (stream-K) a contiguous range that may
+  // cover the end of one tile, whole tiles, and the start of another.
+  // Without stream-K only the tile is used (u0 = tile, one segment of nk
+  // steps); with it the host keeps all unit numbers below 2^31.
+  int u0, u1;
+  int sk_i = 0;
+  if (!SK || (int)blockIdx.x < a.n_dp) {
+    const int t = xcd_remap(blockIdx.x, SK ? a.n_dp : total);
+    u0 = SK ? t * nk : t;
+    u1 = SK ? u0 + nk : t + 1;
+  } else {
+    // consecutive ranges share a tile, so keep them on one XCD
+    sk_i = xcd_remap(blockIdx.x - a.n_dp, a.n_sk);
+    const int units = (total - a.n_dp) * nk;
+    u0 = a.n_dp * nk + sk_start(sk_i, units, a.n_sk);
+    u1 = a.n_dp * nk + sk_start(sk_i + 1, units, a.n_sk);
   }
 
-  // Scales into LDS (past the bf16 tile), published by the epilogue's first barrier.
-  float *s_lds = (float *)(smem + 2 * BM * BN);
-  __syncthreads();  // every wave is done with the slots
-  if (tid < BN) s_lds[tid] = my_scale;
-  main_epilogue<BM, BN, WM, WN>(acc, a, smem, s_lds, m0, n0, wave, lane);
+  for (int u = u0; u < u1;) {
+    // Segment: steps [kb, ke) of one tile.
+    const int tile = SK ? u / nk : u0;
+    const int kb = SK ? u - tile * nk : 0;
+    const int ke = SK ? min(nk, kb + (u1 - u)) : nk;
+    const bool first_seg = u == u0;
+    u += SK ? ke - kb : 1;
+    if (SK && !first_seg) {
+      // the previous segment's last LDS reads (epilogue or ticket flag) and
+      // stores are done before this one's DMAs refill the slots
+      vm_wait<0>();
+      __syncthreads();
+    }
+    const int nkl = ke - kb;  // steps of this segment; local step s is K step kb + s
+
+    // Thread ids.  With stream-K they pass through an empty asm, so the
+    // compiler cannot see through them and computes what derives from them
+    // (DMA offsets, LDS fragment addresses, epilogue addresses) in each
+    // segment instead of hoisting it out of the segment loop and keeping it
+    // live -- spilled -- across every K loop.
+    int tid = threadIdx.x;
+    int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if constexpr (SK) {
+      asm volatile("" : "+v"(tid));
+      asm volatile("" : "+s"(wave));
+    }
+    const int lane = tid & 63;
+    const int wave_m = wave % WM, wave_n = wave / WM;
+    const int g = lane >> 5, lr = lane & 31;
+
+    // DMA instruction t (0..3) of a wave fills 1 KiB block t*8 + wave of a half
+    // step: 8 rows of 128 bytes, lane l taking row l / 8 and logical chunk
+    // (l % 8) ^ swz(row); descriptor t starts at the block's first row (rows past
+    // M / N read zero).
+    const int dma_lrow = wave * ROWS_PER_KB + lane / CH;
+    const int dma_chunk = (lane % CH) ^ swz<BK>(dma_lrow);
+    const uint32_t laneff = (uint32_t)dma_lrow * (uint32_t)K + (uint32_t)dma_chunk * 16u;
+    const uint32_t blk_stride = (uint32_t)(NWAVES * ROWS_PER_KB) * (uint32_t)K;
+    // Fragment reads: lane l reads row (l % 32) of each 32-row block, chunks
+    // 4j + 2(l/32) + {0,1} of 64-byte sub-step j; blocks in first-use order.
+    const int aw_row = wave_n * TN + lr, bx_row = wave_m * TM + lr;
+    const int sa = swz<BK>(aw_row), sbx = swz<BK>(bx_row);
+    int tm, tn;
+    raster(a, tile, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
+    const uint32_t range_x = (uint32_t)rows_x * (uint32_t)K, range_w = (uint32_t)rows_w * (uint32_t)K;
+
+    // The epilogue's scale for column n0 + tid (zero past N); the load is the
+    // oldest vector-memory operation, so every DMA wait below also covers it.
+    float my_scale = 0.0f;
+    if (tid < BN)
+      my_scale = llvm_buffer_load_f32(make_rsrc(a.scale + n0, (uint32_t)(a.N - n0) * 4u), (uint32_t)tid * 4u, 0, 0);
+
+    v4i rw[HDPW], rx[HDPW];
+#pragma unroll
+    for (int t = 0; t < HDPW; ++t) {
+      const uint32_t skip = (uint32_t)t * blk_stride;
+      rw[t] = make_rsrc(a.w + (size_t)n0 * K + skip, range_w > skip ? range_w - skip : 0u);
+      rx[t] = make_rsrc(a.x + (size_t)m0 * K + skip, range_x > skip ? range_x - skip : 0u);
+    }
+
+    // DMA instruction t of local step kt's w (or x) half; nothing past the
+    // segment is fetched.  The tile's tail step points chunks at or past K out
+    // of range (zeros) and fix_tail rebuilds the straddling one.
+    auto dma_half = [&](const v4i &rs, uint32_t range, uint32_t slot, int kt, int t) __attribute__((always_inline)) {
+      const uint32_t lds = smem_base + slot + (uint32_t)(t * NWAVES + wave) * 1024u;
+      if (kt < nkl) {
+        const int kg = kb + kt;
+        if (!KTAIL || kg < nk_full) {
+          dma16(rs, lds, laneff, (uint32_t)kg * BK);
+        } else {
+          const int valid = K - (kg * BK + 16 * dma_chunk);
+          dma16(rs, lds, valid >= 16 ? laneff + (uint32_t)(kg * BK) : range, 0u);
+        }
+      }
+    };
+    auto issue_w = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < HDPW; ++t) dma_half(rw[t], range_w, slot_w(kt), kt, t);
+    };
+    auto issue_x = [&](int kt, int t) __attribute__((always_inline)) { dma_half(rx[t], range_x, slot_x(kt), kt, t); };
+    auto fix_tail = [&](int kt) __attribute__((always_inline)) {
+      const int k0 = (kb + kt) * BK;
+      const int valid = K - (k0 + 16 * dma_chunk);
+      if (valid > 0 && valid < 16) {
+#pragma unroll
+        for (int t = 0; t < 2 * HDPW; ++t) {  // w blocks, then x blocks, one at a time (runs once)
+          const v4i &rs = t < HDPW ? rw[t % HDPW] : rx[t % HDPW];
+          const uint4 v = K >= 16 ? load16_tail(rs, laneff + (uint32_t)k0, valid)
+                                  : load16_partial(rs, laneff + (uint32_t)k0, valid);
+          const uint32_t slot = t < HDPW ? slot_w(kt) : slot_x(kt);
+          *(uint4 *)(smem + slot + ((t % HDPW) * NWAVES + wave) * 1024 + lane * 16) = v;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+
+    v8i fa[2][FN], fb[2][FM];
+    auto read_one = [&](int k, int j, int q, v8i (&af)[FN], v8i (&bf)[FM]) __attribute__((always_inline)) {
+      const int ord = q / 2, half = q % 2;
+      const int blk = ord == 0 ? 0 : (ord <= FM ? FN + ord - 1 : ord - FM);
+      const int c = 4 * j + 2 * g + half;
+      if (blk < FN) {
+        const uint8_t *row = smem + slot_w(k) + (aw_row + 32 * blk) * BK;
+        const uint4 v = *(const uint4 *)(row + ((c ^ sa) << 4));
+        af[blk][4 * half + 0] = (int)v.x; af[blk][4 * half + 1] = (int)v.y;
+        af[blk][4 * half + 2] = (int)v.z; af[blk][4 * half + 3] = (int)v.w;
+      } else {
+        const uint8_t *row = smem + slot_x(k) + (bx_row + 32 * (blk - FN)) * BK;
+        const uint4 v = *(const uint4 *)(row + ((c ^ sbx) << 4));
+        bf[blk - FN][4 * half + 0] = (int)v.x; bf[blk - FN][4 * half + 1] = (int)v.y;
+        bf[blk - FN][4 * half + 2] = (int)v.z; bf[blk - FN][4 * half + 3] = (int)v.w;
+      }
+    };
+
+    v16f acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // Prologue: w(0), x(0), x(1), w(1), x(2) -- the steady-state issue order --
+    // then wait for step 0 (what was issued after x(0) may stay in flight).
+    issue_w(0);
+#pragma unroll
+    for (int t = 0; t < HDPW; ++t) issue_x(0, t);
+#pragma unroll
+    for (int t = 0; t < HDPW; ++t) issue_x(1, t);
+    issue_w(1);
+#pragma unroll
+    for (int t = 0; t < HDPW; ++t) issue_x(2, t);
+    if (nkl >= 3) vm_wait<3 * HDPW>();
+    else if (nkl == 2) vm_wait<2 * HDPW>();
+    else vm_wait<0>();
+    if (KTAIL && kb == nk_full) fix_tail(0);  // the segment is the tail step alone: everything issued has landed
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NREAD; ++q) read_one(0, 0, q, fa[0], fb[0]);
+
+    // Sub-step u = 2s + j of local step s.  j = 1 is the boundary: wait for
+    // this wave's DMA of w(s+1) and x(s+1), barrier (publishes step s+1, retires
+    // step s's slots), then, spread over the MFMAs, w(s+2) into the slot of w(s)
+    // and the first half of x(s+3) into the slot of x(s); sub-step 2s+2 issues
+    // the second half of x(s+3).
+    const int nsub = 2 * nkl;
+    auto substep = [&](const int us, const int cur) __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int s = us >> 1, j = us & 1;
+      if (j == 1) {
+        // This wave's last DMA of w(s+1) came after MFMA 6 of sub-step 2s-1;
+        // after it only x(s+2) instructions 1 (after MFMA 7), 2 and 3 (sub-step
+        // 2s) were issued, so at most 3 may stay in flight.  (At s = 0 the
+        // prologue issued all of x(2) after w(1): waiting for 3 is stricter.)
+        if (s + 2 < nkl) vm_wait<HDPW - 1>();
+        else vm_wait<0>();
+        if (KTAIL && kb + s + 1 == nk_full) fix_tail(s + 1);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int xk = j == 1 ? s + 3 : s + 2;  // x step whose DMAs this sub-step spreads
+      const int xt = j == 1 ? 0 : 2;          // ... instructions xt and xt + 1
+      const bool xdma = j == 1 || s >= 1;
+      const bool more = us + 1 < nsub;
+      const int un = us + 1;
+#pragma unroll
+      for (int q = 0; q < NMFMA; ++q) {
+        const int i = q / FM, jm = q % FM;
+        acc[i][jm] = mfma32(fa[cur][i], fb[cur][jm], acc[i][jm]);
+        if (more) {
+#pragma unroll
+          for (int r = q * NREAD / NMFMA; r < (q + 1) * NREAD / NMFMA; ++r)
+            read_one(un >> 1, un & 1, r, fa[cur ^ 1], fb[cur ^ 1]);
+        }
+        // w(s+2) after MFMAs 0, 2, 4, 6 of the boundary sub-step, x after MFMAs 3
+        // and 7 (measured best among the placements tried: a burst of DMA
+        // instructions right after the barrier stalls the issuing waves)
+        if (j == 1 && (q & 1) == 0) dma_half(rw[q >> 1], range_w, slot_w(s + 2), s + 2, q >> 1);
+        if ((q == 3 || q == 7) && xdma) issue_x(xk, xt + (q == 7 ? 1 : 0));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int s = 0; s < nkl; ++s) {
+      substep(2 * s, 0);
+      substep(2 * s + 1, 1);
+    }
+
+    if constexpr (SK) {
+      if (kb != 0 || ke != nk) {
+        // Part of a tile.  Contributors are the stream-K workgroups c0 .. c1
+        // whose ranges meet the tile, in K order.  Each stores its partial sums
+        // (slot 2i if the segment opens the workgroup's range, else 2i+1: a
+        // range holds at most one opening and one closing partial segment),
+        // and the last to take the tile's ticket adds them all.
+        const int tt = tile - a.n_dp;
+        const int units = (total - a.n_dp) * nk;
+        const int tu0 = tt * nk;
+        const int c0 = sk_owner(tu0, units, a.n_sk), c1 = sk_owner(tu0 + nk - 1, units, a.n_sk);
+        auto slot_of = [&](int i) __attribute__((always_inline)) {
+          return (uint32_t)(2 * i + (sk_start(i, units, a.n_sk) >= tu0 ? 0 : 1)) * kPartialBytes;
+        };
+        const v4i rsrc_p = make_rsrc(a.P, (uint32_t)a.n_sk * 2u * kPartialBytes);
+        // Thread t's float4 q of a partial tile sits at slot + q * 8 KiB + t * 16:
+        // the per-thread part is the one VGPR offset, the rest goes in the
+        // (uniform) scalar offset, so no address registers live across the loop.
+        const uint32_t toff = (uint32_t)tid * 16u;
+        auto own4 = [&](int q) __attribute__((always_inline)) {
+          const int i = q / (4 * FM), jm = (q / 4) % FM, e = 4 * (q % 4);
+          return v4f{acc[i][jm][e], acc[i][jm][e + 1], acc[i][jm][e + 2], acc[i][jm][e + 3]};
+        };
+        {
+          const uint32_t mine = slot_of(sk_i);
+#pragma unroll
+          for (int q = 0; q < 32; ++q)
+            llvm_buffer_store_v4f32(own4(q), rsrc_p, toff, mine + (uint32_t)q * 8192u, kDeviceScope);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+        __syncthreads();  // all partial stores acknowledged; every wave is done with the slots
+        int *flag = (int *)smem;
+        if (tid == 0) *flag = take_ticket(a.tickets + (size_t)tt * kTicketStride, a.epoch, c1 - c0 + 1);
+        __syncthreads();
+        const bool last = *flag != 0;
+        if (!last) continue;
+        asm volatile("" : : : "memory");
+        // acc = P[c0] + P[c0+1] + ... + P[c1], added in that order whoever
+        // finishes (the own part comes from registers), so the result does
+        // not depend on arrival order.  Four float4 per thread at a time.
+#pragma unroll
+        for (int q0 = 0; q0 < 32; q0 += 4) {
+          __builtin_amdgcn_sched_barrier(0);
+          v4f t[4];
+          if (c0 == sk_i) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) t[jj] = own4(q0 + jj);
+          } else {
+            const uint32_t base = slot_of(c0);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              t[jj] = llvm_buffer_load_v4f32(rsrc_p, toff, base + (uint32_t)(q0 + jj) * 8192u, kDeviceScope);
+          }
+          for (int c = c0 + 1; c <= c1; ++c) {
+            if (c == sk_i) {
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) t[jj] += own4(q0 + jj);
+            } else {
+              const uint32_t base = slot_of(c);
+              v4f v[4];
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj)
+                v[jj] = llvm_buffer_load_v4f32(rsrc_p, toff, base + (uint32_t)(q0 + jj) * 8192u, kDeviceScope);
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) t[jj] += v[jj];
+            }
+          }
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int q = q0 + jj, i = q / (4 * FM), jm = (q / 4) % FM, e = 4 * (q % 4);
+            acc[i][jm][e] = t[jj].x; acc[i][jm][e + 1] = t[jj].y;
+            acc[i][jm][e + 2] = t[jj].z; acc[i][jm][e + 3] = t[jj].w;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+
+    // Scales into LDS (past the bf16 tile), published by the epilogue's first barrier.
+    float *s_lds = (float *)(smem + 2 * BM * BN);
+    __syncthreads();  // every wave is done with the slots (and the ticket flag)
+    if (tid < BN) s_lds[tid] = my_scale;
+    main_epilogue<BM, BN, WM, WN>(acc, a, smem, s_lds, m0, n0, wave, lane, tid);
+  }
 }
 
 // ---------------------------------------------------------------- skinny path
@@ -826,7 +1009,7 @@ struct SkinnyArgs {
   uint16_t *y;
   float *P;                  // fp32 partials [column tile][S][M][16*RB] (S > 1)
   unsigned long long *tickets;  // one per column tile, kTicketStride apart (S > 1), any initial value
-  unsigned long long epoch;  // this call's id (< 2^56), unique among calls that share tickets
+  unsigned long long epoch;  // this call's id (< 2^48)
   int M, N, K;
   int k_slice;
   int vec;  // y rows allow 8-byte stores / P rows 16-byte stores (N % 4 == 0)
@@ -871,49 +1054,29 @@ __device__ __forceinline__ v4f mfma16(const v8i &a, const v8i &b, const v4f &c) 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// Cache policy of the split-K partials and their readers: device scope (SC1),
-// the encoding the compiler gives agent-scope atomic loads and stores.  Stores
-// write through the XCD's L2 to the device coherence point and loads do not hit
-// stale lines, so the partials pass between XCDs without flushing or
-// invalidating whole caches.
-constexpr int kDeviceScope = 16;
-
 // Split-K with S > 1 slices, in the same launch.  Every workgroup of a column
 // tile has stored its unscaled fp32 partials (tile-major: the tile's S slices
 // of M x 16*RB floats are contiguous); the last of the tile's S workgroups to
 // finish adds them in slice order s = 0, 1, ..., S-1, scales, rounds to bf16 and
 // writes y, so the result does not depend on the order the workgroups ran in.
-// "Last" is decided on a 64-bit ticket per tile holding (call id << 8 | count):
-// a ticket left by another call restarts at count 1, so nothing is zeroed
-// before the launch.  Ordering: each wave waits until its device-scope partial
-// stores are acknowledged, the workgroup meets at a barrier, and only then does
-// one thread take the ticket; the last workgroup reads with device scope after
-// its ticket.  No L2 write-back or invalidate is needed for these accesses.
+// "Last" is decided on the tile's ticket (take_ticket).  Ordering: each wave
+// waits until its device-scope partial stores are acknowledged, the workgroup
+// meets at a barrier, and only then does one thread take the ticket; the last
+// workgroup reads with device scope after its ticket.  No L2 write-back or
+// invalidate is needed for these accesses.
 template <int RB>
 __device__ __forceinline__ void splitk_finish(const SkinnyArgs &a, int n0, int *flag) {
   constexpr int R = 16 * RB;
   const int S = (int)gridDim.y;
   asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
   __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned long long *t = a.tickets + (size_t)blockIdx.x * kTicketStride;
-    unsigned long long old = __hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned long long want;
-    for (;;) {
-      want = (old >> 8) == a.epoch ? old + 1 : (a.epoch << 8) | 1ull;
-      if (__hip_atomic_compare_exchange_strong(t, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT))
-        break;
-    }
-    *flag = (int)(want & 0xFFull) == S;
-  }
+  if (threadIdx.x == 0) *flag = take_ticket(a.tickets + (size_t)blockIdx.x * kTicketStride, a.epoch, S);
   __syncthreads();
   if (!*flag) return;
   asm volatile("" : : : "memory");
   const v4i rsrc_p = make_rsrc(a.P + (size_t)blockIdx.x * S * a.M * R, (uint32_t)(S * a.M * R) * 4u);
   const uint32_t slice_bytes = (uint32_t)(a.M * R) * 4u;
   constexpr int q4 = R / 4;  // four-column groups in the tile
-  constexpr uint32_t kOut = 0x80000000u;  // past the descriptor's range: reads 0
   // Each thread sums IT items (four columns of one row), IT * SB loads in flight
   // at a time; loads that fall past S or past the items read zero and are unused.
   constexpr int IT = 2, SB = 8;
@@ -1272,6 +1435,9 @@ static const MainConfig kMainConfigs[] = {
     {7, 256, 256, 128, 2}, // 8 waves, wave tile 128 (m) x 64 (n), 128-byte K steps
     {9, 256, 256, 64, 4},  // 8 waves in two ping-pong groups, wave tile 64 (m) x 128 (n)
     {10, 256, 256, 128, 2}, // 8 waves, five half-step LDS slots (x two steps ahead)
+    {16, 256, 256, 128, 2}, // variant 10 with stream-K over the tiles past the full waves
+    {17, 128, 256, 128, 3}, // 8 waves, wave tile 64 x 64: grids of 128 x 256 tiles (mid M)
+    {18, 128, 128, 128, 4}, // 8 waves, wave tile 64 (m) x 32 (n): grids of 128 x 128 tiles (mid M)
 };
 // ids 1-5: LDS-ring kernel, 11-15: direct-to-register kernel; 16 * row_blocks w rows per workgroup
 static const SkinnyConfig kSkinnyConfigs[] = {
@@ -1306,9 +1472,22 @@ static hipError_t launch_main_cfg(const MainLaunch &l, hipStream_t stream) {
 
 static hipError_t launch_main5(const MainLaunch &l, hipStream_t stream) {
   MainArgs a{l.x, l.w, l.scale, l.y, l.M, l.N, l.K, l.tiles_m, l.tiles_n, l.group_m, l.ystore};
-  const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(512);
-  if (l.k_tail) fp8g_main5_kernel<true><<<grid, block, 0, stream>>>(a);
-  else fp8g_main5_kernel<false><<<grid, block, 0, stream>>>(a);
+  const bool sk = l.variant == 16;
+  if (sk) {
+    a.n_dp = l.n_dp;
+    a.n_sk = l.n_sk;
+    a.P = l.partials;
+    a.tickets = l.tickets;
+    a.epoch = l.epoch;
+  }
+  const dim3 grid((unsigned)(sk ? l.n_dp + l.n_sk : l.tiles_m * l.tiles_n)), block(512);
+  if (sk) {
+    if (l.k_tail) fp8g_main5_kernel<true, true><<<grid, block, 0, stream>>>(a);
+    else fp8g_main5_kernel<false, true><<<grid, block, 0, stream>>>(a);
+  } else {
+    if (l.k_tail) fp8g_main5_kernel<true, false><<<grid, block, 0, stream>>>(a);
+    else fp8g_main5_kernel<false, false><<<grid, block, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -1323,6 +1502,9 @@ hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
     case 7: return launch_main_cfg<256, 256, 128, 2, 2, 4>(l, stream);
     case 9: return launch_main_cfg<256, 256, 64, 4, 4, 2, true>(l, stream);
     case 10: return launch_main5(l, stream);
+    case 16: return launch_main5(l, stream);
+    case 17: return launch_main_cfg<128, 256, 128, 3, 2, 4>(l, stream);
+    case 18: return launch_main_cfg<128, 128, 128, 4, 2, 4>(l, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -81,7 +81,12 @@ typedef struct fp8g_plan {
     int32_t k_tail;         /* 1 if K is not a multiple of the K step */
     int64_t grid;           /* workgroups of the first kernel */
     int64_t workspace_bytes;/* per-tile tickets + fp32 partials the call
-                               allocates (split_k > 1) */
+                               allocates (split-K with split_k > 1, or
+                               stream-K) */
+    int32_t dp_tiles;       /* main path: tiles computed whole, one workgroup
+                               each (all tiles unless stream-K) */
+    int32_t sk_groups;      /* main path variant 16: stream-K workgroups that
+                               share the remaining tiles; 0 otherwise */
 } fp8g_plan;
 
 /* y = bf16_rne((x . w^T) * scale), as defined above.
@@ -102,8 +107,16 @@ int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y,
 /* Same operation with parts of the plan forced, for tests and tuning.  Each
  * override is 0 for "let the planner choose":
  *   path    : FP8G_PATH_MAIN or FP8G_PATH_SPLITK (SPLITK needs M <= 64)
- *   variant : a configuration id valid for the path (see fp8_gemm_plan_ex)
- *   split_k : 1..64 K slices (splitk path only)
+ *   variant : a configuration id valid for the path (fp8_gemm_plan_ex reports
+ *             the tile it implies).  Main path: 10 = 256x256 tiles, five LDS
+ *             slots (the large-grid default); 17 = 128x256 and 18 = 128x128
+ *             (mid M); 3 = 64x64 (small problems); 2 = 128x128 four waves;
+ *             1, 4-7, 9 = other 256x256 schedules; 16 = variant 10 with
+ *             stream-K (opt-in).  Split-K path: 1-5 = 16*v w rows per
+ *             workgroup through an LDS ring (default kernel), 11-15 = the
+ *             same row counts loading straight into registers (K >= 16).
+ *   split_k : splitk path: 1..64 K slices; main path variant 16: 1..2048
+ *             stream-K workgroups; other main variants: 0 or 1
  * Invalid overrides give FP8G_ERR_INVALID_ARG.  The result is the same
  * operation to within fp32 summation order. */
 int fp8_gemm_scaled_ex(const void *x, const void *w, const float *scale, void *y,

@@ -32,10 +32,52 @@ MAIN_SHAPES = [(300, 520, 4127), (257, 129, 200), (128, 128, 128), (65, 70, 33),
                (70, 300, 1), (40, 33, 17), (256, 256, 257), (300, 300, 384)]
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 9, 10])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 9, 10, 16, 17, 18])
 @pytest.mark.parametrize("shape", MAIN_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_main_variants_full(variant, shape):
     _full_case(*shape, path=fg.PATH_MAIN, variant=variant)
+
+
+# ------------------------------------------- main path, stream-K (variant 16) --
+# Forced stream-K workgroup counts on small grids: ranges that end inside a
+# tile, ranges that cover several tiles, tiles with one to many contributors,
+# a K tail that falls into a partial segment, one workgroup per unit.
+@pytest.mark.parametrize("shape,groups", [
+    ((300, 300, 384), [1, 2, 3, 5, 7, 12]),      # 4 tiles x 3 steps
+    ((256, 256, 257), [1, 2, 3]),                # 1 tile: 2 steps + the tail
+    ((513, 520, 1000), [5, 16, 40, 72]),         # 9 tiles x 8 steps (last one a tail)
+    ((70, 300, 1), [1, 2]),                      # K below one chunk: one step per tile
+    ((600, 700, 2050), [3, 11, 50, 100]),        # 9 tiles x 17 steps, 2-byte tail
+])
+def test_stream_k_forced_groups(shape, groups):
+    M, N, K = shape
+    x, w, s = synth.fp8_inputs(M, N, K, seed=5)
+    ref = oracle.gemm_scaled(x, w, s)
+    for g in groups:
+        plan = fg.fp8_gemm_plan_ex(M, N, K, path=fg.PATH_MAIN, variant=16, split_k=g)
+        assert plan["sk_groups"] == g and plan["dp_tiles"] == 0
+        say(f"stream-K {shape} groups={g}")
+        compare(run(x, w, s, path=fg.PATH_MAIN, variant=16, split_k=g), ref, f"{shape} groups={g}")
+
+
+def test_stream_k_whole_waves_and_remainder():
+    """528 tiles: the first full wave is computed one tile per workgroup, the
+    last full wave and the 16 remaining tiles by 256 stream-K workgroups."""
+    M, N, K = 4096, 8448, 384
+    plan = fg.fp8_gemm_plan_ex(M, N, K, path=fg.PATH_MAIN, variant=16)
+    assert plan["dp_tiles"] == 256 and plan["sk_groups"] == 256 and plan["grid"] == 512
+    x, w, s = synth.fp8_inputs(M, N, K, seed=6)
+    say(f"stream-K {M}x{N}x{K} plan {plan}")
+    compare(run(x, w, s, path=fg.PATH_MAIN, variant=16), oracle.gemm_scaled(x, w, s), "dp + stream-K")
+
+
+def test_stream_k_deterministic():
+    """Partial sums are added in K order whichever workgroup finishes a tile."""
+    M, N, K = 513, 520, 4000
+    x, w, s = synth.fp8_inputs(M, N, K, seed=8)
+    say("stream-K determinism")
+    ys = [run(x, w, s, path=fg.PATH_MAIN, variant=16, split_k=100) for _ in range(4)]
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
 
 
 # ------------------------------------------- split-K path, forced splits ------
