@@ -365,3 +365,227 @@ ALL_CHECKS = [
     check_scale_linearity,
     check_nan_propagates,
 ]
+
+
+# ======================================================================
+# General formats and the bias / activation epilogue.
+#
+# These checks take an implementation with three more methods
+#
+#     decode5(codes uint8[...])                       -> float64  E5M2 -> value
+#     act(z float64[...], act int)                    -> float64  activation
+#     epi(x, w, scale, bias|None, act, x_fmt, w_fmt)  -> uint16   y as bf16 bits
+#
+# Expected values come from torch's float8_e5m2 / float8_e4m3fn conversions,
+# numpy's float16 (an E5M2 code is the top byte of an fp16), exact Fraction
+# sums with IEEE rules for the special values written out here, torch's
+# float64 activation functions, and closed forms.
+FMT_E4M3, FMT_E5M2 = 0, 1
+ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_TANH = 0, 1, 2, 3
+
+
+def torch_decode5(codes) -> np.ndarray:
+    """Library decode: torch's float8_e5m2 -> float64 conversion."""
+    c = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return c.view(torch.float8_e5m2).to(torch.float64).numpy()
+
+
+def _decode_fmt(codes, fmt):
+    return torch_decode(codes) if fmt == FMT_E4M3 else torch_decode5(codes)
+
+
+def torch_act(z, act):
+    t = torch.from_numpy(np.ascontiguousarray(z, dtype=np.float64))
+    if act == ACT_RELU:
+        t = torch.nn.functional.relu(t)
+    elif act == ACT_SILU:
+        t = torch.nn.functional.silu(t)
+    elif act == ACT_GELU_TANH:
+        t = torch.nn.functional.gelu(t, approximate="tanh")
+    return t.numpy()
+
+
+def exact_epilogue(x, w, scale, bias, act, xf, wf):
+    """y bits from exact Fraction sums of library-decoded values (finite z only
+    goes through torch's activation; the special-value rules are IEEE's)."""
+    dx, dw = _decode_fmt(x, xf), _decode_fmt(w, wf)
+    M, K = dx.shape
+    N = dw.shape[0]
+    out = np.empty((M, N), np.uint16)
+    for m in range(M):
+        for n in range(N):
+            tot, nan, pinf, ninf = Fraction(0), False, False, False
+            for k in range(K):
+                a, b = float(dx[m, k]), float(dw[n, k])
+                if np.isnan(a) or np.isnan(b):
+                    nan = True
+                elif np.isinf(a) or np.isinf(b):
+                    if a == 0.0 or b == 0.0:
+                        nan = True
+                    elif (a < 0) != (b < 0):
+                        ninf = True
+                    else:
+                        pinf = True
+                else:
+                    tot += Fraction(a) * Fraction(b)
+            if nan or (pinf and ninf):
+                acc = float("nan")
+            elif pinf or ninf:
+                acc = float("inf") if pinf else float("-inf")
+            else:
+                acc = float(tot)  # correctly rounded
+            z = acc * float(scale[n]) + (float(bias[n]) if bias is not None else 0.0)
+            if np.isfinite(z):
+                v = float(torch_act(np.array([z]), act)[0])
+            else:
+                v = z
+                if np.isinf(z) and act != ACT_NONE and z < 0:
+                    v = 0.0 if act == ACT_RELU else -0.0
+            out[m, n] = 0x7FC0 if np.isnan(v) else exact_bf16_bits(v)
+    return out
+
+
+def check_e5m2_decode_vs_fp16_and_torch(impl):
+    codes = np.arange(256, dtype=np.uint8)
+    got = impl.decode5(codes)
+    half = (codes.astype(np.uint16) << 8).view(np.float16).astype(np.float64)
+    lib = torch_decode5(codes)
+    for ref in (half, lib):
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
+        ok = ~np.isnan(ref)
+        assert np.array_equal(got[ok], ref[ok])
+        assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def check_e5m2_spot_values(impl):
+    # OCP E5M2: bias 15, 2 mantissa bits, exponent 31 = inf / NaN
+    cases = {0x3C: 1.0, 0x7B: 57344.0, 0x01: 2.0 ** -16, 0x04: 2.0 ** -14, 0x03: 0.75 * 2.0 ** -14,
+             0x3D: 1.25, 0xC0: -2.0, 0x7C: float("inf"), 0xFC: float("-inf"), 0x00: 0.0}
+    got = impl.decode5(np.array(list(cases), np.uint8))
+    assert np.array_equal(got, np.array(list(cases.values())))
+    nan = impl.decode5(np.array([0x7D, 0x7E, 0x7F, 0xFD, 0xFF], np.uint8))
+    assert np.all(np.isnan(nan))
+    assert np.signbit(impl.decode5(np.array([0x80], np.uint8))[0])
+
+
+def check_epi_e4m3_plain_is_the_scaled_definition(impl, seed=21):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(0, 256, (5, 37), dtype=np.uint8)
+    w = rng.integers(0, 256, (6, 37), dtype=np.uint8)
+    s = rng.uniform(0.001, 3.0, 6).astype(np.float32)
+    got = impl.epi(x, w, s, None, ACT_NONE, FMT_E4M3, FMT_E4M3)
+    assert np.array_equal(got, exact_epilogue(x, w, s, None, ACT_NONE, FMT_E4M3, FMT_E4M3))
+
+
+def check_epi_vs_exact_all_formats_and_acts(impl, seed=22):
+    rng = np.random.default_rng(seed)
+    for xf in (FMT_E4M3, FMT_E5M2):
+        for wf in (FMT_E4M3, FMT_E5M2):
+            for act in (ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_TANH):
+                M, N, K = 3, 4, int(rng.integers(1, 12))
+                x = rng.integers(0, 256, (M, K), dtype=np.uint8)
+                w = rng.integers(0, 256, (N, K), dtype=np.uint8)
+                s = rng.uniform(-2.0, 2.0, N).astype(np.float32)
+                b = rng.uniform(-4.0, 4.0, N).astype(np.float32)
+                got = impl.epi(x, w, s, b, act, xf, wf)
+                ref = exact_epilogue(x, w, s, b, act, xf, wf)
+                assert np.array_equal(got, ref), (xf, wf, act)
+
+
+def check_epi_small_values_through_every_act(impl, seed=23):
+    """Sums near the activations' interesting range (|z| < 8), all formats."""
+    rng = np.random.default_rng(seed)
+    small4 = np.array([c for c in range(256) if abs(float(torch_decode(np.array([c], np.uint8))[0])) <= 1.0],
+                      np.uint8)
+    small5 = np.array([c for c in range(256)
+                       if abs(float(torch_decode5(np.array([c], np.uint8))[0])) <= 1.0], np.uint8)
+    for act in (ACT_RELU, ACT_SILU, ACT_GELU_TANH):
+        for xf, wf in ((FMT_E4M3, FMT_E5M2), (FMT_E5M2, FMT_E5M2)):
+            px = small4 if xf == FMT_E4M3 else small5
+            pw = small4 if wf == FMT_E4M3 else small5
+            x = rng.choice(px, (4, 9))
+            w = rng.choice(pw, (5, 9))
+            s = rng.uniform(0.5, 1.5, 5).astype(np.float32)
+            b = rng.uniform(-2.0, 2.0, 5).astype(np.float32)
+            assert np.array_equal(impl.epi(x, w, s, b, act, xf, wf), exact_epilogue(x, w, s, b, act, xf, wf))
+
+
+def check_epi_exact_cancellation_e5m2(impl):
+    # 57344^2 + 2^-32 - 57344^2 = 2^-32 exactly; scaled by 2^32 it is 1.0.  A
+    # plain fp64 running sum loses the middle term (0x0000 instead of 0x3F80).
+    x = np.array([[0x7B, 0x01, 0xFB]], np.uint8)
+    w = np.array([[0x7B, 0x01, 0x7B]], np.uint8)
+    got = impl.epi(x, w, np.array([2.0 ** 32], np.float32), None, ACT_NONE, FMT_E5M2, FMT_E5M2)
+    assert int(got[0, 0]) == 0x3F80
+
+
+def check_epi_special_values(impl):
+    one5, two5, zero, inf5, ninf5, nan5 = 0x3C, 0x40, 0x00, 0x7C, 0xFC, 0x7E
+    s1 = np.ones(1, np.float32)
+
+    def y(xs, ws, act=ACT_NONE, xf=FMT_E5M2, wf=FMT_E5M2, bias=None):
+        return int(impl.epi(np.array([xs], np.uint8), np.array([ws], np.uint8), s1, bias, act, xf, wf)[0, 0])
+
+    assert y([inf5], [zero]) == 0x7FC0                      # inf * 0
+    assert y([inf5, ninf5], [one5, one5]) == 0x7FC0         # inf - inf
+    assert y([inf5, one5], [two5, one5]) == 0x7F80          # inf * 2 + 1
+    assert y([ninf5], [two5]) == 0xFF80
+    assert y([nan5], [zero]) == 0x7FC0
+    assert y([ninf5], [one5], ACT_RELU) == 0x0000           # relu(-inf) = 0
+    assert y([ninf5], [one5], ACT_SILU) == 0x8000           # limit -0
+    assert y([ninf5], [one5], ACT_GELU_TANH) == 0x8000
+    assert y([inf5], [one5], ACT_GELU_TANH) == 0x7F80
+    assert y([inf5], [one5], ACT_SILU) == 0x7F80
+    # an E4M3 NaN operand against an E5M2 zero
+    assert y([0x7F], [zero], xf=FMT_E4M3) == 0x7FC0
+
+
+def check_epi_order_of_scale_bias_act(impl):
+    x = np.array([[0x40]], np.uint8)    # E4M3 2.0
+    w = np.array([[0x3C]], np.uint8)    # E4M3 1.5  -> acc = 3
+    # scale before bias: 3 * 2 + 1 = 7 (bias first would give 8)
+    got = impl.epi(x, w, np.array([2.0], np.float32), np.array([1.0], np.float32), ACT_NONE, FMT_E4M3, FMT_E4M3)
+    assert int(got[0, 0]) == exact_bf16_bits(7.0)
+    # activation last: relu(-3 * 1 + 5) = 2 (relu first would give 5)
+    xn = np.array([[0xC0]], np.uint8)   # E4M3 -2.0 -> acc = -3
+    got = impl.epi(xn, w, np.array([1.0], np.float32), np.array([5.0], np.float32), ACT_RELU, FMT_E4M3, FMT_E4M3)
+    assert int(got[0, 0]) == exact_bf16_bits(2.0)
+
+
+def check_epi_bias_per_column(impl):
+    x = np.zeros((3, 4), np.uint8)
+    w = np.zeros((5, 4), np.uint8)
+    b = np.array([1.0, -2.0, 3.5, 0.25, -0.125], np.float32)
+    got = impl.epi(x, w, np.ones(5, np.float32), b, ACT_NONE, FMT_E5M2, FMT_E4M3)
+    ref = np.array([[exact_bf16_bits(float(v)) for v in b]] * 3, np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def check_act_closed_forms(impl):
+    import math
+    z = np.array([0.0, math.log(3.0), -math.log(3.0), 1.0, -1.0, 40.0, -40.0])
+    silu = impl.act(z, ACT_SILU)
+    # sigma(ln 3) = 3/4, sigma(-ln 3) = 1/4
+    ref = [0.0, 0.75 * math.log(3.0), -0.25 * math.log(3.0), 1 / (1 + math.exp(-1)),
+           -1 / (1 + math.exp(1)), 40.0, -40.0 * math.exp(-40.0)]
+    assert np.allclose(silu, ref, rtol=1e-14, atol=0)
+    relu = impl.act(z, ACT_RELU)
+    assert np.array_equal(relu, np.maximum(z, 0.0))
+    gelu = impl.act(np.array([0.0, 1.0, 40.0]), ACT_GELU_TANH)
+    c = math.sqrt(2.0 / math.pi)
+    assert np.allclose(gelu, [0.0, 0.5 * (1 + math.tanh(c * 1.044715)), 40.0], rtol=1e-14, atol=0)
+    assert np.array_equal(impl.act(z, ACT_NONE), z)
+
+
+EPI_CHECKS = [
+    check_e5m2_decode_vs_fp16_and_torch,
+    check_e5m2_spot_values,
+    check_epi_e4m3_plain_is_the_scaled_definition,
+    check_epi_vs_exact_all_formats_and_acts,
+    check_epi_small_values_through_every_act,
+    check_epi_exact_cancellation_e5m2,
+    check_epi_special_values,
+    check_epi_order_of_scale_bias_act,
+    check_epi_bias_per_column,
+    check_act_closed_forms,
+]

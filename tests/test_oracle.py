@@ -28,6 +28,34 @@ def test_oracle_pin(check):
     check(COracle())
 
 
+class COracleEpilogue:
+    """The C oracle's general-format and epilogue entry points."""
+
+    decode5 = staticmethod(oracle.e5m2_to_double)
+    act = staticmethod(oracle.activation)
+
+    @staticmethod
+    def epi(x, w, scale, bias, act, xf, wf):
+        return oracle.gemm_epilogue(x, w, scale, bias, act, xf, wf)
+
+
+@pytest.mark.parametrize("check", pins.EPI_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_epilogue_pin(check):
+    check(COracleEpilogue())
+
+
+def test_epilogue_sampled_positions_match_full():
+    rng = np.random.default_rng(9)
+    x = rng.integers(0, 256, (29, 300), dtype=np.uint8)
+    w = rng.integers(0, 256, (31, 300), dtype=np.uint8)
+    s = rng.uniform(0.01, 1.0, 31).astype(np.float32)
+    b = rng.uniform(-1, 1, 31).astype(np.float32)
+    y = oracle.gemm_epilogue(x, w, s, b, oracle.ACT_SILU, oracle.FMT_E5M2, oracle.FMT_E4M3)
+    mi, ni = synth.sample_positions(29, 31, 300, seed=10)
+    at = oracle.gemm_epilogue_at(x, w, s, mi, ni, b, oracle.ACT_SILU, oracle.FMT_E5M2, oracle.FMT_E4M3)
+    assert np.array_equal(at, y[mi, ni])
+
+
 def test_sampled_positions_match_full():
     x, w, s = synth.fp8_inputs(37, 53, 300, seed=3)
     y = oracle.gemm_scaled(x, w, s)

@@ -182,3 +182,180 @@ def test_unmutated_numpy_oracle_passes_all_pins():
 def test_each_planted_mistake_is_caught(mutant):
     failed = _failing_pins(mutant())
     assert failed, f"no pin caught the planted mistake {mutant.__name__}"
+
+
+
+# ------------------------------------------------ general formats and epilogue
+def _decode5_ok(codes):
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    s, e, m = c >> 7, (c >> 2) & 31, c & 3
+    mag = np.where(e == 0, np.ldexp(m.astype(np.float64), -16),
+                   np.ldexp((4 + m).astype(np.float64), (e - 17).astype(np.int64)))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def _act_ok(z, act):
+    z = np.asarray(z, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        if act == pins.ACT_RELU:
+            out = np.where(z > 0, z, 0.0)
+        elif act == pins.ACT_SILU:
+            out = z / (1.0 + np.exp(-z))
+        elif act == pins.ACT_GELU_TANH:
+            out = 0.5 * z * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (z + 0.044715 * z ** 3)))
+        else:
+            out = z.copy()
+    lim = np.where(z > 0, z, -0.0 if act in (pins.ACT_SILU, pins.ACT_GELU_TANH) else 0.0)
+    out = np.where(np.isinf(z) & (act != pins.ACT_NONE), lim, out)
+    return np.where(np.isnan(z), z, out)
+
+
+class NumpyEpilogue:
+    """Unmutated reference shape for the epilogue mutants (must pass all pins)."""
+
+    def decode5(self, codes):
+        return _decode5_ok(codes)
+
+    def act(self, z, act):
+        return _act_ok(z, act)
+
+    def decode_fmt(self, codes, fmt):
+        return _decode_ok(codes) if fmt == pins.FMT_E4M3 else self.decode5(codes)
+
+    def dot(self, a, b):
+        """Exact sum of products with IEEE special-value rules (Fractions)."""
+        from fractions import Fraction
+        tot, nan, pinf, ninf = Fraction(0), False, False, False
+        for p, q in zip(a, b):
+            p, q = float(p), float(q)
+            if np.isnan(p) or np.isnan(q):
+                nan = True
+            elif np.isinf(p) or np.isinf(q):
+                if p == 0 or q == 0:
+                    nan = True
+                elif (p < 0) != (q < 0):
+                    ninf = True
+                else:
+                    pinf = True
+            else:
+                tot += Fraction(p) * Fraction(q)
+        if nan or (pinf and ninf):
+            return float("nan")
+        if pinf or ninf:
+            return float("inf") if pinf else float("-inf")
+        return float(tot)
+
+    def z(self, acc, scale, bias, n):
+        return acc * float(scale[n]) + (float(bias[n]) if bias is not None else 0.0)
+
+    def epi(self, x, w, scale, bias, act, xf, wf):
+        dx, dw = self.decode_fmt(x, xf), self.decode_fmt(w, wf)
+        M, N = dx.shape[0], dw.shape[0]
+        z = np.array([[self.z(self.dot(dx[m], dw[n]), scale, bias, n) for n in range(N)] for m in range(M)],
+                     np.float64).reshape(M, N)
+        return _bf16_rne_ok(self.act(z, act))
+
+
+class E5m2Bias16(NumpyEpilogue):
+    def decode5(self, codes):
+        return _decode5_ok(codes) / 2.0
+
+
+class E5m2InfIsFinite(NumpyEpilogue):
+    def decode5(self, codes):
+        d = _decode5_ok(codes)
+        return np.where(np.isinf(d), np.sign(d) * 65536.0, d)
+
+
+class NaiveFp64Sum(NumpyEpilogue):
+    def dot(self, a, b):
+        s = 0.0
+        for p, q in zip(a, b):
+            s += float(p) * float(q)
+        return s
+
+
+class InfTimesZeroIsZero(NumpyEpilogue):
+    def dot(self, a, b):
+        a = np.where(np.isinf(a) & (np.asarray(b) == 0), 0.0, a)
+        b = np.where(np.isinf(b) & (np.asarray(a) == 0), 0.0, b)
+        return super().dot(a, b)
+
+
+class BiasBeforeScale(NumpyEpilogue):
+    def z(self, acc, scale, bias, n):
+        return (acc + (float(bias[n]) if bias is not None else 0.0)) * float(scale[n])
+
+
+class BiasByRow(NumpyEpilogue):
+    def epi(self, x, w, scale, bias, act, xf, wf):
+        if bias is None:
+            return super().epi(x, w, scale, bias, act, xf, wf)
+        M = np.asarray(x).shape[0]
+        rows = np.array([float(bias[m % len(bias)]) for m in range(M)], np.float32)
+        out = np.empty((M, np.asarray(w).shape[0]), np.uint16)
+        for m in range(M):
+            out[m] = super().epi(x[m:m + 1], w, scale, np.full(len(bias), rows[m], np.float32), act, xf, wf)[0]
+        return out
+
+
+class ActBeforeScale(NumpyEpilogue):
+    def epi(self, x, w, scale, bias, act, xf, wf):
+        dx, dw = self.decode_fmt(x, xf), self.decode_fmt(w, wf)
+        M, N = dx.shape[0], dw.shape[0]
+        acc = np.array([[self.dot(dx[m], dw[n]) for n in range(N)] for m in range(M)], np.float64).reshape(M, N)
+        a = self.act(acc, act) * np.asarray(scale, np.float64)[None, :]
+        if bias is not None:
+            a = a + np.asarray(bias, np.float64)[None, :]
+        return _bf16_rne_ok(a)
+
+
+class SiluIsSigmoid(NumpyEpilogue):
+    def act(self, z, act):
+        if act == pins.ACT_SILU:
+            z = np.asarray(z, np.float64)
+            with np.errstate(over="ignore"):
+                return np.where(np.isnan(z), z, 1.0 / (1.0 + np.exp(-z)))
+        return super().act(z, act)
+
+
+class GeluErf(NumpyEpilogue):
+    def act(self, z, act):
+        if act == pins.ACT_GELU_TANH:
+            from math import erf, sqrt
+            z = np.asarray(z, np.float64)
+            return np.array([v if not np.isfinite(v) else 0.5 * v * (1 + erf(v / sqrt(2))) for v in z.ravel()]
+                            ).reshape(z.shape)
+        return super().act(z, act)
+
+
+class ReluKeepsNegative(NumpyEpilogue):
+    def act(self, z, act):
+        if act == pins.ACT_RELU:
+            return np.asarray(z, np.float64).copy()
+        return super().act(z, act)
+
+
+EPI_MUTANTS = [E5m2Bias16, E5m2InfIsFinite, NaiveFp64Sum, InfTimesZeroIsZero, BiasBeforeScale, BiasByRow,
+               ActBeforeScale, SiluIsSigmoid, GeluErf, ReluKeepsNegative]
+
+
+def _failing_epi_pins(impl):
+    failed = []
+    for check in pins.EPI_CHECKS:
+        try:
+            check(impl)
+        except AssertionError:
+            failed.append(check.__name__)
+    return failed
+
+
+def test_unmutated_numpy_epilogue_passes_all_pins():
+    assert _failing_epi_pins(NumpyEpilogue()) == []
+
+
+@pytest.mark.parametrize("mutant", EPI_MUTANTS, ids=lambda m: m.__name__)
+def test_each_planted_epilogue_mistake_is_caught(mutant):
+    failed = _failing_epi_pins(mutant())
+    assert failed, f"no pin caught the planted mistake {mutant.__name__}"
