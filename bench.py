@@ -51,14 +51,21 @@ def bound_of(wl) -> str:
     return "mfma" if wl.flops / (PEAK_FP8_TFLOPS * 1e12) >= wl.bytes / (PEAK_HBM_GBPS * 1e9) else "hbm"
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "fp8_gemm_channel_amd", "csrc", "fp8g_kernels.hip")
+# Sources of the dominant kernel (the five-slot main kernel): its templates and
+# the unit that instantiates it.  A traffic summary taken on other sources is
+# not used.
+KERNEL_SOURCES = [os.path.join(ROOT, "fp8_gemm_channel_amd", "csrc", f)
+                  for f in ("fp8g_kernels.hpp", "fp8g_launch_main5.hip")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_main5_kernel_square-8192_traffic.md")
 
 
 def kernel_source_hash() -> str:
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):

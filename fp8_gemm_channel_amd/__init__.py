@@ -10,10 +10,15 @@ fallback implementation.
 Entry points (same names as the C ABI):
     fp8_gemm_scaled(x, w, scale, y, M, N, K, stream)        raw pointers
     fp8_gemm_scaled_ex(..., path, variant, split_k, stream)  forced plan
+    fp8_gemm_scaled_act(x, w, scale, bias, y, M, N, K, x_format, w_format,
+                        activation, stream)                   bias, activation, E5M2
+    fp8_gemm_scaled_act_ex(..., path, variant, split_k, stream)
     fp8_gemm_plan(M, N, K) / fp8_gemm_plan_ex(...)           host-only planner
     fp8_gemm_strerror(status), fp8_gemm_last_error()
 and the tensor-level convenience wrapper
-    fp8_gemm(x, w, scale, *, out=None, path=0, variant=0, split_k=0) -> y
+    fp8_gemm(x, w, scale, *, bias=None, act=ACT_NONE, out=None, path=0,
+             variant=0, split_k=0) -> y
+(operand formats follow the tensors' dtypes: float8_e4m3fn or float8_e5m2).
 """
 from __future__ import annotations
 
@@ -31,9 +36,12 @@ FP8G_ERR_HIP = 3
 PATH_NONE, PATH_ZERO, PATH_MAIN, PATH_SPLITK = 0, 1, 2, 3
 PATH_NAMES = {PATH_NONE: "none", PATH_ZERO: "zero", PATH_MAIN: "main", PATH_SPLITK: "splitk"}
 
+FMT_E4M3, FMT_E5M2 = 0, 1
+ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_TANH = 0, 1, 2, 3
+
 #: Every symbol include/fp8g.h declares.
-EXPORTED_SYMBOLS = ("fp8_gemm_scaled", "fp8_gemm_scaled_ex", "fp8_gemm_plan", "fp8_gemm_plan_ex",
-                    "fp8_gemm_strerror", "fp8_gemm_last_error")
+EXPORTED_SYMBOLS = ("fp8_gemm_scaled", "fp8_gemm_scaled_ex", "fp8_gemm_scaled_act", "fp8_gemm_scaled_act_ex",
+                    "fp8_gemm_plan", "fp8_gemm_plan_ex", "fp8_gemm_strerror", "fp8_gemm_last_error")
 
 
 class Plan(ctypes.Structure):
@@ -72,6 +80,10 @@ def _load() -> ctypes.CDLL:
     lib.fp8_gemm_scaled.restype = ctypes.c_int
     lib.fp8_gemm_scaled_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
     lib.fp8_gemm_scaled_ex.restype = ctypes.c_int
+    lib.fp8_gemm_scaled_act.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    lib.fp8_gemm_scaled_act.restype = ctypes.c_int
+    lib.fp8_gemm_scaled_act_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp]
+    lib.fp8_gemm_scaled_act_ex.restype = ctypes.c_int
     lib.fp8_gemm_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
     lib.fp8_gemm_plan.restype = ctypes.c_int
     lib.fp8_gemm_plan_ex.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(Plan)]
@@ -97,6 +109,20 @@ def fp8_gemm_scaled_ex(x: int, w: int, scale: int, y: int, M: int, N: int, K: in
     return _lib.fp8_gemm_scaled_ex(x, w, scale, y, M, N, K, path, variant, split_k, stream)
 
 
+def fp8_gemm_scaled_act(x: int, w: int, scale: int, bias: int, y: int, M: int, N: int, K: int,
+                        x_format: int = FMT_E4M3, w_format: int = FMT_E4M3, activation: int = ACT_NONE,
+                        stream: int = 0) -> int:
+    """C entry point with a bias (0 = none), an activation and operand formats."""
+    return _lib.fp8_gemm_scaled_act(x, w, scale, bias or None, y, M, N, K, x_format, w_format, activation, stream)
+
+
+def fp8_gemm_scaled_act_ex(x: int, w: int, scale: int, bias: int, y: int, M: int, N: int, K: int,
+                           x_format: int = FMT_E4M3, w_format: int = FMT_E4M3, activation: int = ACT_NONE,
+                           path: int = 0, variant: int = 0, split_k: int = 0, stream: int = 0) -> int:
+    return _lib.fp8_gemm_scaled_act_ex(x, w, scale, bias or None, y, M, N, K, x_format, w_format, activation,
+                                       path, variant, split_k, stream)
+
+
 def fp8_gemm_plan(M: int, N: int, K: int) -> dict:
     return fp8_gemm_plan_ex(M, N, K)
 
@@ -118,23 +144,33 @@ def fp8_gemm_last_error() -> str:
 
 
 # ------------------------------------------------------------- tensor wrapper --
-def fp8_gemm(x, w, scale, *, out=None, path: int = 0, variant: int = 0, split_k: int = 0, stream=None):
-    """y = bf16((x @ w^T) * scale) on the GPU; returns a new [M, N] bfloat16 tensor
-    (or writes `out`).  x: [M,K], w: [N,K] float8_e4m3fn (or uint8 codes);
-    scale: [N] float32; all contiguous on the same CUDA/HIP device."""
+def fp8_gemm(x, w, scale, *, bias=None, act: int = ACT_NONE, x_format=None, w_format=None, out=None,
+             path: int = 0, variant: int = 0, split_k: int = 0, stream=None):
+    """y = bf16(act((x @ w^T) * scale + bias)) on the GPU; returns a new [M, N]
+    bfloat16 tensor (or writes `out`).  x: [M,K], w: [N,K] float8_e4m3fn or
+    float8_e5m2 (or uint8 codes, E4M3 unless x_format / w_format say E5M2);
+    scale, bias: [N] float32; all contiguous on the same CUDA/HIP device."""
     import torch
 
-    def codes(t, name):
-        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
-            raise TypeError(f"{name} must be float8_e4m3fn (or uint8 E4M3 codes), got {t.dtype}")
+    def codes(t, name, fmt):
+        if t.dtype == torch.float8_e5m2:
+            dfmt = FMT_E5M2
+        elif t.dtype in (torch.float8_e4m3fn, torch.uint8):
+            dfmt = FMT_E4M3
+        else:
+            raise TypeError(f"{name} must be float8_e4m3fn, float8_e5m2 or uint8 codes, got {t.dtype}")
+        if fmt is None:
+            fmt = dfmt
+        elif t.dtype != torch.uint8 and fmt != dfmt:
+            raise TypeError(f"{name}: format {fmt} does not match dtype {t.dtype}")
         if t.dim() != 2 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous 2-d tensor")
         if not t.is_cuda:
             raise ValueError(f"{name} must be on the GPU")
-        return t
+        return t, fmt
 
-    x = codes(x, "x")
-    w = codes(w, "w")
+    x, x_format = codes(x, "x", x_format)
+    w, w_format = codes(w, "w", w_format)
     if scale.dtype != torch.float32 or scale.dim() != 1 or not scale.is_contiguous() or not scale.is_cuda:
         raise TypeError("scale must be a contiguous 1-d float32 GPU tensor")
     M, K = x.shape
@@ -143,6 +179,10 @@ def fp8_gemm(x, w, scale, *, out=None, path: int = 0, variant: int = 0, split_k:
         raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w {tuple(w.shape)}, scale {tuple(scale.shape)}")
     if not (x.device == w.device == scale.device):
         raise ValueError("x, w and scale must be on the same device")
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.shape != scale.shape or not bias.is_contiguous() \
+                or bias.device != scale.device:
+            raise TypeError("bias must be a contiguous [N] float32 tensor on the same device")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
@@ -150,8 +190,10 @@ def fp8_gemm(x, w, scale, *, out=None, path: int = 0, variant: int = 0, split_k:
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     with torch.cuda.device(x.device):
-        st = _lib.fp8_gemm_scaled_ex(x.data_ptr(), w.data_ptr(), scale.data_ptr(), out.data_ptr(),
-                                     M, N, K, path, variant, split_k, stream.cuda_stream)
+        st = _lib.fp8_gemm_scaled_act_ex(x.data_ptr(), w.data_ptr(), scale.data_ptr(),
+                                         bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                                         M, N, K, x_format, w_format, act, path, variant, split_k,
+                                         stream.cuda_stream)
     if st != FP8G_OK:
         raise Fp8gError(st, fp8_gemm_last_error())
     return out

@@ -14,32 +14,60 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libfp8g.so")
-SOURCES = [os.path.join(CSRC, "fp8g_api.cpp"), os.path.join(CSRC, "fp8g_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "fp8g_api.cpp"), os.path.join(CSRC, "fp8g_kernels.hip")] + sorted(
+    os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.startswith("fp8g_launch_") and f.endswith(".hip"))
 
 # Packed-fp32 VALU instructions are kept out of every device build.
-HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
+# Known-harmless diagnostics: the host pass does not know the packed-fp32
+# feature, and m0 is clobbered on purpose by the LDS-DMA asm.
+_NOISE = ("packed-fp32-ops", "clobber list contains reserved registers: m0",
+          "Reserved registers on the clobber list", "warnings generated", "asm volatile(",
+          "^", "| ")
 
-def build(verbose: bool = False) -> str:
+
+def _filter(text: str) -> str:
+    return "\n".join(l for l in text.splitlines()
+                     if not any(n in l for n in _NOISE) and not l.strip().startswith(("9", "|")))
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every translation unit (in parallel) and link libfp8g.so in-tree."""
+    from concurrent.futures import ThreadPoolExecutor
+
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIBRARY + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    # Known-harmless diagnostics: the host pass does not know the packed-fp32
-    # feature, and m0 is clobbered on purpose by the LDS-DMA asm.
-    noise = ("packed-fp32-ops", "clobber list contains reserved registers: m0",
-             "Reserved registers on the clobber list", "warnings generated", "asm volatile(",
-             "^", "| ")
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                    if not any(n in l for n in noise) and not l.strip().startswith(("9", "|")))
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIBRARY)
+    tag = ".tmp%d" % os.getpid()
+    objs = [os.path.join(CSRC, os.path.basename(src) + tag + ".o") for src in SOURCES]
+
+    def compile_one(pair):
+        src, obj = pair
+        cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return subprocess.run(cmd, capture_output=True, text=True)
+
+    jobs = jobs or min(len(SOURCES), int(os.environ.get("MAX_JOBS", "0") or 0) or os.cpu_count() or 1)
+    tmp = LIBRARY + tag
+    try:
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            results = list(pool.map(compile_one, zip(SOURCES, objs)))
+        for src, res in zip(SOURCES, results):
+            out = _filter(res.stdout + res.stderr)
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n" + out)
+            if verbose and out.strip():
+                print(out)
+        link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        res = subprocess.run(link, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n" + _filter(res.stdout + res.stderr))
+        os.replace(tmp, LIBRARY)
+    finally:
+        for f in objs + [tmp]:
+            if os.path.exists(f):
+                os.remove(f)
     return LIBRARY
 
 

@@ -236,21 +236,39 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
-int run(const void *x, const void *w, const float *scale, void *y, int64_t M, int64_t N, int64_t K, int32_t path,
-        int32_t variant, int32_t split_k, void *stream_ptr) {
+// Configurations built for every operand format: main variants 3, 10, 17,
+// 18 (all the planner picks) and the LDS-ring split-K kernel.
+bool supports_formats(const fp8g_plan &p) {
+  if (p.path == FP8G_PATH_MAIN) return p.variant == 3 || p.variant == 10 || p.variant == 17 || p.variant == 18;
+  if (p.path == FP8G_PATH_SPLITK) return p.variant <= 5;
+  return true;
+}
+
+int run(const void *x, const void *w, const float *scale, const float *bias, void *y, int64_t M, int64_t N,
+        int64_t K, int32_t x_format, int32_t w_format, int32_t act, int32_t path, int32_t variant, int32_t split_k,
+        void *stream_ptr) {
   g_last_error.clear();
+  if ((x_format != FP8G_FMT_E4M3 && x_format != FP8G_FMT_E5M2) ||
+      (w_format != FP8G_FMT_E4M3 && w_format != FP8G_FMT_E5M2))
+    return fail(FP8G_ERR_INVALID_ARG, "unknown operand format (x_format=%d w_format=%d)", x_format, w_format);
+  if (act < FP8G_ACT_NONE || act > FP8G_ACT_GELU_TANH) return fail(FP8G_ERR_INVALID_ARG, "unknown activation %d", act);
+  const int fmt = (w_format << 1) | x_format;
   fp8g_plan p;
   int st = plan_impl(M, N, K, path, variant, split_k, &p);
   if (st) return st;
+  if (fmt != 0 && !supports_formats(p))
+    return fail(FP8G_ERR_INVALID_ARG, "%s variant %d is built for E4M3 operands only", p.path == FP8G_PATH_MAIN ? "main" : "split-K",
+                p.variant);
   if (p.path == FP8G_PATH_NONE) return FP8G_OK;
   if (!y) return fail(FP8G_ERR_INVALID_ARG, "y is null");
   if (!scale) return fail(FP8G_ERR_INVALID_ARG, "scale is null");
   if (K > 0 && (!x || !w)) return fail(FP8G_ERR_INVALID_ARG, "x or w is null");
   if ((uintptr_t)scale % 4) return fail(FP8G_ERR_INVALID_ARG, "scale is not 4-byte aligned");
   if ((uintptr_t)y % 2) return fail(FP8G_ERR_INVALID_ARG, "y is not 2-byte aligned");
+  if ((uintptr_t)bias % 4) return fail(FP8G_ERR_INVALID_ARG, "bias is not 4-byte aligned");
   const size_t ybytes = (size_t)M * (size_t)N * 2;
   if (overlaps(y, ybytes, x, (size_t)M * (size_t)K) || overlaps(y, ybytes, w, (size_t)N * (size_t)K) ||
-      overlaps(y, ybytes, scale, (size_t)N * 4))
+      overlaps(y, ybytes, scale, (size_t)N * 4) || overlaps(y, ybytes, bias, (size_t)N * 4))
     return fail(FP8G_ERR_INVALID_ARG, "y overlaps an input");
 
   hipStream_t stream = (hipStream_t)stream_ptr;
@@ -260,13 +278,18 @@ int run(const void *x, const void *w, const float *scale, void *y, int64_t M, in
 
   const bool vec = (N % 4 == 0) && ((uintptr_t)y % 8 == 0);
   if (p.path == FP8G_PATH_ZERO) {
-    e = fp8g::launch_zero((uint16_t *)y, M * N, stream);
-    return e == hipSuccess ? FP8G_OK : hip_fail(e, "zero-fill launch");
+    // K = 0: the empty sum is +0; with a bias or an activation y = act(bias)
+    if (bias || act != FP8G_ACT_NONE) e = fp8g::launch_empty_k((uint16_t *)y, bias, act, M, N, stream);
+    else e = fp8g::launch_zero((uint16_t *)y, M * N, stream);
+    return e == hipSuccess ? FP8G_OK : hip_fail(e, "K = 0 launch");
   }
   if (p.path == FP8G_PATH_MAIN) {
     const int ystore = (N % 8 == 0 && (uintptr_t)y % 16 == 0) ? 16 : vec ? 8 : 2;
     fp8g::MainLaunch l{(const uint8_t *)x, (const uint8_t *)w, scale, (uint16_t *)y, (int)M, (int)N, (int)K,
                        (int)cdiv(M, p.tile_m), (int)cdiv(N, p.tile_n), p.group_m, p.variant, p.k_tail != 0, ystore};
+    l.bias = bias;
+    l.act = act;
+    l.fmt = fmt;
     void *ws = nullptr;
     if (p.sk_groups > 0) {
       // tickets for the stream-K tiles, then two partial tiles per stream-K
@@ -303,6 +326,9 @@ int run(const void *x, const void *w, const float *scale, void *y, int64_t M, in
   const unsigned long long epoch = call_id();
   fp8g::SkinnyLaunch l{(const uint8_t *)x, (const uint8_t *)w, scale, (uint16_t *)y, partials, tickets, epoch,
                        (int)M, (int)N, (int)K, (int)p.k_slice, p.split_k, p.variant, vec};
+  l.bias = bias;
+  l.act = act;
+  l.fmt = fmt;
   e = fp8g::launch_skinny(l, stream);
   if (ws) {
     hipError_t f = hipFreeAsync(ws, stream);
@@ -317,12 +343,24 @@ extern "C" {
 
 int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y, int64_t M, int64_t N, int64_t K,
                     void *stream) {
-  return run(x, w, scale, y, M, N, K, 0, 0, 0, stream);
+  return run(x, w, scale, nullptr, y, M, N, K, FP8G_FMT_E4M3, FP8G_FMT_E4M3, FP8G_ACT_NONE, 0, 0, 0, stream);
 }
 
 int fp8_gemm_scaled_ex(const void *x, const void *w, const float *scale, void *y, int64_t M, int64_t N, int64_t K,
                        int32_t path, int32_t variant, int32_t split_k, void *stream) {
-  return run(x, w, scale, y, M, N, K, path, variant, split_k, stream);
+  return run(x, w, scale, nullptr, y, M, N, K, FP8G_FMT_E4M3, FP8G_FMT_E4M3, FP8G_ACT_NONE, path, variant, split_k,
+             stream);
+}
+
+int fp8_gemm_scaled_act(const void *x, const void *w, const float *scale, const float *bias, void *y, int64_t M,
+                        int64_t N, int64_t K, int32_t x_format, int32_t w_format, int32_t activation, void *stream) {
+  return run(x, w, scale, bias, y, M, N, K, x_format, w_format, activation, 0, 0, 0, stream);
+}
+
+int fp8_gemm_scaled_act_ex(const void *x, const void *w, const float *scale, const float *bias, void *y, int64_t M,
+                           int64_t N, int64_t K, int32_t x_format, int32_t w_format, int32_t activation,
+                           int32_t path, int32_t variant, int32_t split_k, void *stream) {
+  return run(x, w, scale, bias, y, M, N, K, x_format, w_format, activation, path, variant, split_k, stream);
 }
 
 int fp8_gemm_plan(int64_t M, int64_t N, int64_t K, fp8g_plan *out) {

@@ -19,6 +19,9 @@ struct MainLaunch {
   int variant;   // main-path configuration id
   bool k_tail;   // K % tile_k != 0
   int ystore;    // widest y store: 16 (N % 8 == 0, y 16-byte aligned), 8 (N % 4 == 0, y 8-byte aligned) or 2
+  const float *bias = nullptr;  // per-column bias [N], or null
+  int act = 0;                  // epilogue activation (FP8G_ACT_*)
+  int fmt = 0;                  // (w format << 1) | x format, 0 = E4M3, 1 = E5M2
   // variant 16 (stream-K) only:
   int n_dp = 0, n_sk = 0;                 // whole-tile workgroups, stream-K workgroups
   float *partials = nullptr;              // 2 * n_sk partial tiles of kMainPartialBytes
@@ -40,6 +43,9 @@ struct SkinnyLaunch {
   int k_slice, S;
   int variant;      // skinny configuration id
   bool vec;         // N % 4 == 0 and y 8-byte aligned
+  const float *bias = nullptr;  // per-column bias [N], or null
+  int act = 0;                  // epilogue activation (FP8G_ACT_*)
+  int fmt = 0;                  // (w format << 1) | x format, 0 = E4M3, 1 = E5M2
 };
 
 // Split-K tickets sit one 128-byte cache line apart (in 8-byte units): the
@@ -63,7 +69,15 @@ int skinny_max_row_blocks(int M, bool direct);  // limit on row_blocks for this 
 int skinny_chunk_bytes();                   // K granularity of one wave iteration
 
 hipError_t launch_main(const MainLaunch &l, hipStream_t stream);
+hipError_t launch_main5(const MainLaunch &l, hipStream_t stream);            // variants 10, 16
+hipError_t launch_main5_epi(const MainLaunch &l, hipStream_t stream);        // variant 10, bias / activation
+hipError_t launch_main_tiles(const MainLaunch &l, hipStream_t stream);       // variants 3, 17, 18
+hipError_t launch_main_tiles_epi(const MainLaunch &l, hipStream_t stream);   // the same, bias / activation
+hipError_t launch_main_legacy(const MainLaunch &l, hipStream_t stream);      // variants 1, 2, 4-7, 9
+hipError_t launch_skinny_epi(const SkinnyLaunch &l, hipStream_t stream);     // bias / activation, variants 11-15
 hipError_t launch_skinny(const SkinnyLaunch &l, hipStream_t stream);
 hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream);
+// K = 0 with a bias or an activation: y[m, n] = bf16(act(bias[n])).
+hipError_t launch_empty_k(uint16_t *y, const float *bias, int act, int64_t M, int64_t N, hipStream_t stream);
 
 }  // namespace fp8g

@@ -1,4 +1,6 @@
-// fp8g_kernels.hip -- gfx950 (CDNA4) kernels of the scaled FP8 GEMM
+// fp8g_kernels.hip -- configuration tables, the K = 0 kernels and the main-path
+// dispatch of libfp8g.so.  The kernel templates live in fp8g_kernels.hpp; the
+// fp8g_launch_*.hip units instantiate them.
 //
 //     y[m,n] = bf16_rne( (sum_k x[m,k] * w[n,k]) * scale[n] )
 //
@@ -35,1393 +37,23 @@
 // forced to zero: zero bytes add nothing to a dot product, which is why the
 // pages could pad with zeros ("Kimi K3 (256k)", SM100 persistent-TMA Triton
 // cell); here nothing is copied and nothing is padded in memory.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include "fp8g_internal.h"
+#include "fp8g_kernels.hpp"
 
 namespace fp8g {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-// LLVM's raw buffer intrinsics, taking the 128-bit descriptor as <4 x i32>.
-__device__ v4i llvm_buffer_load_v4i32(v4i rsrc, uint32_t voffset, uint32_t soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
-__device__ char llvm_buffer_load_i8(v4i rsrc, uint32_t voffset, uint32_t soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.i8");
-__device__ float llvm_buffer_load_f32(v4i rsrc, uint32_t voffset, uint32_t soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.f32");
-__device__ v4f llvm_buffer_load_v4f32(v4i rsrc, uint32_t voffset, uint32_t soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.v4f32");
-__device__ void llvm_buffer_store_v4f32(v4f data, v4i rsrc, uint32_t voffset, uint32_t soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.store.v4f32");
-__device__ void llvm_buffer_store_f32(float data, v4i rsrc, uint32_t voffset, uint32_t soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.store.f32");
-
-// Buffer descriptor: base address, stride 0 (raw), range `bytes`, and the
-// gfx9 data-format word (32-bit elements, bounds-checked raw access).
-__device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes) {
-  uint64_t a = (uint64_t)(uintptr_t)base;
-  v4i r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
-  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
-  r.w = 0x00020000;
-  return r;
-}
-
-__device__ __forceinline__ uint4 as_u4(v4i v) {
-  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
-}
-
-// 16 bytes at `off`, of which only the first `valid` (< 16) may be read; the
-// rest are zero.  Byte loads: each one is range-checked on its own.
-__device__ __forceinline__ uint4 load16_partial(v4i rsrc, uint32_t off, int valid) {
-  uint32_t d[4] = {0u, 0u, 0u, 0u};
-  for (int j = 0; j < valid; ++j) {
-    uint32_t b = (uint8_t)llvm_buffer_load_i8(rsrc, off + j, 0, 0);
-    d[j >> 2] |= b << (8 * (j & 3));
-  }
-  return make_uint4(d[0], d[1], d[2], d[3]);
-}
-
-// The same for 0 < valid < 16 when the row holds at least 16 bytes up to
-// off + valid (i.e. K >= 16): one 16-byte load that ends at the last valid
-// byte, moved down by 16 - valid bytes (whole dwords first, then the byte
-// remainder with a funnel shift) so the bytes past the row come in as zeros.
-// One memory round trip instead of `valid` dependent byte loads.
-__device__ __forceinline__ uint4 load16_tail(v4i rsrc, uint32_t off, int valid) {
-  const v4i v = llvm_buffer_load_v4i32(rsrc, off + (uint32_t)valid - 16u, 0, 0);
-  const int sh = 16 - valid;  // 1 .. 15
-  const int q = sh >> 2, r = sh & 3;
-  const uint32_t d0 = (uint32_t)v.x, d1 = (uint32_t)v.y, d2 = (uint32_t)v.z, d3 = (uint32_t)v.w;
-  const uint32_t e0 = q == 0 ? d0 : q == 1 ? d1 : q == 2 ? d2 : d3;
-  const uint32_t e1 = q == 0 ? d1 : q == 1 ? d2 : q == 2 ? d3 : 0u;
-  const uint32_t e2 = q == 0 ? d2 : q == 1 ? d3 : 0u;
-  const uint32_t e3 = q == 0 ? d3 : 0u;
-  // alignbyte(hi, lo, r) = low 32 bits of ({hi, lo} >> 8r)
-  return make_uint4(__builtin_amdgcn_alignbyte(e1, e0, r), __builtin_amdgcn_alignbyte(e2, e1, r),
-                    __builtin_amdgcn_alignbyte(e3, e2, r), __builtin_amdgcn_alignbyte(0u, e3, r));
-}
-
-// 16 bytes at `off` with `valid` bytes before the end of the row (any value);
-// K is the row length.
-__device__ __forceinline__ uint4 load16_masked(v4i rsrc, uint32_t off, int valid, int K) {
-  if (valid >= 16) return as_u4(llvm_buffer_load_v4i32(rsrc, off, 0, 0));
-  if (valid <= 0) return make_uint4(0u, 0u, 0u, 0u);
-  if (K >= 16) return load16_tail(rsrc, off, valid);
-  return load16_partial(rsrc, off, valid);
-}
-
-// LDS-DMA: 16 bytes per lane from global (voffset + soffset) into LDS at
-// lds_base + 16 * lane.  Written as inline asm so the compiler does not treat
-// it as an LDS store it must wait for before every LDS read; completion is
-// tracked by hand with vm_wait() below.  m0 is set inside the same statement.
-// (m0 is otherwise unused by these kernels, so clobbering it is safe.)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_base, uint32_t voffset, uint32_t soffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// fp32 -> bf16 bits, round to nearest, ties to even; NaN -> 0x7FC0.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ __forceinline__ v16f mfma32(const v8i &a, const v8i &b, const v16f &c) {
-  // Zero scale operands select the unscaled V_MFMA_F32_32X32X64_F8F6F4.
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// ------------------------------------------------------------------ main path
-//
-// One workgroup computes a BM (m) x BN (n) tile of y with WM x WN waves; each
-// wave owns a (BM/WM) x (BN/WN) sub-tile as 32x32 MFMA blocks.  The K loop
-// stages BK-byte slices of the BN w rows and BM x rows through a STAGES-deep
-// ring of LDS buffers filled by LDS-DMA (16 B per lane, 1 KiB per wave
-// instruction), so the global -> LDS copy needs no VGPRs and overlaps the MFMAs
-// of the stages already resident.
-//
-// LDS layout of one stage: w rows [0, BN) then x rows [0, BM), BK bytes each.
-// Within a row the 16-byte chunk c is stored at chunk position c ^ swz(r).  The
-// MFMA operand reads (lane l reads row l % 32) then touch eight different
-// chunk positions in every eight consecutive lanes and sixteen different
-// (bank half, position) pairs in every sixteen, so they are free of bank
-// conflicts whether LDS serves 128 or 256 bytes per cycle.  A DMA instruction
-// writes 1 KiB contiguously; the swizzle is applied on the global side by
-// choosing which chunk each lane fetches.
-template <int BK>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (BK == 128) return (r & 7) ^ ((r >> 3) & 1);
-  else return ((r >> 1) ^ (r >> 2)) & 3;  // BK == 64: four chunks per row
-}
-
-struct MainArgs {
-  const uint8_t *x;
-  const uint8_t *w;
-  const float *scale;
-  uint16_t *y;
-  int M, N, K;
-  int tiles_m, tiles_n, group_m;
-  int ystore;  // widest y store allowed by N and y's alignment: 16, 8 or 2 bytes
-  // Stream-K (five-slot kernel only; zero elsewhere).  Workgroups 0 .. n_dp-1
-  // each compute one whole tile, the first n_dp tiles of the raster order; the
-  // n_sk workgroups after them split the (tile, K step) units of the remaining
-  // tiles evenly.
-  int n_dp, n_sk;
-  float *P;                      // 2 partial-tile slots per stream-K workgroup
-  unsigned long long *tickets;   // one per stream-K tile, kTicketStride apart
-  unsigned long long epoch;      // this call's id (< 2^48)
-};
-
-// Cache policy of partial sums that pass between workgroups: device scope
-// (SC1), the encoding the compiler gives agent-scope atomic loads and stores.
-// Stores write through the XCD's L2 to the device coherence point and loads do
-// not hit stale lines, so partials move between XCDs without flushing or
-// invalidating whole caches.
-constexpr int kDeviceScope = 16;
-constexpr uint32_t kOut = 0x80000000u;  // a buffer offset past every descriptor's range: reads 0
-
-// Last-arrival hand-off: every workgroup that contributes to an output tile
-// takes the tile's ticket once, after its partial sums are visible device-wide;
-// the one that brings the count to `target` finishes the tile.  A ticket holds
-// (call id << 16 | arrivals); a ticket left by another call (or any stale
-// bytes) restarts at one arrival, so tickets need no zeroing before a launch.
-// The compare-and-swap loop is lock-free: a failed attempt means another
-// workgroup's succeeded.
-__device__ __forceinline__ bool take_ticket(unsigned long long *t, unsigned long long epoch, int target) {
-  unsigned long long old = __hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  unsigned long long want;
-  for (;;) {
-    want = (old >> 16) == epoch ? old + 1 : (epoch << 16) | 1ull;
-    if (__hip_atomic_compare_exchange_strong(t, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT))
-      break;
-  }
-  return (int)(want & 0xFFFFull) == target;
-}
-
-// Scheduling pattern for NM MFMAs and NR LDS reads spread evenly: MFMA q is
-// followed by reads [q*NR/NM, (q+1)*NR/NM).
-template <int Q, int NM, int NR>
-__device__ __forceinline__ void interleave_mfma_reads() {
-  if constexpr (Q < NM) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr ((Q + 1) * NR / NM - Q * NR / NM > 0)
-      __builtin_amdgcn_sched_group_barrier(0x100, (Q + 1) * NR / NM - Q * NR / NM, 0);
-    interleave_mfma_reads<Q + 1, NM, NR>();
-  }
-}
-
-// Workgroup -> tile.  Workgroup ids are dispatched round-robin over the 8 XCDs
-// (each with its own L2), so first renumber them so that every XCD works on a
-// contiguous range of tiles, then walk that range in groups of group_m tile
-// rows (all tile columns of a group before the next group) so the x rows and
-// w rows a group shares stay in the XCD's L2.
-__device__ __forceinline__ int xcd_remap(int pid, int count) {
-  const int xcd = pid & 7, q8 = count >> 3, r8 = count & 7;
-  return xcd * q8 + min(xcd, r8) + (pid >> 3);
-}
-__device__ __forceinline__ void raster(const MainArgs &a, int lpid, int &tm, int &tn) {
-  const int per_group = a.group_m * a.tiles_n;
-  const int gid = lpid / per_group;
-  const int first_m = gid * a.group_m;
-  const int gsize = min(a.tiles_m - first_m, a.group_m);
-  const int within = lpid - gid * per_group;
-  tm = first_m + within % gsize;
-  tn = within / gsize;
-}
-__device__ __forceinline__ void tile_coords(const MainArgs &a, int &tm, int &tn) {
-  raster(a, xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n), tm, tn);
-}
-
-// Epilogue of the main kernels: y[m, n..n+3] = bf16(acc * scale[n..n+3]) for a
-// BM x BN tile computed by WM x WN waves (wave tile (BM/WM) x (BN/WN) as 32x32
-// blocks), with the tile's scales at s_lds[0 .. BN) and at least 2*BM*BN bytes
-// of LDS at smem that no wave uses any more after the first barrier.
-template <int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void main_epilogue(const v16f (&acc)[BN / WN / 32][BM / WM / 32], const MainArgs &a,
-                                              uint8_t *smem, const float *s_lds, int m0, int n0, int wave,
-                                              int lane, int tid) {
-  constexpr int NWAVES = WM * WN, TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  // Epilogue: y[m, n..n+3] = bf16(acc * scale[n..n+3]), written through LDS so
-  // that y leaves in whole rows.  A lane's results are four consecutive n of
-  // one m, so stored directly every store instruction would touch 32 rows with
-  // 16 bytes each and every 128-byte line of y would be assembled from eight
-  // partial writes.  Instead the waves put the bf16 tile into the (now idle)
-  // stage buffers -- row pitch 2*BN bytes, 16-byte chunk c of row r at
-  // c ^ (r % CPR), which keeps both the 32-row writes and the row reads nearly
-  // free of bank conflicts -- and then write it out row by row, 16 bytes per
-  // lane, so one store instruction covers whole rows of the tile.
-  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
-  constexpr int PITCH = 2 * BN;
-  constexpr int NTHREADS = NWAVES * 64;
-  const int g = lane >> 5, lr = lane & 31;
-  const int wave_m = wave % WM, wave_n = wave / WM;
-  __syncthreads();  // every wave is done with the stage buffers (and s_lds is published)
-#pragma unroll
-  for (int i = 0; i < FN; ++i) {
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int nl = wave_n * TN + 32 * i + 8 * qd + 4 * g;
-      const float4 sc = *(const float4 *)(s_lds + nl);
-#pragma unroll
-      for (int jm = 0; jm < FM; ++jm) {
-        const int ml = wave_m * TM + 32 * jm + lr;
-        const uint32_t b0 = bf16_rne(acc[i][jm][4 * qd + 0] * sc.x);
-        const uint32_t b1 = bf16_rne(acc[i][jm][4 * qd + 1] * sc.y);
-        const uint32_t b2 = bf16_rne(acc[i][jm][4 * qd + 2] * sc.z);
-        const uint32_t b3 = bf16_rne(acc[i][jm][4 * qd + 3] * sc.w);
-        const int off = ml * PITCH + (((nl >> 3) ^ (ml & (CPR - 1))) << 4) + ((nl & 7) << 1);
-        *(uint2 *)(smem + off) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < BM * CPR; idx += NTHREADS) {
-    const int r = idx / CPR, c = idx % CPR;
-    const int m = m0 + r, n = n0 + 8 * c;
-    if (m >= a.M || n >= a.N) continue;
-    const uint4 v = *(const uint4 *)(smem + r * PITCH + ((c ^ (r & (CPR - 1))) << 4));
-    uint16_t *dst = a.y + (size_t)m * a.N + n;
-    if (a.ystore == 16) {  // N % 8 == 0 and y 16-byte aligned: the chunk is whole
-      *(uint4 *)dst = v;
-    } else if (a.ystore == 8) {  // N % 4 == 0 and y 8-byte aligned
-      *(uint2 *)dst = make_uint2(v.x, v.y);
-      if (n + 4 < a.N) *(uint2 *)(dst + 4) = make_uint2(v.z, v.w);
-    } else {
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (n + e < a.N) dst[e] = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
-    }
-  }
-}
-
-// Software pipeline.  A K step is BK bytes (one stage buffer), worked as BK/64
-// MFMA sub-steps; F[u & 1] holds the operands of sub-step u.  Sub-step u:
-//
-//     [last sub-step of step s only] wait for this wave's DMA of step s+1,
-//         workgroup barrier, LDS-DMA of step s+DIST into a retired buffer
-//     MFMAs of sub-step u (operands in F[u & 1]), interleaved with the LDS
-//     reads of sub-step u+1's operands into F[(u+1) & 1]
-//
-// The barrier publishes step s+1 (every wave's DMA has landed) and retires the
-// buffer of step s (every wave has read its operands).  BK = 128 halves the
-// barriers and has each DMA instruction fetch 8 rows x 128 bytes instead of
-// 16 rows x 64 bytes, which the global-to-LDS path serves faster (measured on
-// MI355X: ~7% on 4096^3 and 8192^3).
-// With 8 waves per workgroup two waves share each SIMD, so one wave's MFMAs
-// cover the other's barrier and LDS waits; a single wave per SIMD can neither
-// keep the matrix pipe full nor keep enough LDS reads in flight (measured on
-// MI355X: ~4.0-4.5 vs ~4.8 PFLOP/s for back-to-back MFMAs, ~110 vs ~200
-// B/clk/CU for 16-byte LDS reads).
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool KTAIL, bool PP>
-__global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) {
-  constexpr int NWAVES = WM * WN;
-  constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
-  constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 blocks per wave
-  constexpr int SUB = BK / 64;               // MFMA sub-steps per K step
-  constexpr int CH = BK / 16;                // 16-byte chunks per row
-  constexpr int ROWS_PER_KB = 1024 / BK;     // rows in one 1 KiB DMA block
-  constexpr int STAGE_BYTES = (BM + BN) * BK;
-  constexpr int BLOCKS = STAGE_BYTES / 1024;
-  constexpr int DPW = BLOCKS / NWAVES;       // DMA instructions per wave per stage
-  constexpr int W_DPW = (BN / ROWS_PER_KB) / NWAVES;  // of which fill w rows
-  constexpr int NMFMA = FN * FM;             // MFMAs per wave per 64-byte sub-step
-  constexpr int NREAD = (FN + FM) * 2;       // 16-byte LDS reads per wave per sub-step
-  // Prefetch distance in steps.  BK = 64: step k+STAGES-1 goes into the buffer
-  // retired one barrier earlier (issuing one step further ahead measured no
-  // faster).  BK = 128: step k+STAGES goes into the buffer of step k itself,
-  // which a step's last sub-step retires.
-  constexpr int DIST = SUB == 1 ? STAGES - 1 : STAGES;
-  static_assert(BK == 64 || BK == 128, "BK");
-  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
-  static_assert(BLOCKS % NWAVES == 0 && (BN / ROWS_PER_KB) % NWAVES == 0, "DMA split");
-  static_assert(DIST >= 2 && DIST <= 5 && (DIST - 1) * DPW < 64, "vmcnt range");
-  static_assert(BN <= 256, "one DMA instruction stages the tile's scales");
-
-  // Stage ring, then the tile's BN scales.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES + 1024];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave_m = wave % WM, wave_n = wave / WM;
-
-  int tm, tn;
-  tile_coords(a, tm, tn);
-
-  const int K = a.K;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
-  // A tile's rows form one range of at most 256 * (2^24 - 1) bytes, so an
-  // offset equal to it never wraps 32 bits; rows past M / N read zero.
-  const uint32_t range_x = (uint32_t)rows_x * (uint32_t)K, range_w = (uint32_t)rows_w * (uint32_t)K;
-
-  const int g = lane >> 5, lr = lane & 31;
-  const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
-  const uint32_t scale_lds = smem_base + STAGES * STAGE_BYTES;
-  // The tile's scales scale[n0 .. n0+BN) go to LDS now (wave 0, one DMA; columns
-  // past N read as zero), so the epilogue does not wait on global memory.  This
-  // is wave 0's oldest vector-memory operation, so its first stage wait covers
-  // it, and every barrier after that publishes it.
-  if (wave == 0) {
-    const v4i rsrc_s = make_rsrc(a.scale + n0, (uint32_t)(a.N - n0) * 4u);
-    dma16(rsrc_s, scale_lds, (uint32_t)lane * 16u, 0u);
-  }
-
-  // DMA instruction t of a wave fills 1 KiB block t*NWAVES + wave of a stage
-  // (w rows first, then x rows): ROWS_PER_KB rows of BK bytes, lane l taking
-  // row l / CH of the block and logical chunk (l % CH) ^ swz(row).  Blocks
-  // start at multiples of ROWS_PER_KB rows and NWAVES is even, so the row bits
-  // the swizzle reads are the same in every block: each lane has one source
-  // offset relative to its block and one chunk for all t, and block t gets
-  // its own descriptor (base moved to the block's first row, range cut to
-  // match, so rows past M / N still read zero).
-  static_assert(NWAVES % 2 == 0 && BN % 16 == 0, "block-invariant swizzle");
-  const int dma_lrow = wave * ROWS_PER_KB + lane / CH;  // row within block t = 0
-  const int dma_chunk = (lane % CH) ^ swz<BK>(dma_lrow);
-  const uint32_t laneff = (uint32_t)dma_lrow * (uint32_t)K + (uint32_t)dma_chunk * 16u;
-  const uint32_t blk_stride = (uint32_t)(NWAVES * ROWS_PER_KB) * (uint32_t)K;
-  v4i rs[DPW];
-#pragma unroll
-  for (int t = 0; t < DPW; ++t) {
-    const int tt = t < W_DPW ? t : t - W_DPW;
-    const uint32_t range = t < W_DPW ? range_w : range_x;
-    const uint32_t skip = (uint32_t)tt * blk_stride;  // < 256 * K: no wrap
-    const uint8_t *base = t < W_DPW ? a.w + (size_t)n0 * K : a.x + (size_t)m0 * K;
-    rs[t] = make_rsrc(base + skip, range > skip ? range - skip : 0u);
-  }
-
-  const int nk_full_c = K / BK;  // K steps that lie entirely before K
-
-  // Full K step kt -> stage buffer `st` via LDS-DMA.
-  auto issue_full = [&](int kt, int st) __attribute__((always_inline)) {
-    const uint32_t k0 = (uint32_t)kt * BK;
-    const uint32_t sb = smem_base + (uint32_t)st * STAGE_BYTES;
-#pragma unroll
-    for (int t = 0; t < DPW; ++t) dma16(rs[t], sb + (uint32_t)(t * NWAVES + wave) * 1024u, laneff, k0);
-  };
-  // Last, partial K step (k0 + BK > K) -> stage buffer `st`, also by LDS-DMA:
-  // chunks entirely before K load as usual, chunks at or past K are pointed out
-  // of range and land as zeros, and the one chunk per row that straddles K is
-  // zeroed the same way here and rebuilt later by fix_tail.
-  auto issue_tail = [&](int kt, int st) __attribute__((always_inline)) {
-    const int k0 = kt * BK;
-    const uint32_t sb = smem_base + (uint32_t)st * STAGE_BYTES;
-    const int valid = K - (k0 + 16 * dma_chunk);
-    // range_w / range_x bound every block's cut range from above
-    const uint32_t off_w = valid >= 16 ? laneff + (uint32_t)k0 : range_w;
-    const uint32_t off_x = valid >= 16 ? laneff + (uint32_t)k0 : range_x;
-#pragma unroll
-    for (int t = 0; t < DPW; ++t) dma16(rs[t], sb + (uint32_t)(t * NWAVES + wave) * 1024u, t < W_DPW ? off_w : off_x, 0u);
-  };
-  // Rebuild the straddling chunks of the tail stage (one shifted 16-byte load
-  // each, or byte loads when K < 16), bytes at or past K zero.  Called once every DMA
-  // of the tail stage has landed and before the barrier that publishes it; the
-  // barrier's LDS wait covers these writes.
-  auto fix_tail = [&](int st) __attribute__((always_inline)) {
-    const int k0 = nk_full_c * BK;
-    uint8_t *sb = smem + st * STAGE_BYTES;
-    const int valid = K - (k0 + 16 * dma_chunk);
-    if (valid > 0 && valid < 16) {
-#pragma unroll
-      for (int t = 0; t < DPW; ++t) {
-        const uint4 v = K >= 16 ? load16_tail(rs[t], laneff + (uint32_t)k0, valid)
-                                : load16_partial(rs[t], laneff + (uint32_t)k0, valid);
-        *(uint4 *)(sb + (t * NWAVES + wave) * 1024 + lane * 16) = v;
-      }
-    }
-  };
-  const int nk = nk_full_c + (KTAIL ? 1 : 0);
-  const int nk_full = nk_full_c;
-  auto issue = [&](int kt) __attribute__((always_inline)) {
-    if (kt < nk_full) issue_full(kt, kt % STAGES);
-    else if (KTAIL && kt == nk_full) issue_tail(kt, kt % STAGES);
-  };
-
-  // Fragment reads.  Lane l reads row (l % 32) of each 32-row block and the two
-  // chunks 4j + 2(l/32) + {0,1} of 64-byte sub-step j.
-  const int aw_row = wave_n * TN + lr;  // w row of block 0 (block i adds 32 i rows)
-  const int bx_row = wave_m * TM + lr;  // x row of block 0
-  const int sa = swz<BK>(aw_row), sbx = swz<BK>(bx_row);  // 32 i leaves the swizzle unchanged
-
-  // Operand registers of two sub-steps: F[u & 1] holds sub-step u.
-  v8i fa[2][FN], fb[2][FM];
-  // LDS read number q (q in [0, NREAD)) of sub-step j of stage `st`: low then
-  // high 16 bytes of each block, blocks in the order the MFMAs first use them
-  // (w block 0, all FM x blocks, then w blocks 1 .. FN-1).
-  auto read_one = [&](int st, int j, int q, v8i (&af)[FN], v8i (&bf)[FM]) __attribute__((always_inline)) {
-    const int ord = q / 2, half = q % 2;
-    const int blk = ord == 0 ? 0 : (ord <= FM ? FN + ord - 1 : ord - FM);
-    const int c = 4 * j + 2 * g + half;
-    const uint8_t *sw_ = smem + st * STAGE_BYTES;
-    if (blk < FN) {
-      const uint8_t *row = sw_ + (aw_row + 32 * blk) * BK;
-      const uint4 v = *(const uint4 *)(row + ((c ^ sa) << 4));
-      af[blk][4 * half + 0] = (int)v.x; af[blk][4 * half + 1] = (int)v.y;
-      af[blk][4 * half + 2] = (int)v.z; af[blk][4 * half + 3] = (int)v.w;
-    } else {
-      const uint8_t *row = sw_ + BN * BK + (bx_row + 32 * (blk - FN)) * BK;
-      const uint4 v = *(const uint4 *)(row + ((c ^ sbx) << 4));
-      bf[blk - FN][4 * half + 0] = (int)v.x; bf[blk - FN][4 * half + 1] = (int)v.y;
-      bf[blk - FN][4 * half + 2] = (int)v.z; bf[blk - FN][4 * half + 3] = (int)v.w;
-    }
-  };
-
-  v16f acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // Wait until this wave's DMA of a step has landed while the `ahead` (<= 4)
-  // steps issued after it may stay in flight (vmcnt completes in order).
-  auto wait_ahead = [&](int ahead) __attribute__((always_inline)) {
-    if (ahead >= 4) vm_wait<4 * DPW>();
-    else if (ahead == 3) vm_wait<3 * DPW>();
-    else if (ahead == 2) vm_wait<2 * DPW>();
-    else if (ahead == 1) vm_wait<DPW>();
-    else vm_wait<0>();
-  };
-
-  // Prologue: DMA of steps 0 .. DIST-1, then sub-step 0's operands.
-#pragma unroll
-  for (int s = 0; s < DIST; ++s) issue(s);
-  wait_ahead(min(DIST - 1, nk - 1));
-  if (KTAIL && nk_full == 0) {  // the tail is step 0: every DMA issued so far has landed
-    vm_wait<0>();
-    fix_tail(0);
-  }
-  __syncthreads();
-
-  if constexpr (PP) {
-    // Ping-pong schedule.  Waves are dealt to the four SIMDs round-robin, so
-    // waves 0-3 (group 0) and 4-7 (group 1) put one wave of each group on every
-    // SIMD.  The groups alternate between two kinds of phase, separated by
-    // workgroup barriers: a compute phase issues the wave's 8 MFMAs of one K step
-    // back to back from registers; a memory phase reads the next K step's
-    // operands from LDS and issues the wave's LDS-DMA share of the step three
-    // ahead.  While one wave of a SIMD computes, the other one loads, so the
-    // matrix pipe of every SIMD is fed by one wave or the other and a barrier
-    // does not drain it.
-    //
-    //   phase 2k  : group 0 memory(k)            group 1 compute(k-1)
-    //   phase 2k+1: group 0 compute(k)           group 1 memory(k)
-    //
-    // Step k lives in stage k % 4.  Memory(k) issues step k+3 into the stage of
-    // step k-1, which both groups finished reading by the end of phase 2k-1.
-    // The barrier ending phase 2k+1 publishes step k+1: before it every wave
-    // waits for its own DMA of step k+1 (steps k+2 and k+3 may stay in flight).
-    static_assert(SUB == 1 && STAGES == 4 && NWAVES == 8 && DIST == 3, "ping-pong layout");
-    const int grp = wave >> 2;
-    auto mem = [&](int k) __attribute__((always_inline)) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < NREAD; ++q) read_one(k % STAGES, 0, q, fa[0], fb[0]);
-      issue(k + DIST);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto comp = [&]() __attribute__((always_inline)) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < NMFMA; ++q) {
-        const int i = q / FM, jm = q % FM;
-        acc[i][jm] = mfma32(fa[0][i], fb[0][jm], acc[i][jm]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // Both groups run the same body, memory(k) then compute(k); group 1 runs
-    // it one phase later (an extra barrier first, none after its last compute),
-    // so every wave executes the same number of barriers.  The wait that
-    // publishes step k+1 belongs to phase 2k+1, which is group 0's compute and
-    // group 1's memory phase.
-    auto publish = [&](int k) __attribute__((always_inline)) {
-      wait_ahead(min(2, nk - 2 - k));
-      if (KTAIL && k + 1 == nk_full) fix_tail((k + 1) % STAGES);
-    };
-    if (grp == 1) __syncthreads();
-    for (int k = 0; k < nk; ++k) {
-      mem(k);
-      if (grp == 1) publish(k);
-      __syncthreads();
-      comp();
-      if (grp == 0) publish(k);
-      if (grp == 0 || k + 1 < nk) __syncthreads();
-    }
-  } else {
-#pragma unroll
-  for (int q = 0; q < NREAD; ++q) read_one(0, 0, q, fa[0], fb[0]);
-
-  // Sub-step u (step s = u / SUB, part j = u % SUB): MFMAs on F[cur],
-  // interleaved with the reads of sub-step u+1 into F[cur ^ 1].  The last
-  // sub-step of a step is a boundary: before it, step s+1 must be published.
-  const int nsub = nk * SUB;
-  auto substep = [&](const int u, const int cur, const bool boundary) __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-    const int s = u / SUB;
-    if (boundary) {
-      // Own DMA of step s+1 must have landed; steps s+2 .. s+DIST-1 (issued
-      // earlier) may stay in flight.
-      wait_ahead(min(DIST - 2, nk - 2 - s));
-      // step s+1 is the tail: the wait above covered its DMA (nothing is
-      // issued after the tail), so rebuild its straddling chunks before
-      // publishing it
-      if (KTAIL && s + 1 == nk_full) fix_tail((s + 1) % STAGES);
-      // After this barrier every wave has read all operands of step s (the
-      // last of them during the previous sub-step), so its buffer is free;
-      // so is the buffer of step s-1.  Step s+DIST goes into one of them.
-      __syncthreads();
-      issue(s + DIST);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const bool more = u + 1 < nsub;
-    const int un = u + 1;
-    const int st = (un / SUB) % STAGES, jn = un % SUB;
-#pragma unroll
-    for (int q = 0; q < NMFMA; ++q) {
-      const int i = q / FM, jm = q % FM;
-      acc[i][jm] = mfma32(fa[cur][i], fb[cur][jm], acc[i][jm]);
-      if (more) {
-#pragma unroll
-        for (int r = q * NREAD / NMFMA; r < (q + 1) * NREAD / NMFMA; ++r) read_one(st, jn, r, fa[cur ^ 1], fb[cur ^ 1]);
-      }
-    }
-    interleave_mfma_reads<0, NMFMA, NREAD>();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  if constexpr (SUB == 1) {
-    int u = 0;
-    for (; u + 1 < nsub; u += 2) {
-      substep(u, 0, true);
-      substep(u + 1, 1, true);
-    }
-    if (u < nsub) substep(u, 0, true);
-  } else {
-    for (int s = 0; s < nk; ++s) {
-      substep(2 * s, 0, false);
-      substep(2 * s + 1, 1, true);
-    }
-  }
-  }  // PP
-
-  static_assert(2 * BM * BN <= STAGES * STAGE_BYTES, "the bf16 tile fits in the stage buffers");
-  main_epilogue<BM, BN, WM, WN>(acc, a, smem, (const float *)(smem + STAGES * STAGE_BYTES), m0, n0, wave, lane,
-                                (int)threadIdx.x);
-}
-
-// ------------------------------------------------- main path, five LDS slots
-//
-// 256 x 256 tiles, 128-byte K steps, 8 waves with 64 (m) x 128 (n) wave tiles,
-// as variant 6 of the kernel above, but with a deeper feed.  Measured on
-// MI355X, the global-to-LDS copy of a K step (64 KiB per workgroup, 64 LDS-DMA
-// instructions) is limited by how fast the compute unit accepts DMA
-// instructions (about one per 20-25 cycles): issued in one burst after the
-// barrier, the second wave of every SIMD stalls for ~1400 cycles before it can
-// issue its MFMAs.  Spreading the instructions over the step needs them to be
-// issued earlier, i.e. more buffering than two 64 KiB stages in 160 KiB of LDS.
-//
-// So a stage is split in halves: LDS holds five 32 KiB slots, each one K step
-// of either the tile's w rows or its x rows -- w of step k in slot k % 2, x of
-// step k in slot 2 + k % 3.  x (whose rows are shared by fewer of the tiles an
-// XCD runs at once, so it misses L2 more often) is fetched two steps ahead and
-// w one step ahead, and every DMA instruction is issued between two MFMAs, so
-// no wave waits long for the instruction queue.  The epilogue's
-// scales no longer fit in LDS during the K loop: thread t < 256 keeps
-// scale[n0 + t] in a register and writes it to LDS after the loop.
-// Stream-K work split (variant 16).  Units are (tile, K step) pairs numbered
-// tile * nk + step over the stream-K tiles only; stream-K workgroup i takes the
-// units [sk_start(i), sk_start(i + 1)).
-// The host keeps every unit number below 2^31.
-__device__ __forceinline__ int sk_start(int i, int units, int n_sk) { return (int)((int64_t)i * units / n_sk); }
-// The stream-K workgroup whose range holds unit u (the largest i with sk_start(i) <= u).
-__device__ __forceinline__ int sk_owner(int u, int units, int n_sk) {
-  return (int)(((int64_t)(u + 1) * n_sk - 1) / units);
-}
-// Bytes of one partial tile: 512 threads x 128 fp32 accumulators, stored in
-// register order (thread t's float4 q at (q * 512 + t) * 16), since only the
-// same thread of another workgroup of this kernel reads it back.
-constexpr uint32_t kPartialBytes = (uint32_t)kMainPartialBytes;
-
-template <bool KTAIL, bool SK>
-__global__ __launch_bounds__(512, 1) void fp8g_main5_kernel(MainArgs a) {
-  constexpr int BM = 256, BN = 256, BK = 128, WM = 4, WN = 2, NWAVES = 8;
-  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  constexpr int CH = BK / 16, ROWS_PER_KB = 1024 / BK;
-  constexpr int SLOT = 256 * BK;                         // one half step: 256 rows x 128 bytes
-  constexpr int HDPW = SLOT / 1024 / NWAVES;             // DMA instructions per wave per half step (4)
-  constexpr int NMFMA = FN * FM, NREAD = (FN + FM) * 2;  // per wave per 64-byte sub-step
-  static_assert(HDPW == 4 && NMFMA == 8, "x DMAs are spread two per sub-step, after MFMAs 1 and 5");
-  static_assert(2 * BM * BN + BN * 4 <= 5 * SLOT, "epilogue tile and scales fit");
-  static_assert(FN * FM * 16 == 128 && NWAVES * 64 * 128 * 4 == (int)kPartialBytes, "partial tile layout");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * SLOT];
-
-  const int K = a.K;
-  const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
-  const int total = a.tiles_m * a.tiles_n;
-  const int nk_full = K / BK;
-  const int nk = nk_full + (KTAIL ? 1 : 0);  // K steps of a tile
-  auto slot_w = [&](int k) __attribute__((always_inline)) { return (uint32_t)((k & 1) * SLOT); };
-  auto slot_x = [&](int k) __attribute__((always_inline)) { return (uint32_t)((2 + k % 3) * SLOT); };
-
-  // This workgroup's units [u0, u1), unit = tile * nk + K step with tiles in
-  // raster order: one whole tile, or (stream-K) a contiguous range that may
-  // cover the end of one tile, whole tiles, and the start of another.
-  // Without stream-K only the tile is used (u0 = tile, one segment of nk
-  // steps); with it the host keeps all unit numbers below 2^31.
-  int u0, u1;
-  int sk_i = 0;
-  if (!SK || (int)blockIdx.x < a.n_dp) {
-    const int t = xcd_remap(blockIdx.x, SK ? a.n_dp : total);
-    u0 = SK ? t * nk : t;
-    u1 = SK ? u0 + nk : t + 1;
-  } else {
-    // consecutive ranges share a tile, so keep them on one XCD
-    sk_i = xcd_remap(blockIdx.x - a.n_dp, a.n_sk);
-    const int units = (total - a.n_dp) * nk;
-    u0 = a.n_dp * nk + sk_start(sk_i, units, a.n_sk);
-    u1 = a.n_dp * nk + sk_start(sk_i + 1, units, a.n_sk);
-  }
-
-  for (int u = u0; u < u1;) {
-    // Segment: steps [kb, ke) of one tile.
-    const int tile = SK ? u / nk : u0;
-    const int kb = SK ? u - tile * nk : 0;
-    const int ke = SK ? min(nk, kb + (u1 - u)) : nk;
-    const bool first_seg = u == u0;
-    u += SK ? ke - kb : 1;
-    if (SK && !first_seg) {
-      // the previous segment's last LDS reads (epilogue or ticket flag) and
-      // stores are done before this one's DMAs refill the slots
-      vm_wait<0>();
-      __syncthreads();
-    }
-    const int nkl = ke - kb;  // steps of this segment; local step s is K step kb + s
-
-    // Thread ids.  With stream-K they pass through an empty asm, so the
-    // compiler cannot see through them and computes what derives from them
-    // (DMA offsets, LDS fragment addresses, epilogue addresses) in each
-    // segment instead of hoisting it out of the segment loop and keeping it
-    // live -- spilled -- across every K loop.
-    int tid = threadIdx.x;
-    int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if constexpr (SK) {
-      asm volatile("" : "+v"(tid));
-      asm volatile("" : "+s"(wave));
-    }
-    const int lane = tid & 63;
-    const int wave_m = wave % WM, wave_n = wave / WM;
-    const int g = lane >> 5, lr = lane & 31;
-
-    // DMA instruction t (0..3) of a wave fills 1 KiB block t*8 + wave of a half
-    // step: 8 rows of 128 bytes, lane l taking row l / 8 and logical chunk
-    // (l % 8) ^ swz(row); descriptor t starts at the block's first row (rows past
-    // M / N read zero).
-    const int dma_lrow = wave * ROWS_PER_KB + lane / CH;
-    const int dma_chunk = (lane % CH) ^ swz<BK>(dma_lrow);
-    const uint32_t laneff = (uint32_t)dma_lrow * (uint32_t)K + (uint32_t)dma_chunk * 16u;
-    const uint32_t blk_stride = (uint32_t)(NWAVES * ROWS_PER_KB) * (uint32_t)K;
-    // Fragment reads: lane l reads row (l % 32) of each 32-row block, chunks
-    // 4j + 2(l/32) + {0,1} of 64-byte sub-step j; blocks in first-use order.
-    const int aw_row = wave_n * TN + lr, bx_row = wave_m * TM + lr;
-    const int sa = swz<BK>(aw_row), sbx = swz<BK>(bx_row);
-    int tm, tn;
-    raster(a, tile, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
-    const uint32_t range_x = (uint32_t)rows_x * (uint32_t)K, range_w = (uint32_t)rows_w * (uint32_t)K;
-
-    // The epilogue's scale for column n0 + tid (zero past N); the load is the
-    // oldest vector-memory operation, so every DMA wait below also covers it.
-    float my_scale = 0.0f;
-    if (tid < BN)
-      my_scale = llvm_buffer_load_f32(make_rsrc(a.scale + n0, (uint32_t)(a.N - n0) * 4u), (uint32_t)tid * 4u, 0, 0);
-
-    v4i rw[HDPW], rx[HDPW];
-#pragma unroll
-    for (int t = 0; t < HDPW; ++t) {
-      const uint32_t skip = (uint32_t)t * blk_stride;
-      rw[t] = make_rsrc(a.w + (size_t)n0 * K + skip, range_w > skip ? range_w - skip : 0u);
-      rx[t] = make_rsrc(a.x + (size_t)m0 * K + skip, range_x > skip ? range_x - skip : 0u);
-    }
-
-    // DMA instruction t of local step kt's w (or x) half; nothing past the
-    // segment is fetched.  The tile's tail step points chunks at or past K out
-    // of range (zeros) and fix_tail rebuilds the straddling one.
-    auto dma_half = [&](const v4i &rs, uint32_t range, uint32_t slot, int kt, int t) __attribute__((always_inline)) {
-      const uint32_t lds = smem_base + slot + (uint32_t)(t * NWAVES + wave) * 1024u;
-      if (kt < nkl) {
-        const int kg = kb + kt;
-        if (!KTAIL || kg < nk_full) {
-          dma16(rs, lds, laneff, (uint32_t)kg * BK);
-        } else {
-          const int valid = K - (kg * BK + 16 * dma_chunk);
-          dma16(rs, lds, valid >= 16 ? laneff + (uint32_t)(kg * BK) : range, 0u);
-        }
-      }
-    };
-    auto issue_w = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-      for (int t = 0; t < HDPW; ++t) dma_half(rw[t], range_w, slot_w(kt), kt, t);
-    };
-    auto issue_x = [&](int kt, int t) __attribute__((always_inline)) { dma_half(rx[t], range_x, slot_x(kt), kt, t); };
-    auto fix_tail = [&](int kt) __attribute__((always_inline)) {
-      const int k0 = (kb + kt) * BK;
-      const int valid = K - (k0 + 16 * dma_chunk);
-      if (valid > 0 && valid < 16) {
-#pragma unroll
-        for (int t = 0; t < 2 * HDPW; ++t) {  // w blocks, then x blocks, one at a time (runs once)
-          const v4i &rs = t < HDPW ? rw[t % HDPW] : rx[t % HDPW];
-          const uint4 v = K >= 16 ? load16_tail(rs, laneff + (uint32_t)k0, valid)
-                                  : load16_partial(rs, laneff + (uint32_t)k0, valid);
-          const uint32_t slot = t < HDPW ? slot_w(kt) : slot_x(kt);
-          *(uint4 *)(smem + slot + ((t % HDPW) * NWAVES + wave) * 1024 + lane * 16) = v;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    };
-
-    v8i fa[2][FN], fb[2][FM];
-    auto read_one = [&](int k, int j, int q, v8i (&af)[FN], v8i (&bf)[FM]) __attribute__((always_inline)) {
-      const int ord = q / 2, half = q % 2;
-      const int blk = ord == 0 ? 0 : (ord <= FM ? FN + ord - 1 : ord - FM);
-      const int c = 4 * j + 2 * g + half;
-      if (blk < FN) {
-        const uint8_t *row = smem + slot_w(k) + (aw_row + 32 * blk) * BK;
-        const uint4 v = *(const uint4 *)(row + ((c ^ sa) << 4));
-        af[blk][4 * half + 0] = (int)v.x; af[blk][4 * half + 1] = (int)v.y;
-        af[blk][4 * half + 2] = (int)v.z; af[blk][4 * half + 3] = (int)v.w;
-      } else {
-        const uint8_t *row = smem + slot_x(k) + (bx_row + 32 * (blk - FN)) * BK;
-        const uint4 v = *(const uint4 *)(row + ((c ^ sbx) << 4));
-        bf[blk - FN][4 * half + 0] = (int)v.x; bf[blk - FN][4 * half + 1] = (int)v.y;
-        bf[blk - FN][4 * half + 2] = (int)v.z; bf[blk - FN][4 * half + 3] = (int)v.w;
-      }
-    };
-
-    v16f acc[FN][FM];
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int j = 0; j < FM; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    // Prologue: w(0), x(0), x(1), w(1), x(2) -- the steady-state issue order --
-    // then wait for step 0 (what was issued after x(0) may stay in flight).
-    issue_w(0);
-#pragma unroll
-    for (int t = 0; t < HDPW; ++t) issue_x(0, t);
-#pragma unroll
-    for (int t = 0; t < HDPW; ++t) issue_x(1, t);
-    issue_w(1);
-#pragma unroll
-    for (int t = 0; t < HDPW; ++t) issue_x(2, t);
-    if (nkl >= 3) vm_wait<3 * HDPW>();
-    else if (nkl == 2) vm_wait<2 * HDPW>();
-    else vm_wait<0>();
-    if (KTAIL && kb == nk_full) fix_tail(0);  // the segment is the tail step alone: everything issued has landed
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < NREAD; ++q) read_one(0, 0, q, fa[0], fb[0]);
-
-    // Sub-step u = 2s + j of local step s.  j = 1 is the boundary: wait for
-    // this wave's DMA of w(s+1) and x(s+1), barrier (publishes step s+1, retires
-    // step s's slots), then, spread over the MFMAs, w(s+2) into the slot of w(s)
-    // and the first half of x(s+3) into the slot of x(s); sub-step 2s+2 issues
-    // the second half of x(s+3).
-    const int nsub = 2 * nkl;
-    auto substep = [&](const int us, const int cur) __attribute__((always_inline)) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int s = us >> 1, j = us & 1;
-      if (j == 1) {
-        // This wave's last DMA of w(s+1) came after MFMA 6 of sub-step 2s-1;
-        // after it only x(s+2) instructions 1 (after MFMA 7), 2 and 3 (sub-step
-        // 2s) were issued, so at most 3 may stay in flight.  (At s = 0 the
-        // prologue issued all of x(2) after w(1): waiting for 3 is stricter.)
-        if (s + 2 < nkl) vm_wait<HDPW - 1>();
-        else vm_wait<0>();
-        if (KTAIL && kb + s + 1 == nk_full) fix_tail(s + 1);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const int xk = j == 1 ? s + 3 : s + 2;  // x step whose DMAs this sub-step spreads
-      const int xt = j == 1 ? 0 : 2;          // ... instructions xt and xt + 1
-      const bool xdma = j == 1 || s >= 1;
-      const bool more = us + 1 < nsub;
-      const int un = us + 1;
-#pragma unroll
-      for (int q = 0; q < NMFMA; ++q) {
-        const int i = q / FM, jm = q % FM;
-        acc[i][jm] = mfma32(fa[cur][i], fb[cur][jm], acc[i][jm]);
-        if (more) {
-#pragma unroll
-          for (int r = q * NREAD / NMFMA; r < (q + 1) * NREAD / NMFMA; ++r)
-            read_one(un >> 1, un & 1, r, fa[cur ^ 1], fb[cur ^ 1]);
-        }
-        // w(s+2) after MFMAs 0, 2, 4, 6 of the boundary sub-step, x after MFMAs 3
-        // and 7 (measured best among the placements tried: a burst of DMA
-        // instructions right after the barrier stalls the issuing waves)
-        if (j == 1 && (q & 1) == 0) dma_half(rw[q >> 1], range_w, slot_w(s + 2), s + 2, q >> 1);
-        if ((q == 3 || q == 7) && xdma) issue_x(xk, xt + (q == 7 ? 1 : 0));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    for (int s = 0; s < nkl; ++s) {
-      substep(2 * s, 0);
-      substep(2 * s + 1, 1);
-    }
-
-    if constexpr (SK) {
-      if (kb != 0 || ke != nk) {
-        // Part of a tile.  Contributors are the stream-K workgroups c0 .. c1
-        // whose ranges meet the tile, in K order.  Each stores its partial sums
-        // (slot 2i if the segment opens the workgroup's range, else 2i+1: a
-        // range holds at most one opening and one closing partial segment),
-        // and the last to take the tile's ticket adds them all.
-        const int tt = tile - a.n_dp;
-        const int units = (total - a.n_dp) * nk;
-        const int tu0 = tt * nk;
-        const int c0 = sk_owner(tu0, units, a.n_sk), c1 = sk_owner(tu0 + nk - 1, units, a.n_sk);
-        auto slot_of = [&](int i) __attribute__((always_inline)) {
-          return (uint32_t)(2 * i + (sk_start(i, units, a.n_sk) >= tu0 ? 0 : 1)) * kPartialBytes;
-        };
-        const v4i rsrc_p = make_rsrc(a.P, (uint32_t)a.n_sk * 2u * kPartialBytes);
-        // Thread t's float4 q of a partial tile sits at slot + q * 8 KiB + t * 16:
-        // the per-thread part is the one VGPR offset, the rest goes in the
-        // (uniform) scalar offset, so no address registers live across the loop.
-        const uint32_t toff = (uint32_t)tid * 16u;
-        auto own4 = [&](int q) __attribute__((always_inline)) {
-          const int i = q / (4 * FM), jm = (q / 4) % FM, e = 4 * (q % 4);
-          return v4f{acc[i][jm][e], acc[i][jm][e + 1], acc[i][jm][e + 2], acc[i][jm][e + 3]};
-        };
-        {
-          const uint32_t mine = slot_of(sk_i);
-#pragma unroll
-          for (int q = 0; q < 32; ++q)
-            llvm_buffer_store_v4f32(own4(q), rsrc_p, toff, mine + (uint32_t)q * 8192u, kDeviceScope);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-        __syncthreads();  // all partial stores acknowledged; every wave is done with the slots
-        int *flag = (int *)smem;
-        if (tid == 0) *flag = take_ticket(a.tickets + (size_t)tt * kTicketStride, a.epoch, c1 - c0 + 1);
-        __syncthreads();
-        const bool last = *flag != 0;
-        if (!last) continue;
-        asm volatile("" : : : "memory");
-        // acc = P[c0] + P[c0+1] + ... + P[c1], added in that order whoever
-        // finishes (the own part comes from registers), so the result does
-        // not depend on arrival order.  Four float4 per thread at a time.
-#pragma unroll
-        for (int q0 = 0; q0 < 32; q0 += 4) {
-          __builtin_amdgcn_sched_barrier(0);
-          v4f t[4];
-          if (c0 == sk_i) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) t[jj] = own4(q0 + jj);
-          } else {
-            const uint32_t base = slot_of(c0);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-              t[jj] = llvm_buffer_load_v4f32(rsrc_p, toff, base + (uint32_t)(q0 + jj) * 8192u, kDeviceScope);
-          }
-          for (int c = c0 + 1; c <= c1; ++c) {
-            if (c == sk_i) {
-#pragma unroll
-              for (int jj = 0; jj < 4; ++jj) t[jj] += own4(q0 + jj);
-            } else {
-              const uint32_t base = slot_of(c);
-              v4f v[4];
-#pragma unroll
-              for (int jj = 0; jj < 4; ++jj)
-                v[jj] = llvm_buffer_load_v4f32(rsrc_p, toff, base + (uint32_t)(q0 + jj) * 8192u, kDeviceScope);
-#pragma unroll
-              for (int jj = 0; jj < 4; ++jj) t[jj] += v[jj];
-            }
-          }
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int q = q0 + jj, i = q / (4 * FM), jm = (q / 4) % FM, e = 4 * (q % 4);
-            acc[i][jm][e] = t[jj].x; acc[i][jm][e + 1] = t[jj].y;
-            acc[i][jm][e + 2] = t[jj].z; acc[i][jm][e + 3] = t[jj].w;
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-
-    // Scales into LDS (past the bf16 tile), published by the epilogue's first barrier.
-    float *s_lds = (float *)(smem + 2 * BM * BN);
-    __syncthreads();  // every wave is done with the slots (and the ticket flag)
-    if (tid < BN) s_lds[tid] = my_scale;
-    main_epilogue<BM, BN, WM, WN>(acc, a, smem, s_lds, m0, n0, wave, lane, tid);
-  }
-}
-
-// ---------------------------------------------------------------- skinny path
-//
-// M <= 64 (decode-shaped): the time is the stream of w through HBM.  A workgroup
-// owns R = 16*RB rows of w (output columns) and one K slice.  Its four waves take
-// the slice's 128-byte K chunks round-robin (wave v: chunks v, v+4, v+8, ...), so
-// together they read every w row front to back.  Each wave streams its chunks --
-// R rows of w and 16*MB rows of x, 128 bytes each -- into a private ring of D LDS
-// slots with LDS-DMA, one 1 KiB instruction per 8 rows, and multiplies them with
-// V_MFMA_F32_16X16X128_F8F6F4 (A = 16 w rows, B = 16 x rows).  w is loaded with
-// the non-temporal policy (read once; on gfx950 this roughly doubles streaming
-// read bandwidth), x without it (every workgroup re-reads x, so it should stay in
-// L2).  No barrier is needed in the K loop because no wave reads another wave's
-// slots; completion is tracked with vmcnt.  At the end the four per-wave sums are
-// added through LDS in wave order, so results are deterministic.
-//
-// MFMA 16x16x128 layout (gfx950, checked on the hardware): operand lane l supplies
-// row l % 16 and the 32 bytes of K-group l / 16; accumulator lane l, element e is
-// row 4*(l/16) + e, column l % 16.  Rows here are w rows (n), columns x rows (m).
-//
-// blockIdx.y selects the K slice [s * k_slice, min(K, (s+1) * k_slice)).  With one
-// slice the kernel scales and writes bf16 y; with several it writes unscaled fp32
-// partials that the last workgroup of the column tile adds in slice order
-// (splitk_finish).
-struct SkinnyArgs {
-  const uint8_t *x;
-  const uint8_t *w;
-  const float *scale;
-  uint16_t *y;
-  float *P;                  // fp32 partials [column tile][S][M][16*RB] (S > 1)
-  unsigned long long *tickets;  // one per column tile, kTicketStride apart (S > 1), any initial value
-  unsigned long long epoch;  // this call's id (< 2^48)
-  int M, N, K;
-  int k_slice;
-  int vec;  // y rows allow 8-byte stores / P rows 16-byte stores (N % 4 == 0)
-};
-
-template <int RB, int MB>
-struct SkinnyShape {
-  static constexpr int R = 16 * RB;        // w rows per workgroup
-  static constexpr int MX = 16 * MB;       // x rows staged per chunk
-  static constexpr int ROWS = R + MX;
-  static constexpr int SLOT = ROWS * 128;  // bytes per ring slot
-  static constexpr int OPS = ROWS / 8;     // 1 KiB DMA instructions per chunk
-  static constexpr int D = 3;              // ring depth (chunks in flight per wave)
-  static constexpr int WAVE_LDS = D * SLOT;
-  static_assert(4 * WAVE_LDS <= 160 * 1024, "LDS");
-  static_assert((D - 1) * OPS < 64, "vmcnt range");
-};
-
-// 128-byte rows, 16-row MFMA reads: chunk c of row r lives at position c ^ swz16(r);
-// every 8 consecutive rows use 8 different positions, every 16 rows 16 different
-// (bank half, position) pairs.
-__device__ __forceinline__ int swz16(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-__device__ __forceinline__ void dma16_nt(v4i rsrc, uint32_t lds_base, uint32_t voffset, uint32_t soffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
-               :
-               : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
-               : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N) / lgkmcnt(0) as compiler memory barriers: LDS reads of data
-// written by LDS-DMA must not be moved above the wait that covers the DMA.
-template <int N>
-__device__ __forceinline__ void vm_wait_fence() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-__device__ __forceinline__ void lgkm_wait_fence() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
-
-__device__ __forceinline__ v4f mfma16(const v8i &a, const v8i &b, const v4f &c) {
-  // Zero scale operands select the unscaled V_MFMA_F32_16X16X128_F8F6F4.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// Split-K with S > 1 slices, in the same launch.  Every workgroup of a column
-// tile has stored its unscaled fp32 partials (tile-major: the tile's S slices
-// of M x 16*RB floats are contiguous); the last of the tile's S workgroups to
-// finish adds them in slice order s = 0, 1, ..., S-1, scales, rounds to bf16 and
-// writes y, so the result does not depend on the order the workgroups ran in.
-// "Last" is decided on the tile's ticket (take_ticket).  Ordering: each wave
-// waits until its device-scope partial stores are acknowledged, the workgroup
-// meets at a barrier, and only then does one thread take the ticket; the last
-// workgroup reads with device scope after its ticket.  No L2 write-back or
-// invalidate is needed for these accesses.
-template <int RB>
-__device__ __forceinline__ void splitk_finish(const SkinnyArgs &a, int n0, int *flag) {
-  constexpr int R = 16 * RB;
-  const int S = (int)gridDim.y;
-  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) *flag = take_ticket(a.tickets + (size_t)blockIdx.x * kTicketStride, a.epoch, S);
-  __syncthreads();
-  if (!*flag) return;
-  asm volatile("" : : : "memory");
-  const v4i rsrc_p = make_rsrc(a.P + (size_t)blockIdx.x * S * a.M * R, (uint32_t)(S * a.M * R) * 4u);
-  const uint32_t slice_bytes = (uint32_t)(a.M * R) * 4u;
-  constexpr int q4 = R / 4;  // four-column groups in the tile
-  // Each thread sums IT items (four columns of one row), IT * SB loads in flight
-  // at a time; loads that fall past S or past the items read zero and are unused.
-  constexpr int IT = 2, SB = 8;
-  const int items = a.M * q4;
-  const v4i rsrc_s = make_rsrc(a.scale + n0, (uint32_t)min(R, a.N - n0) * 4u);
-  for (int i0 = threadIdx.x; i0 < items; i0 += IT * (int)blockDim.x) {
-    uint32_t off[IT];
-    v4f acc[IT], sc[IT];
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const int idx = i0 + i * (int)blockDim.x;
-      off[i] = idx < items ? (uint32_t)((idx / q4) * R + 4 * (idx % q4)) * 4u : kOut;
-      // scale of the item's four columns, requested before the partials
-      sc[i] = llvm_buffer_load_v4f32(rsrc_s, idx < items ? (uint32_t)(4 * (idx % q4)) * 4u : kOut, 0, 0);
-      acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int s0 = 0; s0 < S; s0 += SB) {
-      v4f v[IT][SB];
-#pragma unroll
-      for (int j = 0; j < SB; ++j)
-#pragma unroll
-        for (int i = 0; i < IT; ++i)
-          v[i][j] = llvm_buffer_load_v4f32(rsrc_p, s0 + j < S ? off[i] + (uint32_t)(s0 + j) * slice_bytes : kOut, 0,
-                                           kDeviceScope);
-#pragma unroll
-      for (int j = 0; j < SB; ++j)
-#pragma unroll
-        for (int i = 0; i < IT; ++i) {
-          if (s0 + j >= S) continue;
-          // slice 0 starts the sum (keeps its sign of zero), the others add in order
-          if (s0 + j == 0) acc[i] = v[i][j];
-          else { acc[i].x += v[i][j].x; acc[i].y += v[i][j].y; acc[i].z += v[i][j].z; acc[i].w += v[i][j].w; }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const int idx = i0 + i * (int)blockDim.x;
-      if (idx >= items) continue;
-      const int m = idx / q4, n = n0 + 4 * (idx % q4);
-      if (n >= a.N) continue;
-      uint16_t *yr = a.y + (size_t)m * a.N;
-      const uint32_t b0 = bf16_rne(acc[i].x * sc[i].x), b1 = bf16_rne(acc[i].y * sc[i].y);
-      const uint32_t b2 = bf16_rne(acc[i].z * sc[i].z), b3 = bf16_rne(acc[i].w * sc[i].w);
-      if (a.vec) {
-        *(uint2 *)(yr + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-      } else {
-        const uint32_t b[4] = {b0, b1, b2, b3};
-        for (int e = 0; e < 4 && n + e < a.N; ++e) yr[n + e] = (uint16_t)b[e];
-      }
-    }
-  }
-}
-
-// End of a skinny workgroup: the four waves' sums are added through LDS (`red`,
-// 4*RB*MB*4*64 floats) in wave order, so the result does not depend on timing;
-// wave v finishes blocks v, v+4, ...  One K slice: scale and bf16 store; several:
-// unscaled fp32 partials, which the column tile's last workgroup adds.
-template <int RB, int MB>
-__device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const SkinnyArgs &a, float *red, int n0,
-                                              int s, int wave, int lane) {
-  const int g = lane >> 4, lr = lane & 15;
-  __syncthreads();
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[(((wave * RB + rb) * MB + mb) * 4 + e) * 64 + lane] = acc[rb][mb][e];
-  __syncthreads();
-  const v4i rsrc_s = make_rsrc(a.scale, (uint32_t)a.N * 4u);
-  for (int b = wave; b < RB * MB; b += 4) {
-    const int rb = b / MB, mb = b % MB;
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float t = red[((b) * 4 + e) * 64 + lane];
-#pragma unroll
-      for (int o = 1; o < 4; ++o) t += red[((o * RB * MB + b) * 4 + e) * 64 + lane];
-      v[e] = t;
-    }
-    const int n = n0 + 16 * rb + 4 * g;
-    const int m = 16 * mb + lr;
-    if (m >= a.M) continue;
-    if (gridDim.y > 1) {
-      // all 16*RB columns of the tile are stored, also those past N (never read)
-      const v4i rsrc_p = make_rsrc(a.P + ((size_t)blockIdx.x * gridDim.y + s) * a.M * (16 * RB),
-                                   (uint32_t)(a.M * 16 * RB) * 4u);
-      llvm_buffer_store_v4f32(v4f{v[0], v[1], v[2], v[3]}, rsrc_p, (uint32_t)(m * 16 * RB + (n - n0)) * 4u, 0,
-                              kDeviceScope);
-    } else {
-      uint16_t *yr = a.y + (size_t)m * a.N;
-      uint32_t bits[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bits[e] = bf16_rne(v[e] * llvm_buffer_load_f32(rsrc_s, (uint32_t)(n + e) * 4u, 0, 0));
-      if (a.vec) {
-        if (n < a.N) *(uint2 *)(yr + n) = make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < a.N) yr[n + e] = (uint16_t)bits[e];
-      }
-    }
-  }
-  if (gridDim.y > 1) splitk_finish<RB>(a, n0, (int *)red);
-}
-
-template <int RB, int MB>
-__global__ __launch_bounds__(256, 1) void fp8g_splitk_partial_kernel(SkinnyArgs a) {
-  using S = SkinnyShape<RB, MB>;
-  constexpr int R = S::R, OPS = S::OPS, D = S::D, SLOT = S::SLOT, W_OPS = R / 8;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * S::WAVE_LDS];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int K = a.K;
-  const int n0 = blockIdx.x * R;
-  const int rows_w = min(R, a.N - n0);
-  const int s = blockIdx.y;
-  const int kbeg = s * a.k_slice;
-  const int kend = min(K, kbeg + a.k_slice);
-  const int nch = (kend - kbeg + 127) >> 7;
-  const int my = nch > wave ? (nch - wave + 3) >> 2 : 0;  // chunks of this wave
-
-  const v4i rsrc_w = make_rsrc(a.w + (size_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
-  const v4i rsrc_x = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)K);
-
-  // DMA instruction t moves rows 8t .. 8t+7 of a slot (w rows, then x rows).
-  uint32_t src_off[OPS], src_chunk[OPS];
-#pragma unroll
-  for (int t = 0; t < OPS; ++t) {
-    const int row = 8 * t + (lane >> 3);
-    const int r = t < W_OPS ? row : row - R;
-    const int c = (lane & 7) ^ swz16(r);
-    src_chunk[t] = (uint32_t)c * 16u;
-    src_off[t] = (uint32_t)r * (uint32_t)K + src_chunk[t];
-  }
-  const uint32_t ring_base =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem + (uint32_t)wave * S::WAVE_LDS;
-  uint8_t *ring = smem + wave * S::WAVE_LDS;
-
-  // Local chunk j (global chunk wave + 4j) -> slot j % D.
-  auto issue = [&](int j) __attribute__((always_inline)) {
-    const int kc = kbeg + ((wave + 4 * j) << 7);
-    const int slot = j % D;
-    if (kc + 128 <= kend) {
-#pragma unroll
-      for (int t = 0; t < OPS; ++t) {
-        const uint32_t lds = ring_base + (uint32_t)(slot * SLOT + t * 1024);
-        if (t < W_OPS) dma16_nt(rsrc_w, lds, src_off[t], (uint32_t)kc);
-        else dma16(rsrc_x, lds, src_off[t], (uint32_t)kc);
-      }
-    } else {
-      // the last chunk of K: bytes at or past K are zero
-#pragma unroll
-      for (int t = 0; t < OPS; ++t) {
-        const uint4 v = load16_masked(t < W_OPS ? rsrc_w : rsrc_x, src_off[t] + (uint32_t)kc,
-                                      kend - (kc + (int)src_chunk[t]), K);
-        *(uint4 *)(ring + slot * SLOT + t * 1024 + lane * 16) = v;
-      }
-    }
-  };
-
-  v4f acc[RB][MB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  const int g = lane >> 4, lr = lane & 15;
-  const int sw = swz16(lr);  // 16 rb and 16 mb leave the swizzle unchanged
-  const int c0 = (2 * g) ^ sw, c1 = (2 * g + 1) ^ sw;
-
-  for (int j = 0; j < D && j < my; ++j) issue(j);
-  for (int j = 0; j < my; ++j) {
-    const int ahead = min(D - 1, my - 1 - j);  // chunks issued after j
-    if (ahead >= 2) vm_wait_fence<2 * OPS>();
-    else if (ahead == 1) vm_wait_fence<OPS>();
-    else vm_wait_fence<0>();
-    const uint8_t *sl = ring + (j % D) * SLOT;
-    v8i af[RB], bf[MB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const uint8_t *row = sl + (16 * rb + lr) * 128;
-      const uint4 lo = *(const uint4 *)(row + (c0 << 4)), hi = *(const uint4 *)(row + (c1 << 4));
-      af[rb] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const uint8_t *row = sl + (R + 16 * mb + lr) * 128;
-      const uint4 lo = *(const uint4 *)(row + (c0 << 4)), hi = *(const uint4 *)(row + (c1 << 4));
-      bf[mb] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    if (j + D < my) {
-      lgkm_wait_fence();  // this slot's reads are done before it is refilled
-      issue(j + D);
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = mfma16(af[rb], bf[mb], acc[rb][mb]);
-  }
-
-  skinny_finish<RB, MB>(acc, a, (float *)smem, n0, s, wave, lane);
-}
-
-// Direct variant of the skinny kernel: no LDS in the K loop.  Every lane
-// loads its own MFMA operands from global memory straight into registers, so
-// neither w nor x passes through LDS and nothing but the final cross-wave sum
-// needs it.  For V_MFMA_F32_16X16X128_F8F6F4 lane l supplies row l % 16 of a
-// 16-row block and 32 bytes of K.  Any permutation of K inside one MFMA is
-// harmless as long as A and B use the same one, so lane l (r = l % 16,
-// g = l / 16) takes bytes [16g, 16g+16) and [64 + 16g, 64 + 16g + 16) of the
-// 128-byte chunk: the four lanes of a row then read 64 contiguous bytes per
-// load instruction.  Wave v takes chunks v, v+4, v+8, ... of the workgroup's K
-// slice and keeps D chunks in flight (register ring, loads issued D chunks
-// ahead of the MFMAs that use them); w is read with the non-temporal policy,
-// x (re-read by every workgroup, so best kept in L2) without.
-template <int RB, int MB, int D>
-__global__ __launch_bounds__(256, 1) void fp8g_skinny_direct_kernel(SkinnyArgs a) {
-  constexpr int NB = RB + MB;  // 16-row blocks per chunk: RB of w, then MB of x
-  __shared__ __attribute__((aligned(16))) float red[4 * RB * MB * 4 * 64];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int K = a.K;
-  const int n0 = blockIdx.x * 16 * RB;
-  const int rows_w = min(16 * RB, a.N - n0);
-  const int s = blockIdx.y;
-  const int kbeg = s * a.k_slice;
-  const int kend = min(K, kbeg + a.k_slice);
-  const int nch = (kend - kbeg + 127) >> 7;
-  const int my = nch > wave ? (nch - wave + 3) >> 2 : 0;  // chunks of this wave
-
-  const v4i rsrc_w = make_rsrc(a.w + (size_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
-  const v4i rsrc_x = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)K);
-  const int g = lane >> 4, r = lane & 15;
-  uint32_t off[NB];  // lane's row start + 16g, per block (rows past N or M read as zero)
-#pragma unroll
-  for (int b = 0; b < NB; ++b) off[b] = (uint32_t)(16 * (b < RB ? b : b - RB) + r) * (uint32_t)K + 16u * g;
-
-  // Only the slice's last chunk can end past kend; it belongs to wave
-  // (nch - 1) % 4 as its last chunk.  Its loads are issued before everything
-  // else and it is used last, so the main loop has no tail logic.
-  const bool has_tail = ((kend - kbeg) & 127) != 0 && ((nch - 1) & 3) == wave;
-  const int my_full = my - (has_tail ? 1 : 0);
-
-  // Chunk j of this wave into registers: bb[b][h] = 16 bytes at k = kc + 64h + 16g.
-  // Every load is issued unconditionally: a chunk past the wave's share is
-  // pointed 2^31 bytes past the buffer, beyond its range (rows * K < 2^31), so
-  // it reads zeros without touching memory and its MFMAs add nothing.  With no
-  // load under a branch the compiler can wait for exactly the chunk it needs
-  // (a conditional load would force it to wait for all of them).  The
-  // scheduling barriers keep the loads in chunk order.
-  auto load = [&](int j, v4i (&bb)[NB][2]) __attribute__((always_inline)) {
-    const uint32_t kc = j < my_full ? (uint32_t)(kbeg + ((wave + 4 * j) << 7)) : 0x80000000u;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        bb[b][h] = b < RB ? llvm_buffer_load_v4i32(rsrc_w, off[b] + 64u * h, kc, 2)
-                          : llvm_buffer_load_v4i32(rsrc_x, off[b] + 64u * h, kc, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  v4f acc[RB][MB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const v4i (&bb)[NB][2]) __attribute__((always_inline)) {
-    v8i op[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const v4i lo = bb[b][0], hi = bb[b][1];
-      op[b] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = mfma16(op[rb], op[RB + mb], acc[rb][mb]);
-  };
-
-  // Tail chunk: a piece with valid bytes 0 < v < 16 is loaded as the 16 bytes
-  // ending at its last valid byte (within its row, since K >= 16) and moved
-  // into place at the end; a piece with none is zeroed there.
-  v4i tail[NB][2];
-  int tvalid[2] = {0, 0};
-  if (has_tail) {
-    const int kc = kbeg + ((wave + 4 * my_full) << 7);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) tvalid[h] = kend - (kc + 64 * h + 16 * g);
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int v = tvalid[h];
-        const uint32_t o = off[b] + (uint32_t)(kc + 64 * h) + (uint32_t)(v >= 16 ? 0 : v > 0 ? v - 16 : 0);
-        tail[b][h] = llvm_buffer_load_v4i32(b < RB ? rsrc_w : rsrc_x, o, 0, b < RB ? 2 : 0);
-      }
-  }
-  // D chunks in flight: chunk j lives in slot j % D and is refilled with chunk
-  // j + D right after its MFMAs; the last round issues no refills.
-  v4i buf[D][NB][2];
-#pragma unroll
-  for (int d = 0; d < D; ++d) load(d, buf[d]);
-  const int rounds = (my_full + D - 1) / D;
-  for (int rd = 0; rd + 1 < rounds; ++rd) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      mma(buf[d]);
-      load(rd * D + d + D, buf[d]);
-    }
-  }
-#pragma unroll
-  for (int d = 0; d < D; ++d) mma(buf[d]);
-  if (has_tail) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int v = tvalid[h];
-        if (v >= 16) continue;
-        if (v <= 0) {
-          tail[b][h] = v4i{0, 0, 0, 0};
-          continue;
-        }
-        const int sh = 16 - v, q = sh >> 2, r8 = sh & 3;
-        const uint32_t d0 = (uint32_t)tail[b][h].x, d1 = (uint32_t)tail[b][h].y;
-        const uint32_t d2 = (uint32_t)tail[b][h].z, d3 = (uint32_t)tail[b][h].w;
-        const uint32_t e0 = q == 0 ? d0 : q == 1 ? d1 : q == 2 ? d2 : d3;
-        const uint32_t e1 = q == 0 ? d1 : q == 1 ? d2 : q == 2 ? d3 : 0u;
-        const uint32_t e2 = q == 0 ? d2 : q == 1 ? d3 : 0u;
-        const uint32_t e3 = q == 0 ? d3 : 0u;
-        tail[b][h] = v4i{(int)__builtin_amdgcn_alignbyte(e1, e0, r8), (int)__builtin_amdgcn_alignbyte(e2, e1, r8),
-                         (int)__builtin_amdgcn_alignbyte(e3, e2, r8), (int)__builtin_amdgcn_alignbyte(0u, e3, r8)};
-      }
-    mma(tail);
-  }
-  skinny_finish<RB, MB>(acc, a, red, n0, s, wave, lane);
-}
 
 __global__ __launch_bounds__(256) void fp8g_zero_kernel(uint16_t *__restrict__ y, int64_t count) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = 0;
+}
+
+// K = 0 with a bias or an activation: the empty sum is +0, so
+// y[m, n] = bf16(act(bias[n])) (bias 0 when absent); grid-stride over y.
+__global__ __launch_bounds__(256) void fp8g_empty_k_kernel(uint16_t *__restrict__ y, const float *__restrict__ bias,
+                                                           int act, int64_t N, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x) {
+    const float z = bias ? bias[i % N] : 0.0f;
+    y[i] = (uint16_t)bf16_rne(activation_rt(z, act));
+  }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -1461,85 +93,15 @@ int skinny_max_row_blocks(int M, bool direct) {
 }
 int skinny_chunk_bytes() { return 128; }
 
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool PP = false>
-static hipError_t launch_main_cfg(const MainLaunch &l, hipStream_t stream) {
-  MainArgs a{l.x, l.w, l.scale, l.y, l.M, l.N, l.K, l.tiles_m, l.tiles_n, l.group_m, l.ystore};
-  const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(WM * WN * 64);
-  if (l.k_tail) fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, true, PP><<<grid, block, 0, stream>>>(a);
-  else fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, false, PP><<<grid, block, 0, stream>>>(a);
-  return hipGetLastError();
-}
-
-static hipError_t launch_main5(const MainLaunch &l, hipStream_t stream) {
-  MainArgs a{l.x, l.w, l.scale, l.y, l.M, l.N, l.K, l.tiles_m, l.tiles_n, l.group_m, l.ystore};
-  const bool sk = l.variant == 16;
-  if (sk) {
-    a.n_dp = l.n_dp;
-    a.n_sk = l.n_sk;
-    a.P = l.partials;
-    a.tickets = l.tickets;
-    a.epoch = l.epoch;
-  }
-  const dim3 grid((unsigned)(sk ? l.n_dp + l.n_sk : l.tiles_m * l.tiles_n)), block(512);
-  if (sk) {
-    if (l.k_tail) fp8g_main5_kernel<true, true><<<grid, block, 0, stream>>>(a);
-    else fp8g_main5_kernel<false, true><<<grid, block, 0, stream>>>(a);
-  } else {
-    if (l.k_tail) fp8g_main5_kernel<true, false><<<grid, block, 0, stream>>>(a);
-    else fp8g_main5_kernel<false, false><<<grid, block, 0, stream>>>(a);
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
   switch (l.variant) {
-    case 1: return launch_main_cfg<256, 256, 64, 4, 4, 2>(l, stream);
-    case 2: return launch_main_cfg<128, 128, 64, 4, 2, 2>(l, stream);
-    case 3: return launch_main_cfg<64, 64, 128, 3, 2, 2>(l, stream);
-    case 4: return launch_main_cfg<256, 256, 64, 4, 2, 4>(l, stream);
-    case 5: return launch_main_cfg<256, 256, 64, 4, 2, 2>(l, stream);
-    case 6: return launch_main_cfg<256, 256, 128, 2, 4, 2>(l, stream);
-    case 7: return launch_main_cfg<256, 256, 128, 2, 2, 4>(l, stream);
-    case 9: return launch_main_cfg<256, 256, 64, 4, 4, 2, true>(l, stream);
-    case 10: return launch_main5(l, stream);
+    case 10:
     case 16: return launch_main5(l, stream);
-    case 17: return launch_main_cfg<128, 256, 128, 3, 2, 4>(l, stream);
-    case 18: return launch_main_cfg<128, 128, 128, 4, 2, 4>(l, stream);
-    default: return hipErrorInvalidValue;
+    case 3:
+    case 17:
+    case 18: return launch_main_tiles(l, stream);
+    default: return launch_main_legacy(l, stream);
   }
-}
-
-template <int RB, int MB, bool DIRECT>
-static hipError_t launch_skinny_cfg(const SkinnyLaunch &l, hipStream_t stream) {
-  SkinnyArgs a{l.x, l.w, l.scale, l.y, l.partials, l.tickets, l.epoch, l.M, l.N, l.K, l.k_slice, l.vec};
-  const dim3 grid((unsigned)((l.N + 16 * RB - 1) / (16 * RB)), (unsigned)l.S), block(256);
-  if constexpr (DIRECT) fp8g_skinny_direct_kernel<RB, MB, 4><<<grid, block, 0, stream>>>(a);
-  else fp8g_splitk_partial_kernel<RB, MB><<<grid, block, 0, stream>>>(a);
-  return hipGetLastError();
-}
-
-template <int MB>
-static hipError_t launch_skinny_mb(const SkinnyLaunch &l, hipStream_t stream) {
-  switch (l.variant) {
-    case 1: return launch_skinny_cfg<1, MB, false>(l, stream);
-    case 2: return launch_skinny_cfg<2, MB, false>(l, stream);
-    case 3: if constexpr (MB <= 2) return launch_skinny_cfg<3, MB, false>(l, stream); else break;
-    case 4: if constexpr (MB <= 2) return launch_skinny_cfg<4, MB, false>(l, stream); else break;
-    case 5: if constexpr (MB == 1) return launch_skinny_cfg<5, MB, false>(l, stream); else break;
-    case 11: return launch_skinny_cfg<1, MB, true>(l, stream);
-    case 12: return launch_skinny_cfg<2, MB, true>(l, stream);
-    case 13: return launch_skinny_cfg<3, MB, true>(l, stream);
-    case 14: return launch_skinny_cfg<4, MB, true>(l, stream);
-    case 15: return launch_skinny_cfg<5, MB, true>(l, stream);
-    default: break;
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_skinny(const SkinnyLaunch &l, hipStream_t stream) {
-  if (l.M <= 16) return launch_skinny_mb<1>(l, stream);
-  if (l.M <= 32) return launch_skinny_mb<2>(l, stream);
-  return launch_skinny_mb<4>(l, stream);
 }
 
 hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream) {
@@ -1547,6 +109,15 @@ hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream) {
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   fp8g_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(y, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_empty_k(uint16_t *y, const float *bias, int act, int64_t M, int64_t N, hipStream_t stream) {
+  const int64_t count = M * N;
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  fp8g_empty_k_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(y, bias, act, N, count);
   return hipGetLastError();
 }
 

@@ -1,0 +1,9 @@
+// fp8g_launch_skinny_epi.hip -- the split-K kernels with the general epilogue
+// (bias, activation), and the direct-to-register variants 11-15.
+#include "fp8g_kernels.hpp"
+
+namespace fp8g {
+
+hipError_t launch_skinny_epi(const SkinnyLaunch &l, hipStream_t stream) { return launch_skinny_t<true>(l, stream); }
+
+}  // namespace fp8g

@@ -131,6 +131,50 @@ int fp8_gemm_plan(int64_t M, int64_t N, int64_t K, fp8g_plan *out);
 int fp8_gemm_plan_ex(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant,
                      int32_t split_k, fp8g_plan *out);
 
+/* ------------------------------------------------- epilogue and formats ----
+ * The same operation with a per-column bias, an elementwise activation and a
+ * choice of FP8 format for each operand:
+ *
+ *     y[m,n] = bf16_rne( act( (sum_k dec_x(x[m,k]) * dec_w(w[n,k])) * scale[n]
+ *                             + bias[n] ) )
+ *
+ * Sources on the pages: the per-output-channel scale is applied by the
+ * per-column linear-combination + per-column bias + elementwise-activation
+ * epilogue kind ("DeepSeek V4 Flash (0731)", CUTLASS 3.x SM90 fp8 GEMM cell);
+ * the f8f6f4 matrix-core kind takes either FP8 format ("Claude Fable 5",
+ * tcgen05 fp8 GEMM cell).  Formats: E4M3 as above; E5M2 is the OCP FP8 E5M2
+ * format (bias 15, largest finite 57344, with infinities and NaN).  The sum
+ * is accumulated in fp32 by the matrix cores; scale, bias and activation are
+ * applied in fp32 in that order.  Activations: ReLU max(z, 0); SiLU
+ * z / (1 + e^-z); GELU in its tanh form 0.5 z (1 + tanh(sqrt(2/pi) (z +
+ * 0.044715 z^3))); each takes its limit at +-inf and keeps NaN. */
+#define FP8G_FMT_E4M3 0
+#define FP8G_FMT_E5M2 1
+
+#define FP8G_ACT_NONE 0
+#define FP8G_ACT_RELU 1
+#define FP8G_ACT_SILU 2
+#define FP8G_ACT_GELU_TANH 3
+
+/*   bias     : device pointer to N fp32 values, 4-byte aligned, or NULL (no
+ *              bias); must not overlap y.
+ *   x_format, w_format : FP8G_FMT_E4M3 or FP8G_FMT_E5M2.
+ *   activation         : FP8G_ACT_*.
+ * Other arguments, ownership, errors and threading as fp8_gemm_scaled.  With
+ * K == 0 the sum is +0 and y = bf16(act(bias)) (+0 without a bias). */
+int fp8_gemm_scaled_act(const void *x, const void *w, const float *scale, const float *bias, void *y,
+                        int64_t M, int64_t N, int64_t K, int32_t x_format, int32_t w_format,
+                        int32_t activation, void *stream);
+
+/* With forced plan parts as fp8_gemm_scaled_ex.  Operands other than E4M3 x
+ * E4M3 are built for main variants 3, 10, 17, 18 and split-K variants 1-5
+ * (everything the planner chooses); other forced variants give
+ * FP8G_ERR_INVALID_ARG.  Bias and activation work with every variant. */
+int fp8_gemm_scaled_act_ex(const void *x, const void *w, const float *scale, const float *bias, void *y,
+                           int64_t M, int64_t N, int64_t K, int32_t x_format, int32_t w_format,
+                           int32_t activation, int32_t path, int32_t variant, int32_t split_k,
+                           void *stream);
+
 /* Static description of a status code. */
 const char *fp8_gemm_strerror(int status);
 

@@ -12,6 +12,10 @@ mode, so these are readings; each is stated in the design doc):
     which rounds to nearest, ties to even.  Clamping first makes the cast
     saturating.  sigma = 1 is the default workload.
   * scale[N]: U[0.005, 0.02] fp32 drawn after w from the same generator.
+  * E5M2 operands (``fp8_inputs_fmt``): the same draws clamped to +-57344 and
+    cast to ``float8_e5m2`` (round to nearest, ties to even).
+  * bias[N] (``bias_values``): U[-0.5, 0.5] fp32 from its own generator, about
+    the spread of the scaled sums at K = 4096, so activations see both signs.
 The same host bytes feed the oracle and, copied to device memory, the GPU path.
 """
 from __future__ import annotations
@@ -67,6 +71,33 @@ def fp8_inputs(M: int, N: int, K: int, seed: int = 42, sigma: float = 1.0,
     w = quantize_e4m3(torch.randn(N, K, generator=g) * sigma)
     scale = (scale_lo + (scale_hi - scale_lo) * torch.rand(N, generator=g)).numpy().astype(np.float32)
     return x, w, scale
+
+
+E5M2_MAX = 57344.0
+FMT_E4M3, FMT_E5M2 = 0, 1
+
+
+def quantize_e5m2(values: torch.Tensor) -> np.ndarray:
+    """Saturating round-to-nearest-even fp32 -> E5M2 codes (uint8 numpy array)."""
+    v = values.to(torch.float32).clamp(-E5M2_MAX, E5M2_MAX)
+    return v.to(torch.float8_e5m2).view(torch.uint8).numpy().copy()
+
+
+def fp8_inputs_fmt(M: int, N: int, K: int, x_format: int, w_format: int, seed: int = 42, sigma: float = 1.0,
+                   scale_lo: float = 0.005, scale_hi: float = 0.02):
+    """As fp8_inputs, with each operand quantised to its format (FMT_E4M3 / FMT_E5M2)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = {FMT_E4M3: quantize_e4m3, FMT_E5M2: quantize_e5m2}
+    x = q[x_format](torch.randn(M, K, generator=g) * sigma)
+    w = q[w_format](torch.randn(N, K, generator=g) * sigma)
+    scale = (scale_lo + (scale_hi - scale_lo) * torch.rand(N, generator=g)).numpy().astype(np.float32)
+    return x, w, scale
+
+
+def bias_values(N: int, seed: int, lo: float = -0.5, hi: float = 0.5) -> np.ndarray:
+    """Seeded per-column bias, U[lo, hi] fp32."""
+    g = torch.Generator(device="cpu").manual_seed(seed + 7919)
+    return (lo + (hi - lo) * torch.rand(N, generator=g)).numpy().astype(np.float32)
 
 
 def random_codes(shape, seed: int, allow_nan: bool = False) -> np.ndarray:
