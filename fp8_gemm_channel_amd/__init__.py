@@ -51,7 +51,7 @@ class Plan(ctypes.Structure):
                 ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("k_slice", ctypes.c_int64), ("group_m", ctypes.c_int32), ("k_tail", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("dp_tiles", ctypes.c_int32), ("sk_groups", ctypes.c_int32)]
+                ("dp_tiles", ctypes.c_int32), ("sk_groups", ctypes.c_int32), ("pad_k", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         d = {name: getattr(self, name) for name, _ in self._fields_}

@@ -16,6 +16,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "fp8g.h"
@@ -53,6 +54,45 @@ int fail(int status, const char *fmt, ...) {
 
 int hip_fail(hipError_t e, const char *what) {
   return fail(FP8G_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+// Workspace memory (split-K partials and tickets, padded rows, stream-K
+// partials): stream-ordered allocations from one memory pool per device that
+// keeps freed blocks for reuse (release threshold unlimited).  With a pool that
+// returns memory at every synchronisation, each call mapped fresh pages: a
+// 34 MB workspace measured ~25 us of extra call time.  Created on first use.
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mutex;
+hipMemPool_t g_pools[kMaxDevices] = {};
+
+hipError_t workspace_alloc(void **ptr, size_t bytes, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  hipMemPool_t pool;
+  {
+    std::lock_guard<std::mutex> lock(g_pool_mutex);
+    if (!g_pools[dev]) {
+      hipMemPoolProps props;
+      memset(&props, 0, sizeof props);
+      props.allocType = hipMemAllocationTypePinned;
+      props.location.type = hipMemLocationTypeDevice;
+      props.location.id = dev;
+      hipMemPool_t created;
+      e = hipMemPoolCreate(&created, &props);
+      if (e != hipSuccess) return e;
+      uint64_t keep = UINT64_MAX;
+      e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep);
+      if (e != hipSuccess) {
+        hipMemPoolDestroy(created);
+        return e;
+      }
+      g_pools[dev] = created;
+    }
+    pool = g_pools[dev];
+  }
+  return hipMallocFromPoolAsync(ptr, bytes, pool, stream);
 }
 
 constexpr int kNumCUs = 256;          // MI355X compute units
@@ -195,8 +235,8 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     return FP8G_OK;
   }
   if (variant == 0) variant = auto_main_variant(M, N, K);
-  if (split_k > 1 && variant != 16)
-    return fail(FP8G_ERR_INVALID_ARG, "split_k applies to the split-K path and to main variant 16 only");
+  if (split_k > 2 && variant != 16)
+    return fail(FP8G_ERR_INVALID_ARG, "main variant %d takes split_k 0..2 (row realignment choice)", variant);
 
   const fp8g::MainConfig *c = fp8g::main_config(variant);
   if (!c) return fail(FP8G_ERR_INVALID_ARG, "unknown main variant %d", variant);
@@ -208,7 +248,35 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
   p->tile_n = c->bn;
   p->tile_k = c->bk;
   p->group_m = (int32_t)(tiles_m < 8 ? tiles_m : 8);
-  p->k_tail = (K % c->bk) != 0;
+  // Rows whose length is not a multiple of 128 bytes start off the cache-line
+  // grid, and every 128-byte K chunk the kernels stage then spans two lines.
+  // Measured on MI355X (4096 x 4096, cold): K = 4096 or 4224 63.7 us, 4160
+  // (rows at 64-byte offsets) 73.4, 4112 / 4128 (16 / 32) ~83, 4127 (any
+  // byte) 94.  Copying x and w once into rows zero-padded to a multiple of 128
+  // bytes costs one read and one write of the operands and gives the same
+  // sums (zero bytes add nothing, and the K steps stay in order).  Measured
+  // (in place -> copied): 4096^2 x 4127 96 -> 84 us, 8192^2 x 8191 664 -> 521,
+  // 3072^2 x 3073 72 -> 60, 512 x 8192 x 8193 91 -> 76, 1024 x 4096 x 4100
+  // 42.7 -> 40.7; but 2048^2 x 2049 27 -> 31 and 1024^2 x 1025 11 -> 18, where
+  // the copy's fixed cost (launch, a latency-bound small copy) dominates.  So
+  // copy for GEMMs of at least 30 GFLOP with at least 512 flops per operand
+  // byte copied (2 M N / (M + N)).  split_k (not variant 16) forces the
+  // choice: 1 = read rows in place, 2 = copy.
+  int64_t kk = K;
+  if (K % 128 != 0) {
+    const int64_t kp = cdiv(K, 128) * 128;
+    // (the copy must also stay a modest workspace: at most 4 GiB)
+    const bool fits = (M + N) * kp <= (int64_t(4) << 30);
+    const double flops = 2.0 * (double)M * (double)N * (double)K;
+    const bool pad_auto = fits && flops >= 3e10 && 2.0 * (double)M * (double)N / (double)(M + N) >= 512.0;
+    const bool pad = variant == 16 ? pad_auto : ((split_k == 2 && fits) || (split_k == 0 && pad_auto));
+    if (pad) {
+      kk = kp;
+      p->pad_k = (int32_t)kk;
+      p->workspace_bytes = (M + N) * kk;
+    }
+  }
+  p->k_tail = (kk % c->bk) != 0;
   p->grid = tiles_m * tiles_n;
   p->dp_tiles = (int32_t)(tiles_m * tiles_n);
   if (variant == 16) {
@@ -217,7 +285,7 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     // splits the (tile, K step) units of those tiles evenly, so every compute
     // unit gets between one and two tiles' worth (less than one when the tiles
     // do not fill a wave).  split_k forces the number of stream-K workgroups.
-    const int64_t T = tiles_m * tiles_n, nk = cdiv(K, c->bk);
+    const int64_t T = tiles_m * tiles_n, nk = cdiv(kk, c->bk);
     const int64_t n_dp = T > kNumCUs ? (T / kNumCUs - 1) * kNumCUs : 0;
     if (T * nk >= INT32_MAX) return fail(FP8G_ERR_UNSUPPORTED, "stream-K needs tiles x K steps below 2^31");
     int64_t n_sk = split_k > 0 ? split_k : kNumCUs;
@@ -225,7 +293,7 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     p->dp_tiles = (int32_t)n_dp;
     p->sk_groups = (int32_t)n_sk;
     p->grid = n_dp + n_sk;
-    p->workspace_bytes = splitk_ticket_bytes(T - n_dp) + 2 * n_sk * fp8g::kMainPartialBytes;
+    p->workspace_bytes += splitk_ticket_bytes(T - n_dp) + 2 * n_sk * fp8g::kMainPartialBytes;
   }
   return FP8G_OK;
 }
@@ -291,23 +359,35 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
     l.act = act;
     l.fmt = fmt;
     void *ws = nullptr;
-    if (p.sk_groups > 0) {
-      // tickets for the stream-K tiles, then two partial tiles per stream-K
-      // workgroup; uninitialized (tickets carry the call id, partials are
-      // written before they are read)
-      e = hipMallocAsync(&ws, (size_t)p.workspace_bytes, stream);
-      if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(stream-K workspace)");
+    if (p.workspace_bytes > 0) {
+      // [padded x rows | padded w rows] (pad plan), then, for stream-K, the
+      // tickets of the stream-K tiles and two partial tiles per stream-K
+      // workgroup; uninitialized (the pad kernel writes every padded byte,
+      // tickets carry the call id, partials are written before they are read)
+      e = workspace_alloc(&ws, (size_t)p.workspace_bytes, stream);
+      if (e != hipSuccess) return hip_fail(e, "workspace allocation (main path)");
+    }
+    char *wsp = (char *)ws;
+    if (p.pad_k > 0) {
+      uint8_t *xp = (uint8_t *)wsp, *wp = xp + (size_t)M * (size_t)p.pad_k;
+      e = fp8g::launch_pad_rows((const uint8_t *)x, (const uint8_t *)w, xp, M, N, K, p.pad_k, stream);
+      l.x = xp;
+      l.w = wp;
+      l.K = p.pad_k;
+      wsp += (size_t)(M + N) * (size_t)p.pad_k;
+    }
+    if (e == hipSuccess && p.sk_groups > 0) {
       const int64_t sk_tiles = cdiv(M, p.tile_m) * cdiv(N, p.tile_n) - p.dp_tiles;
       l.n_dp = p.dp_tiles;
       l.n_sk = p.sk_groups;
-      l.tickets = (unsigned long long *)ws;
-      l.partials = (float *)((char *)ws + splitk_ticket_bytes(sk_tiles));
+      l.tickets = (unsigned long long *)wsp;
+      l.partials = (float *)(wsp + splitk_ticket_bytes(sk_tiles));
       l.epoch = call_id();
     }
-    e = fp8g::launch_main(l, stream);
+    if (e == hipSuccess) e = fp8g::launch_main(l, stream);
     if (ws) {
       hipError_t f = hipFreeAsync(ws, stream);
-      if (e == hipSuccess && f != hipSuccess) return hip_fail(f, "hipFreeAsync(stream-K workspace)");
+      if (e == hipSuccess && f != hipSuccess) return hip_fail(f, "hipFreeAsync(main-path workspace)");
     }
     return e == hipSuccess ? FP8G_OK : hip_fail(e, "main kernel launch");
   }
@@ -316,8 +396,8 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
   float *partials = nullptr;
   unsigned long long *tickets = nullptr;
   if (p.split_k > 1) {
-    e = hipMallocAsync(&ws, (size_t)p.workspace_bytes, stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(split-K workspace)");
+    e = workspace_alloc(&ws, (size_t)p.workspace_bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "workspace allocation (split-K)");
     // The workspace is not initialized: a ticket carries the call id, so stale
     // values are harmless, and every partial is written before it is read.
     tickets = (unsigned long long *)ws;

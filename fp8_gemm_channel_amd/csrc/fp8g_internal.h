@@ -77,6 +77,10 @@ hipError_t launch_main_legacy(const MainLaunch &l, hipStream_t stream);      // 
 hipError_t launch_skinny_epi(const SkinnyLaunch &l, hipStream_t stream);     // bias / activation, variants 11-15
 hipError_t launch_skinny(const SkinnyLaunch &l, hipStream_t stream);
 hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream);
+// Copies x [M, K] and w [N, K] (rows at any byte alignment) into dst as
+// [M + N, K16] rows, bytes K .. K16-1 zero (K16: K rounded up to a multiple of 16).
+hipError_t launch_pad_rows(const uint8_t *x, const uint8_t *w, uint8_t *dst, int64_t M, int64_t N, int64_t K,
+                           int64_t K16, hipStream_t stream);
 // K = 0 with a bias or an activation: y[m, n] = bf16(act(bias[n])).
 hipError_t launch_empty_k(uint16_t *y, const float *bias, int act, int64_t M, int64_t N, hipStream_t stream);
 

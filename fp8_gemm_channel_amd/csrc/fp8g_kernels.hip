@@ -46,6 +46,30 @@ __global__ __launch_bounds__(256) void fp8g_zero_kernel(uint16_t *__restrict__ y
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = 0;
 }
 
+// Row realignment (rows of K bytes whose starts are not 128-byte aligned): one
+// wave per row (x rows, then w rows), lane l copying 16-byte chunks l, l + 64,
+// ...; the source row is one buffer of K bytes (so the descriptor is uniform),
+// bytes at or past K read zero and the chunk that straddles K is rebuilt by a
+// shifted load.  Sources are read once (non-temporal); the padded rows are
+// written with ordinary aligned 16-byte stores, since the GEMM reads them next.
+__global__ __launch_bounds__(256) void fp8g_pad_rows_kernel(const uint8_t *__restrict__ x,
+                                                            const uint8_t *__restrict__ w, uint8_t *__restrict__ dst,
+                                                            int64_t rows, int64_t M, int K, int Kp) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const uint8_t *src = row < M ? x + row * K : w + (row - M) * K;
+  const v4i rsrc = make_rsrc(src, (uint32_t)K);
+  uint4 *out = (uint4 *)(dst + row * Kp);
+  for (int c = lane; c < Kp / 16; c += 64) {
+    const int valid = K - 16 * c;
+    uint4 v;
+    if (valid >= 16) v = as_u4(llvm_buffer_load_v4i32(rsrc, (uint32_t)c * 16u, 0, 2));
+    else v = load16_masked(rsrc, (uint32_t)c * 16u, valid, K);
+    out[c] = v;
+  }
+}
+
 // K = 0 with a bias or an activation: the empty sum is +0, so
 // y[m, n] = bf16(act(bias[n])) (bias 0 when absent); grid-stride over y.
 __global__ __launch_bounds__(256) void fp8g_empty_k_kernel(uint16_t *__restrict__ y, const float *__restrict__ bias,
@@ -109,6 +133,15 @@ hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream) {
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   fp8g_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(y, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_rows(const uint8_t *x, const uint8_t *w, uint8_t *dst, int64_t M, int64_t N, int64_t K,
+                           int64_t K16, hipStream_t stream) {
+  const int64_t rows = M + N;
+  if (rows <= 0) return hipSuccess;
+  fp8g_pad_rows_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(x, w, dst, rows, M, (int)K,
+                                                                                   (int)K16);
   return hipGetLastError();
 }
 

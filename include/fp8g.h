@@ -29,12 +29,17 @@
  *     the same launch, by the last workgroup to finish each column tile.
  *   - K need not be a multiple of any tile size: the pages zero-pad copies of
  *     the operands ("Kimi K3 (256k)", SM100 persistent-TMA Triton cell: zero
- *     bytes add nothing to the dot); this library masks the K tail inside the
- *     kernel instead and never copies an operand.
+ *     bytes add nothing to the dot).  This library masks the K tail inside the
+ *     kernel; for K % 128 != 0 on large main-path calls it also copies x and
+ *     w, on every call, into rows padded to 128 bytes (cache-line-aligned rows
+ *     stream much faster), see fp8g_plan.pad_k.  Nothing is cached between
+ *     calls.
  *
  * Ownership and threading: the caller owns every buffer.  The library keeps no
  * data between calls; its only globals are a thread-local copy of the last
- * error message and an atomic call counter (ids for split-K tickets).  Calls are asynchronous: they enqueue kernels on
+ * error message, an atomic call counter (ids for split-K tickets) and one
+ * memory pool per device for call workspaces (created on first use; freed
+ * workspace memory stays in the pool for reuse until the process ends).  Calls are asynchronous: they enqueue kernels on
  * `stream` (a hipStream_t; NULL is the default stream) and return without
  * synchronising.  Buffers must stay valid until that work has finished.
  */
@@ -87,6 +92,11 @@ typedef struct fp8g_plan {
                                each (all tiles unless stream-K) */
     int32_t sk_groups;      /* main path variant 16: stream-K workgroups that
                                share the remaining tiles; 0 otherwise */
+    int32_t pad_k;          /* main path, K % 128 != 0: x and w are first
+                               copied into rows of pad_k = K rounded up to 128
+                               bytes (zero-filled; part of the workspace) so
+                               that the kernel reads cache-line-aligned rows;
+                               0 otherwise */
 } fp8g_plan;
 
 /* y = bf16_rne((x . w^T) * scale), as defined above.
@@ -98,9 +108,9 @@ typedef struct fp8g_plan {
  *   stream         : hipStream_t, or NULL for the default stream.
  * Returns FP8G_OK, FP8G_ERR_INVALID_ARG (bad sizes, null pointers with non-zero
  * extent, misaligned scale/y, overlapping output), or FP8G_ERR_HIP (no device,
- * launch failure, or failure to allocate the split-K workspace; that is
- * allocated stream-ordered with hipMallocAsync and freed with hipFreeAsync on
- * `stream` inside the call, so calls on different streams never share it). */
+ * launch failure, or failure to allocate the call's workspace; that is
+ * allocated stream-ordered from the library's pool and freed with hipFreeAsync
+ * on `stream` inside the call, so calls on different streams never share it). */
 int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y,
                     int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -116,7 +126,8 @@ int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y,
  *             workgroup through an LDS ring (default kernel), 11-15 = the
  *             same row counts loading straight into registers (K >= 16).
  *   split_k : splitk path: 1..64 K slices; main path variant 16: 1..2048
- *             stream-K workgroups; other main variants: 0 or 1
+ *             stream-K workgroups; other main variants, for K % 128 != 0:
+ *             1 = read operand rows in place, 2 = realign them (pad_k)
  * Invalid overrides give FP8G_ERR_INVALID_ARG.  The result is the same
  * operation to within fp32 summation order. */
 int fp8_gemm_scaled_ex(const void *x, const void *w, const float *scale, void *y,

@@ -54,11 +54,12 @@ def test_plan_of_benchmark_shapes(wl):
     else:
         assert p["path_name"] == "main"
         assert p["grid"] == -(-wl.M // p["tile_m"]) * -(-wl.N // p["tile_n"])
-        assert p["k_tail"] == (wl.K % p["tile_k"] != 0)
+        kk = p["pad_k"] or wl.K  # the kernel's K (rows realigned into pad_k bytes)
+        assert p["k_tail"] == (kk % p["tile_k"] != 0)
     if wl.M >= 4096:
         assert (p["tile_m"], p["tile_n"]) == (256, 256) and p["grid"] >= 256
     if wl.name == "odd-k-4127":
-        assert p["k_tail"] == 1
+        assert p["pad_k"] == 4224 and p["k_tail"] == 0
 
 
 def test_plan_special_extents():
@@ -91,9 +92,25 @@ def test_plan_rejects_bad_dims(args):
     assert e.value.status == fg.FP8G_ERR_INVALID_ARG
 
 
+def test_plan_row_realignment():
+    """K % 16 != 0: large main-path calls copy x and w into 16-byte rows first."""
+    p = fg.fp8_gemm_plan(4096, 4096, 4127)
+    assert p["pad_k"] == 4224 and p["workspace_bytes"] == 8192 * 4224 and p["k_tail"] == 0
+    assert fg.fp8_gemm_plan(4096, 4096, 4112)["pad_k"] == 4224    # 16-byte rows still straddle lines
+    assert fg.fp8_gemm_plan(4096, 4096, 4096)["pad_k"] == 0       # aligned rows
+    assert fg.fp8_gemm_plan(256, 256, 257)["pad_k"] == 0           # copy not worth it
+    assert fg.fp8_gemm_plan(2048, 2048, 2049)["pad_k"] == 0        # (measured slower)
+    assert fg.fp8_gemm_plan(32, 12288, 4127)["pad_k"] == 0         # split-K path reads in place
+    forced = fg.fp8_gemm_plan_ex(256, 256, 257, fg.PATH_MAIN, 0, 2)
+    assert forced["pad_k"] == 384 and forced["workspace_bytes"] == 512 * 384
+    assert fg.fp8_gemm_plan_ex(4096, 4096, 4127, fg.PATH_MAIN, 0, 1)["pad_k"] == 0
+    sk = fg.fp8_gemm_plan_ex(4096, 4352, 4127, fg.PATH_MAIN, 16, 0)
+    assert sk["pad_k"] == 4224 and sk["workspace_bytes"] > (4096 + 4352) * 4224
+
+
 @pytest.mark.parametrize("kw", [
     dict(path=7), dict(path=fg.PATH_SPLITK, M=65), dict(variant=99), dict(split_k=65),
-    dict(split_k=-1), dict(path=fg.PATH_MAIN, split_k=2), dict(path=fg.PATH_SPLITK, variant=9),
+    dict(split_k=-1), dict(path=fg.PATH_MAIN, split_k=3), dict(path=fg.PATH_SPLITK, variant=9),
 ])
 def test_plan_rejects_bad_overrides(kw):
     M = kw.pop("M", 32)

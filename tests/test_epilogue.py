@@ -154,3 +154,17 @@ def test_benchmark_shapes_sampled(name, fmts, act):
     mi, ni = synth.sample_positions(wl.M, wl.N, 4000, seed=3)
     ref = oracle.gemm_epilogue_at(x, w, s, mi, ni, b, act, *fmts)
     compare(got[mi, ni], ref, f"{name} sampled")
+
+
+@pytest.mark.parametrize("fmts", FORMATS, ids=lambda f: f"x{f[0]}w{f[1]}")
+@pytest.mark.parametrize("act", ACTS)
+def test_realigned_rows_epilogue_sampled(fmts, act):
+    """Odd K large enough that the plan copies the rows into 128-byte rows first."""
+    M, N, K = 2304, 2560, 3001
+    assert fg.fp8_gemm_plan(M, N, K)["pad_k"] == 3072
+    x, w, s = synth.fp8_inputs_fmt(M, N, K, *fmts, seed=13)
+    b = synth.bias_values(N, 13)
+    say(f"realigned epilogue fmts={fmts} act={act}")
+    got = run_epi(x, w, s, b, act, *fmts)
+    mi, ni = synth.sample_positions(M, N, 3000, seed=5)
+    compare(got[mi, ni], oracle.gemm_epilogue_at(x, w, s, mi, ni, b, act, *fmts), "realigned sampled")

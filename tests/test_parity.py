@@ -153,3 +153,42 @@ def test_benchmark_shape_other_seeds(name, seed):
         compare(got, oracle.gemm_scaled(x, w, s), name)
     else:
         _sampled(x, w, s, got, seed=seed, edges=(0, 255, 256, wl.M - 1))
+
+
+# ------------------------------------- odd K: operand rows realigned first ----
+@pytest.mark.parametrize("variant", [2, 3, 10, 17, 18])
+@pytest.mark.parametrize("shape", [(300, 520, 4127), (70, 300, 1), (40, 33, 17), (256, 256, 257), (129, 300, 1003)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_row_realignment_matches_in_place(variant, shape):
+    """split_k = 2 copies x and w into zero-padded 128-byte rows before the
+    kernel; the sums are the same as reading the rows in place (split_k = 1),
+    bit for bit, and both match the oracle."""
+    M, N, K = shape
+    x, w, s = synth.fp8_inputs(M, N, K, seed=9)
+    say(f"realign {shape} variant {variant}")
+    padded = run(x, w, s, path=fg.PATH_MAIN, variant=variant, split_k=2)
+    in_place = run(x, w, s, path=fg.PATH_MAIN, variant=variant, split_k=1)
+    compare(padded, oracle.gemm_scaled(x, w, s), f"{shape} v{variant} padded")
+    assert np.array_equal(padded, in_place), "padded rows changed the sums"
+
+
+def test_row_realignment_unaligned_pointers():
+    """Operand pointers at odd byte addresses with an odd K, default plan (pads)."""
+    import torch
+    M, N, K = 2304, 2560, 3001
+    x, w, s = synth.fp8_inputs(M, N, K, seed=10)
+    assert fg.fp8_gemm_plan(M, N, K)["pad_k"] == 3072
+    xb = torch.zeros(M * K + 3, dtype=torch.uint8, device="cuda")
+    wb = torch.zeros(N * K + 5, dtype=torch.uint8, device="cuda")
+    xb[3:].copy_(torch.from_numpy(x.reshape(-1)))
+    wb[5:].copy_(torch.from_numpy(w.reshape(-1)))
+    sd = torch.from_numpy(s).cuda()
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    say("realign with unaligned operand pointers")
+    st = fg.fp8_gemm_scaled(xb.data_ptr() + 3, wb.data_ptr() + 5, sd.data_ptr(), y.data_ptr(), M, N, K,
+                            torch.cuda.current_stream().cuda_stream)
+    assert st == fg.FP8G_OK, fg.fp8_gemm_last_error()
+    torch.cuda.synchronize()
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    mi, ni = synth.sample_positions(M, N, 4000, seed=11)
+    compare(got[mi, ni], oracle.gemm_scaled_at(x, w, s, mi, ni), "unaligned + realigned")
