@@ -30,7 +30,7 @@ thread_local std::string g_last_error;
 // like this call's: ids are a counter passed through the splitmix64 finalizer
 // (a bijection), so consecutive ids differ in about half their 56 bits and no
 // simple pattern (zero, small integers, float bits) is likely to match one.
-// Ids keep 48 bits: a ticket holds (id << 16 | arrivals).
+// Ids keep 48 bits: a ticket holds (id << 16 | arrivals); no id is 0.
 std::atomic<unsigned long long> g_call_counter{0};
 
 unsigned long long call_id() {
@@ -38,7 +38,8 @@ unsigned long long call_id() {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
   z ^= z >> 31;
-  return z & ((1ull << 48) - 1);
+  z &= (1ull << 48) - 1;
+  return z ? z : 1;  // 0 marks a released ticket
 }
 
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));

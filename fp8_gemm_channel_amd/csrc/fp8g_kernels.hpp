@@ -260,7 +260,10 @@ constexpr uint32_t kOut = 0x80000000u;  // a buffer offset past every descriptor
 // the one that brings the count to `target` finishes the tile.  A ticket holds
 // (call id << 16 | arrivals); a ticket left by another call (or any stale
 // bytes) restarts at one arrival, so tickets need no zeroing before a launch.
-// The compare-and-swap loop is lock-free: a failed attempt means another
+// The last arrival sets the ticket back to 0 (no call id is 0): a replay of a
+// captured launch -- same call id, same workspace -- then starts from a clean
+// ticket instead of counting on from the previous replay's total.  The
+// compare-and-swap loop is lock-free: a failed attempt means another
 // workgroup's succeeded.
 __device__ __forceinline__ bool take_ticket(unsigned long long *t, unsigned long long epoch, int target) {
   unsigned long long old = __hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -271,7 +274,10 @@ __device__ __forceinline__ bool take_ticket(unsigned long long *t, unsigned long
                                              __HIP_MEMORY_SCOPE_AGENT))
       break;
   }
-  return (int)(want & 0xFFFFull) == target;
+  const bool last = (int)(want & 0xFFFFull) == target;
+  // every contributor has arrived: nobody else touches this ticket in this launch
+  if (last) __hip_atomic_store(t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
 }
 
 // Scheduling pattern for NM MFMAs and NR LDS reads spread evenly: MFMA q is
