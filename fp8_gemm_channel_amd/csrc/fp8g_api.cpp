@@ -86,7 +86,7 @@ hipError_t workspace_alloc(void **ptr, size_t bytes, hipStream_t stream) {
       uint64_t keep = UINT64_MAX;
       e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep);
       if (e != hipSuccess) {
-        hipMemPoolDestroy(created);
+        (void)hipMemPoolDestroy(created);
         return e;
       }
       g_pools[dev] = created;
