@@ -266,8 +266,10 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
   int64_t kk = K;
   if (K % 128 != 0) {
     const int64_t kp = cdiv(K, 128) * 128;
-    // (the copy must also stay a modest workspace: at most 4 GiB)
-    const bool fits = (M + N) * kp <= (int64_t(4) << 30);
+    // (the copy must also stay a modest workspace, at most 4 GiB, and the padded
+    // K within FP8G_MAX_K: a tile's rows form one buffer range of 256 * K
+    // bytes, which must stay below 2^32)
+    const bool fits = (M + N) * kp <= (int64_t(4) << 30) && kp <= FP8G_MAX_K;
     const double flops = 2.0 * (double)M * (double)N * (double)K;
     const bool pad_auto = fits && flops >= 3e10 && 2.0 * (double)M * (double)N / (double)(M + N) >= 512.0;
     const bool pad = variant == 16 ? pad_auto : ((split_k == 2 && fits) || (split_k == 0 && pad_auto));

@@ -104,6 +104,8 @@ def test_plan_row_realignment():
     forced = fg.fp8_gemm_plan_ex(256, 256, 257, fg.PATH_MAIN, 0, 2)
     assert forced["pad_k"] == 384 and forced["workspace_bytes"] == 512 * 384
     assert fg.fp8_gemm_plan_ex(4096, 4096, 4127, fg.PATH_MAIN, 0, 1)["pad_k"] == 0
+    # the padded K must stay within the largest K (a tile's rows are one 32-bit range)
+    assert fg.fp8_gemm_plan_ex(256, 256, (1 << 24) - 1, fg.PATH_MAIN, 0, 2)["pad_k"] == 0
     sk = fg.fp8_gemm_plan_ex(4096, 4352, 4127, fg.PATH_MAIN, 16, 0)
     assert sk["pad_k"] == 4224 and sk["workspace_bytes"] > (4096 + 4352) * 4224
 

@@ -202,3 +202,19 @@ def test_status_codes_on_gpu():
         fg.fp8_gemm(x, w[:, :4].contiguous(), s)
     with pytest.raises(TypeError):
         fg.fp8_gemm(x.to(torch.int16), w, s)
+
+
+@pytest.mark.parametrize("shape,kw", [
+    ((130, 136, 1_000_003), {}),                               # main path, long odd rows
+    ((130, 136, 1_000_003), dict(path=fg.PATH_MAIN, split_k=2)),  # ... realigned first
+    ((3, 200, 2_000_001), {}),                                 # split-K path
+    ((40, 300, 1_048_576 + 17), dict(path=fg.PATH_SPLITK, split_k=7)),
+])
+def test_long_k(shape, kw):
+    """K up to 2^21: 32-bit buffer offsets, many K steps and slices."""
+    M, N, K = shape
+    x, w, s = synth.fp8_inputs(M, N, K, seed=17, scale_lo=1e-4, scale_hi=2e-4)
+    say(f"long K {shape} {kw}")
+    got = run(x, w, s, **kw)
+    mi, ni = synth.sample_positions(M, N, 600, seed=18)
+    compare(got[mi, ni], oracle.gemm_scaled_at(x, w, s, mi, ni), f"long K {shape}")
