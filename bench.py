@@ -10,8 +10,13 @@ rewritten (outside the timed events) so no operand is served from the 4 MiB
 per-XCD L2 or the 256 MiB Infinity Cache: cold-cache timing, as the deck the
 pages grade against does with its L2 flush.
 
-Each GEMM is timed with HIP events on the stream it is launched on.  Per
-shape: TFLOP/s (GB/s for the memory-bound M=32 shape) and the fraction of the
+Each GEMM is timed with HIP events on the stream it is launched on, attached
+to the call's own kernels (hipExtLaunchKernel through fp8_gemm_scaled_act_timed:
+start when the first kernel begins, stop when the last one ends, as a kernel
+trace times them).  Each step also times a second cold call of each shape
+between a hipEventRecord pair, reported as `marker_median_us` and
+`value_marker_timed`: that pair alone (nothing between the records) costs
+~4.4 us on MI355X, most of the time of a small GEMM.  Per shape: TFLOP/s (GB/s for the memory-bound M=32 shape) and the fraction of the
 MI355X roofline t_roof / t, with t_roof = max(FLOPs / 5.0 PFLOP/s dense fp8,
 algorithmic bytes / 8.0 TB/s).  `value` is the geometric mean of the five
 fractions.  `roofline` describes the dominant kernel (the main kernel on the
@@ -177,19 +182,34 @@ def main() -> int:
     times = {wl.name: [] for wl in workloads}
     ev = {wl.name: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for wl in workloads}
+    kev = {wl.name: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for wl in workloads}
+    for pair in list(ev.values()) + list(kev.values()):
+        for e in pair:  # torch creates a HIP event at its first record
+            e.record(stream)
+    torch.cuda.synchronize()
+    marker_times = {wl.name: [] for wl in workloads}
 
     def step(record: bool, i: int) -> None:
         for wl in workloads:
             xd, wd, sd, yd = dev_bufs[wl.name]
+            e0, e1 = ev[wl.name]
+            k0, k1 = kev[wl.name]
+            # two cold calls: one with the events attached to its kernels, one
+            # between a hipEventRecord pair (attaching events adds work around
+            # the call, so the two timings never share a call)
             if not args.no_flush:
                 flush.fill_(i)
-            e0, e1 = ev[wl.name]
+            fg.fp8_gemm(xd, wd, sd, out=yd, stream=stream, events=(k0, k1))
+            if not args.no_flush:
+                flush.fill_(i + 1)
             e0.record(stream)
             fg.fp8_gemm(xd, wd, sd, out=yd, stream=stream)
             e1.record(stream)
             if record:
                 e1.synchronize()
-                times[wl.name].append(e0.elapsed_time(e1) * 1e-3)
+                times[wl.name].append(k0.elapsed_time(k1) * 1e-3)
+                marker_times[wl.name].append(e0.elapsed_time(e1) * 1e-3)
 
     for i in range(args.warmup):
         step(False, i)
@@ -210,12 +230,15 @@ def main() -> int:
         per.append({"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "path": plan["path_name"],
                     "variant": plan["variant"], "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
                     "split_k": plan["split_k"], "median_us": round(med * 1e6, 2),
+                    "marker_median_us": round(float(np.median(marker_times[wl.name])) * 1e6, 2),
                     "min_us": round(float(t.min()) * 1e6, 2), "tflops": round(wl.flops / med / 1e12, 1),
                     "gbps": round(wl.bytes / med / 1e9, 1), "bound": bound_of(wl),
                     "fraction": round(frac, 4)})
         log(f"{wl.name:>12}: {med*1e6:9.2f} us  {wl.flops/med/1e12:7.1f} TFLOP/s  "
             f"{wl.bytes/med/1e9:7.1f} GB/s  frac {frac:.4f} ({bound_of(wl)})")
     geo = math.exp(sum(math.log(f) for f in fracs) / len(fracs))
+    geo_marker = math.exp(sum(math.log(roof_seconds(wl) / float(np.median(marker_times[wl.name])))
+                              for wl in workloads) / len(workloads))
     ms_per_step = sum(float(np.mean(times[w.name])) for w in workloads) * 1e3
 
     # Dominant kernel: the main kernel on the largest square shape.
@@ -251,6 +274,9 @@ def main() -> int:
         "data": "synthetic (seed 42; N(0,1)->e4m3fn saturating RNE; scale U[0.005,0.02])",
         "config": {"workload": "5-shape sweep: " + ", ".join(f"{w.name} {w.M}x{w.N}x{w.K}" for w in workloads),
                    "cache": "warm" if args.no_flush else "cold (512 MiB rewrite before each GEMM)"},
+        "timing": "HIP events attached to each call's first and last kernel (hipExtLaunchKernel); "
+                  "marker_median_us / value_marker_timed: a hipEventRecord pair around a second cold call",
+        "value_marker_timed": round(geo_marker, 4),
         "per_config": per,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -13,11 +13,13 @@ Entry points (same names as the C ABI):
     fp8_gemm_scaled_act(x, w, scale, bias, y, M, N, K, x_format, w_format,
                         activation, stream)                   bias, activation, E5M2
     fp8_gemm_scaled_act_ex(..., path, variant, split_k, stream)
+    fp8_gemm_scaled_act_timed(..., stream, start_event, stop_event)
+                                                              events on the call's kernels
     fp8_gemm_plan(M, N, K) / fp8_gemm_plan_ex(...)           host-only planner
     fp8_gemm_strerror(status), fp8_gemm_last_error()
 and the tensor-level convenience wrapper
     fp8_gemm(x, w, scale, *, bias=None, act=ACT_NONE, out=None, path=0,
-             variant=0, split_k=0) -> y
+             variant=0, split_k=0, stream=None, events=None) -> y
 (operand formats follow the tensors' dtypes: float8_e4m3fn or float8_e5m2).
 """
 from __future__ import annotations
@@ -41,7 +43,7 @@ ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_TANH = 0, 1, 2, 3
 
 #: Every symbol include/fp8g.h declares.
 EXPORTED_SYMBOLS = ("fp8_gemm_scaled", "fp8_gemm_scaled_ex", "fp8_gemm_scaled_act", "fp8_gemm_scaled_act_ex",
-                    "fp8_gemm_plan", "fp8_gemm_plan_ex", "fp8_gemm_strerror", "fp8_gemm_last_error")
+                    "fp8_gemm_scaled_act_timed", "fp8_gemm_plan", "fp8_gemm_plan_ex", "fp8_gemm_strerror", "fp8_gemm_last_error")
 
 
 class Plan(ctypes.Structure):
@@ -72,7 +74,7 @@ def _load() -> ctypes.CDLL:
     import torch  # noqa: F401
 
     if not os.path.exists(LIBRARY):
-        raise ImportError(f"{LIBRARY} is not built; run `python -m fp8_gemm_channel_amd.build` "
+        raise ImportError(f"{LIBRARY} is not built; run `python fp8_gemm_channel_amd/build.py` "
                           "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(LIBRARY)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
@@ -84,6 +86,9 @@ def _load() -> ctypes.CDLL:
     lib.fp8_gemm_scaled_act.restype = ctypes.c_int
     lib.fp8_gemm_scaled_act_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp]
     lib.fp8_gemm_scaled_act_ex.restype = ctypes.c_int
+    lib.fp8_gemm_scaled_act_timed.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                              vp, vp, vp]
+    lib.fp8_gemm_scaled_act_timed.restype = ctypes.c_int
     lib.fp8_gemm_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
     lib.fp8_gemm_plan.restype = ctypes.c_int
     lib.fp8_gemm_plan_ex.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(Plan)]
@@ -123,6 +128,16 @@ def fp8_gemm_scaled_act_ex(x: int, w: int, scale: int, bias: int, y: int, M: int
                                        path, variant, split_k, stream)
 
 
+def fp8_gemm_scaled_act_timed(x: int, w: int, scale: int, bias: int, y: int, M: int, N: int, K: int,
+                              x_format: int = FMT_E4M3, w_format: int = FMT_E4M3, activation: int = ACT_NONE,
+                              path: int = 0, variant: int = 0, split_k: int = 0, stream: int = 0,
+                              start_event: int = 0, stop_event: int = 0) -> int:
+    """fp8_gemm_scaled_act_ex with hipEvent_t handles attached to the call's
+    first and last kernels (0 = none)."""
+    return _lib.fp8_gemm_scaled_act_timed(x, w, scale, bias or None, y, M, N, K, x_format, w_format, activation,
+                                          path, variant, split_k, stream, start_event or None, stop_event or None)
+
+
 def fp8_gemm_plan(M: int, N: int, K: int) -> dict:
     return fp8_gemm_plan_ex(M, N, K)
 
@@ -145,11 +160,14 @@ def fp8_gemm_last_error() -> str:
 
 # ------------------------------------------------------------- tensor wrapper --
 def fp8_gemm(x, w, scale, *, bias=None, act: int = ACT_NONE, x_format=None, w_format=None, out=None,
-             path: int = 0, variant: int = 0, split_k: int = 0, stream=None):
+             path: int = 0, variant: int = 0, split_k: int = 0, stream=None, events=None):
     """y = bf16(act((x @ w^T) * scale + bias)) on the GPU; returns a new [M, N]
     bfloat16 tensor (or writes `out`).  x: [M,K], w: [N,K] float8_e4m3fn or
     float8_e5m2 (or uint8 codes, E4M3 unless x_format / w_format say E5M2);
-    scale, bias: [N] float32; all contiguous on the same CUDA/HIP device."""
+    scale, bias: [N] float32; all contiguous on the same CUDA/HIP device.
+    `events` = (start, stop) torch.cuda.Event(enable_timing=True) pair: start
+    is recorded when the call's first kernel begins, stop when its last kernel
+    ends (start.elapsed_time(stop) is the GPU time of the call)."""
     import torch
 
     def codes(t, name, fmt):
@@ -190,10 +208,15 @@ def fp8_gemm(x, w, scale, *, bias=None, act: int = ACT_NONE, x_format=None, w_fo
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     with torch.cuda.device(x.device):
-        st = _lib.fp8_gemm_scaled_act_ex(x.data_ptr(), w.data_ptr(), scale.data_ptr(),
-                                         bias.data_ptr() if bias is not None else None, out.data_ptr(),
-                                         M, N, K, x_format, w_format, act, path, variant, split_k,
-                                         stream.cuda_stream)
+        args = (x.data_ptr(), w.data_ptr(), scale.data_ptr(), bias.data_ptr() if bias is not None else None,
+                out.data_ptr(), M, N, K, x_format, w_format, act, path, variant, split_k, stream.cuda_stream)
+        if events is None:
+            st = _lib.fp8_gemm_scaled_act_ex(*args)
+        else:
+            for e in events:
+                if e.cuda_event == 0:  # torch creates the HIP event at its first record
+                    e.record(stream)
+            st = _lib.fp8_gemm_scaled_act_timed(*args, events[0].cuda_event, events[1].cuda_event)
     if st != FP8G_OK:
         raise Fp8gError(st, fp8_gemm_last_error())
     return out

@@ -1,6 +1,8 @@
 """Build libfp8g.so (the HIP library behind include/fp8g.h) in-tree for gfx950.
 
-    python -m fp8_gemm_channel_amd.build [--verbose]
+    python fp8_gemm_channel_amd/build.py [--verbose]
+
+(run as a file: importing the package loads the library this builds)
 
 hipcc cross-compiles the device code for gfx950 without a GPU present.
 """
@@ -25,7 +27,7 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 # feature, and m0 is clobbered on purpose by the LDS-DMA asm.
 _NOISE = ("packed-fp32-ops", "clobber list contains reserved registers: m0",
           "Reserved registers on the clobber list", "warnings generated", "asm volatile(",
-          "^", "| ")
+          "^", "| ", "In file included from")
 
 
 def _filter(text: str) -> str:

@@ -317,7 +317,7 @@ bool supports_formats(const fp8g_plan &p) {
 
 int run(const void *x, const void *w, const float *scale, const float *bias, void *y, int64_t M, int64_t N,
         int64_t K, int32_t x_format, int32_t w_format, int32_t act, int32_t path, int32_t variant, int32_t split_k,
-        void *stream_ptr) {
+        void *stream_ptr, void *start_event = nullptr, void *stop_event = nullptr) {
   g_last_error.clear();
   if ((x_format != FP8G_FMT_E4M3 && x_format != FP8G_FMT_E5M2) ||
       (w_format != FP8G_FMT_E4M3 && w_format != FP8G_FMT_E5M2))
@@ -330,7 +330,15 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
   if (fmt != 0 && !supports_formats(p))
     return fail(FP8G_ERR_INVALID_ARG, "%s variant %d is built for E4M3 operands only", p.path == FP8G_PATH_MAIN ? "main" : "split-K",
                 p.variant);
-  if (p.path == FP8G_PATH_NONE) return FP8G_OK;
+  hipStream_t stream = (hipStream_t)stream_ptr;
+  const fp8g::DispatchEvents events{(hipEvent_t)start_event, (hipEvent_t)stop_event};
+  if (p.path == FP8G_PATH_NONE) {
+    // no kernel to attach the events to: record them on the stream instead
+    hipError_t e = hipSuccess;
+    if (events.start) e = hipEventRecord(events.start, stream);
+    if (e == hipSuccess && events.stop) e = hipEventRecord(events.stop, stream);
+    return e == hipSuccess ? FP8G_OK : hip_fail(e, "hipEventRecord (empty extent)");
+  }
   if (!y) return fail(FP8G_ERR_INVALID_ARG, "y is null");
   if (!scale) return fail(FP8G_ERR_INVALID_ARG, "scale is null");
   if (K > 0 && (!x || !w)) return fail(FP8G_ERR_INVALID_ARG, "x or w is null");
@@ -342,7 +350,6 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
       overlaps(y, ybytes, scale, (size_t)N * 4) || overlaps(y, ybytes, bias, (size_t)N * 4))
     return fail(FP8G_ERR_INVALID_ARG, "y overlaps an input");
 
-  hipStream_t stream = (hipStream_t)stream_ptr;
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -350,8 +357,8 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
   const bool vec = (N % 4 == 0) && ((uintptr_t)y % 8 == 0);
   if (p.path == FP8G_PATH_ZERO) {
     // K = 0: the empty sum is +0; with a bias or an activation y = act(bias)
-    if (bias || act != FP8G_ACT_NONE) e = fp8g::launch_empty_k((uint16_t *)y, bias, act, M, N, stream);
-    else e = fp8g::launch_zero((uint16_t *)y, M * N, stream);
+    if (bias || act != FP8G_ACT_NONE) e = fp8g::launch_empty_k((uint16_t *)y, bias, act, M, N, stream, events);
+    else e = fp8g::launch_zero((uint16_t *)y, M * N, stream, events);
     return e == hipSuccess ? FP8G_OK : hip_fail(e, "K = 0 launch");
   }
   if (p.path == FP8G_PATH_MAIN) {
@@ -361,6 +368,7 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
     l.bias = bias;
     l.act = act;
     l.fmt = fmt;
+    l.ev = events;
     void *ws = nullptr;
     if (p.workspace_bytes > 0) {
       // [padded x rows | padded w rows] (pad plan), then, for stream-K, the
@@ -373,7 +381,10 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
     char *wsp = (char *)ws;
     if (p.pad_k > 0) {
       uint8_t *xp = (uint8_t *)wsp, *wp = xp + (size_t)M * (size_t)p.pad_k;
-      e = fp8g::launch_pad_rows((const uint8_t *)x, (const uint8_t *)w, xp, M, N, K, p.pad_k, stream);
+      // two kernels: the start event goes with the copy, the stop event with the GEMM
+      e = fp8g::launch_pad_rows((const uint8_t *)x, (const uint8_t *)w, xp, M, N, K, p.pad_k, stream,
+                                fp8g::DispatchEvents{events.start, nullptr});
+      l.ev.start = nullptr;
       l.x = xp;
       l.w = wp;
       l.K = p.pad_k;
@@ -412,6 +423,7 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
   l.bias = bias;
   l.act = act;
   l.fmt = fmt;
+  l.ev = events;
   e = fp8g::launch_skinny(l, stream);
   if (ws) {
     hipError_t f = hipFreeAsync(ws, stream);
@@ -444,6 +456,14 @@ int fp8_gemm_scaled_act_ex(const void *x, const void *w, const float *scale, con
                            int64_t N, int64_t K, int32_t x_format, int32_t w_format, int32_t activation,
                            int32_t path, int32_t variant, int32_t split_k, void *stream) {
   return run(x, w, scale, bias, y, M, N, K, x_format, w_format, activation, path, variant, split_k, stream);
+}
+
+int fp8_gemm_scaled_act_timed(const void *x, const void *w, const float *scale, const float *bias, void *y,
+                              int64_t M, int64_t N, int64_t K, int32_t x_format, int32_t w_format,
+                              int32_t activation, int32_t path, int32_t variant, int32_t split_k, void *stream,
+                              void *start_event, void *stop_event) {
+  return run(x, w, scale, bias, y, M, N, K, x_format, w_format, activation, path, variant, split_k, stream,
+             start_event, stop_event);
 }
 
 int fp8_gemm_plan(int64_t M, int64_t N, int64_t K, fp8g_plan *out) {

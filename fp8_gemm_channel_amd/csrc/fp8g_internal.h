@@ -9,6 +9,13 @@
 namespace fp8g {
 
 // One launch of the main (tiled MFMA) kernel.
+// Events attached to one kernel's own dispatch (hipExtLaunchKernel): `start` is
+// recorded when the kernel begins and `stop` when it has ended; null = none.
+struct DispatchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 struct MainLaunch {
   const uint8_t *x;
   const uint8_t *w;
@@ -27,6 +34,7 @@ struct MainLaunch {
   float *partials = nullptr;              // 2 * n_sk partial tiles of kMainPartialBytes
   unsigned long long *tickets = nullptr;  // one per stream-K tile, kTicketStride apart (any initial value)
   unsigned long long epoch = 0;           // id of this call, < 2^48
+  DispatchEvents ev;                      // attached to the main kernel's dispatch
 };
 
 // One launch of the skinny split-K kernel (with S > 1 the last workgroup of each
@@ -46,6 +54,7 @@ struct SkinnyLaunch {
   const float *bias = nullptr;  // per-column bias [N], or null
   int act = 0;                  // epilogue activation (FP8G_ACT_*)
   int fmt = 0;                  // (w format << 1) | x format, 0 = E4M3, 1 = E5M2
+  DispatchEvents ev;            // attached to the kernel's dispatch
 };
 
 // Split-K tickets sit one 128-byte cache line apart (in 8-byte units): the
@@ -76,12 +85,13 @@ hipError_t launch_main_tiles_epi(const MainLaunch &l, hipStream_t stream);   // 
 hipError_t launch_main_legacy(const MainLaunch &l, hipStream_t stream);      // variants 1, 2, 4-7, 9
 hipError_t launch_skinny_epi(const SkinnyLaunch &l, hipStream_t stream);     // bias / activation, variants 11-15
 hipError_t launch_skinny(const SkinnyLaunch &l, hipStream_t stream);
-hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream);
+hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream, const DispatchEvents &ev);
 // Copies x [M, K] and w [N, K] (rows at any byte alignment) into dst as
 // [M + N, K16] rows, bytes K .. K16-1 zero (K16: K rounded up to a multiple of 16).
 hipError_t launch_pad_rows(const uint8_t *x, const uint8_t *w, uint8_t *dst, int64_t M, int64_t N, int64_t K,
-                           int64_t K16, hipStream_t stream);
+                           int64_t Kp, hipStream_t stream, const DispatchEvents &ev);
 // K = 0 with a bias or an activation: y[m, n] = bf16(act(bias[n])).
-hipError_t launch_empty_k(uint16_t *y, const float *bias, int act, int64_t M, int64_t N, hipStream_t stream);
+hipError_t launch_empty_k(uint16_t *y, const float *bias, int act, int64_t M, int64_t N, hipStream_t stream,
+                          const DispatchEvents &ev);
 
 }  // namespace fp8g

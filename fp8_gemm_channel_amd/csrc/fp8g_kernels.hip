@@ -128,30 +128,28 @@ hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
   }
 }
 
-hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream) {
+hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream, const DispatchEvents &ev) {
   int64_t blocks = (count + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  fp8g_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(y, count);
-  return hipGetLastError();
+  return dispatch(fp8g_zero_kernel, dim3((unsigned)blocks), dim3(256), stream, ev, y, count);
 }
 
 hipError_t launch_pad_rows(const uint8_t *x, const uint8_t *w, uint8_t *dst, int64_t M, int64_t N, int64_t K,
-                           int64_t K16, hipStream_t stream) {
+                           int64_t Kp, hipStream_t stream, const DispatchEvents &ev) {
   const int64_t rows = M + N;
   if (rows <= 0) return hipSuccess;
-  fp8g_pad_rows_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(x, w, dst, rows, M, (int)K,
-                                                                                   (int)K16);
-  return hipGetLastError();
+  return dispatch(fp8g_pad_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), stream, ev, x, w, dst, rows, M,
+                  (int)K, (int)Kp);
 }
 
-hipError_t launch_empty_k(uint16_t *y, const float *bias, int act, int64_t M, int64_t N, hipStream_t stream) {
+hipError_t launch_empty_k(uint16_t *y, const float *bias, int act, int64_t M, int64_t N, hipStream_t stream,
+                          const DispatchEvents &ev) {
   const int64_t count = M * N;
   int64_t blocks = (count + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  fp8g_empty_k_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(y, bias, act, N, count);
-  return hipGetLastError();
+  return dispatch(fp8g_empty_k_kernel, dim3((unsigned)blocks), dim3(256), stream, ev, y, bias, act, N, count);
 }
 
 }  // namespace fp8g

@@ -40,6 +40,7 @@
 // cell); here nothing is copied and nothing is padded in memory.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1562,6 +1563,16 @@ __global__ __launch_bounds__(256, 1) void fp8g_skinny_direct_kernel(SkinnyArgs a
 inline bool has_epilogue(const MainLaunch &l) { return l.bias != nullptr || l.act != kActNone; }
 inline bool has_epilogue(const SkinnyLaunch &l) { return l.bias != nullptr || l.act != kActNone; }
 
+// Launches kernel(args...) on `stream`; with events set they are attached to
+// this dispatch (recorded when the kernel begins and when it has ended).
+template <typename... P, typename... A>
+static inline hipError_t dispatch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                                  const DispatchEvents &ev, A... args) {
+  if (ev.start || ev.stop) hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
+  else kernel<<<grid, block, 0, stream>>>(args...);
+  return hipGetLastError();
+}
+
 // Kernel arguments of a main-path launch.
 static inline MainArgs main_args(const MainLaunch &l) {
   MainArgs a{l.x, l.w, l.scale, l.y, l.M, l.N, l.K, l.tiles_m, l.tiles_n, l.group_m, l.ystore};
@@ -1590,9 +1601,9 @@ static hipError_t launch_main_cfg(const MainLaunch &l, hipStream_t stream) {
   const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(WM * WN * 64);
   auto go = [&](auto fmt) {
     constexpr int F = decltype(fmt)::value;
-    if (l.k_tail) fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, true, PP, F, EPI><<<grid, block, 0, stream>>>(a);
-    else fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, false, PP, F, EPI><<<grid, block, 0, stream>>>(a);
-    return hipGetLastError();
+    if (l.k_tail) return dispatch(fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, true, PP, F, EPI>, grid, block, stream,
+                                  l.ev, a);
+    return dispatch(fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, false, PP, F, EPI>, grid, block, stream, l.ev, a);
   };
   if constexpr (ALLFMT) return with_format(l.fmt, go);
   if (l.fmt != 0) return hipErrorInvalidValue;
@@ -1617,9 +1628,8 @@ static hipError_t launch_main5_dp(const MainLaunch &l, hipStream_t stream) {
   const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(512);
   return with_format(l.fmt, [&](auto fmt) {
     constexpr int F = decltype(fmt)::value;
-    if (l.k_tail) fp8g_main5_kernel<true, false, F, EPI><<<grid, block, 0, stream>>>(a);
-    else fp8g_main5_kernel<false, false, F, EPI><<<grid, block, 0, stream>>>(a);
-    return hipGetLastError();
+    if (l.k_tail) return dispatch(fp8g_main5_kernel<true, false, F, EPI>, grid, block, stream, l.ev, a);
+    return dispatch(fp8g_main5_kernel<false, false, F, EPI>, grid, block, stream, l.ev, a);
   });
 }
 
@@ -1630,13 +1640,11 @@ static hipError_t launch_skinny_cfg(const SkinnyLaunch &l, hipStream_t stream) {
   const dim3 grid((unsigned)((l.N + 16 * RB - 1) / (16 * RB)), (unsigned)l.S), block(256);
   if constexpr (DIRECT) {
     if (l.fmt != 0) return hipErrorInvalidValue;
-    fp8g_skinny_direct_kernel<RB, MB, 4, EPI><<<grid, block, 0, stream>>>(a);
-    return hipGetLastError();
+    return dispatch(fp8g_skinny_direct_kernel<RB, MB, 4, EPI>, grid, block, stream, l.ev, a);
   } else {
     return with_format(l.fmt, [&](auto fmt) {
       constexpr int F = decltype(fmt)::value;
-      fp8g_splitk_partial_kernel<RB, MB, F, EPI><<<grid, block, 0, stream>>>(a);
-      return hipGetLastError();
+      return dispatch(fp8g_splitk_partial_kernel<RB, MB, F, EPI>, grid, block, stream, l.ev, a);
     });
   }
 }

@@ -14,9 +14,8 @@ hipError_t launch_main5(const MainLaunch &l, hipStream_t stream) {
   a.tickets = l.tickets;
   a.epoch = l.epoch;
   const dim3 grid((unsigned)(l.n_dp + l.n_sk)), block(512);
-  if (l.k_tail) fp8g_main5_kernel<true, true, 0, true><<<grid, block, 0, stream>>>(a);
-  else fp8g_main5_kernel<false, true, 0, true><<<grid, block, 0, stream>>>(a);
-  return hipGetLastError();
+  if (l.k_tail) return dispatch(fp8g_main5_kernel<true, true, 0, true>, grid, block, stream, l.ev, a);
+  return dispatch(fp8g_main5_kernel<false, true, 0, true>, grid, block, stream, l.ev, a);
 }
 
 }  // namespace fp8g

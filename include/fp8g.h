@@ -186,6 +186,26 @@ int fp8_gemm_scaled_act_ex(const void *x, const void *w, const float *scale, con
                            int32_t activation, int32_t path, int32_t variant, int32_t split_k,
                            void *stream);
 
+/* ------------------------------------------------------------- timing -----
+ * fp8_gemm_scaled_act_ex with two HIP events attached to the call's own
+ * kernels (hipExtLaunchKernel): start_event is recorded when the call's first
+ * kernel begins and stop_event when its last kernel has ended, so
+ * hipEventElapsedTime(start, stop) is the GPU time of the call (one kernel, or
+ * the row copy plus the GEMM when K is realigned) without the marker packets
+ * that hipEventRecord adds around it.  The stream-ordered workspace allocation
+ * and release are not kernels and fall outside that window.
+ *   start_event, stop_event : hipEvent_t handles created by the caller (with
+ *              timing enabled) on the device of the call, or NULL (not
+ *              recorded).  Borrowed: the library records them, nothing more.
+ * With M == 0 or N == 0 no kernel runs and both events are recorded with
+ * hipEventRecord on the stream.  The events are recorded only on success;
+ * after an error their state is unspecified.  Everything else as
+ * fp8_gemm_scaled_act_ex. */
+int fp8_gemm_scaled_act_timed(const void *x, const void *w, const float *scale, const float *bias, void *y,
+                              int64_t M, int64_t N, int64_t K, int32_t x_format, int32_t w_format,
+                              int32_t activation, int32_t path, int32_t variant, int32_t split_k,
+                              void *stream, void *start_event, void *stop_event);
+
 /* Static description of a status code. */
 const char *fp8_gemm_strerror(int status);
 

@@ -144,6 +144,14 @@ def test_scaled_rejects_bad_arguments_without_hip(case, detail):
     assert detail in fg.fp8_gemm_last_error()
 
 
+def test_timed_entry_checks_arguments_like_the_others():
+    st = fg.fp8_gemm_scaled_act_timed(FAKE * 2, FAKE * 4, FAKE * 6, 0, 0, 16, 16, 64, stream=0,
+                                      start_event=FAKE * 10, stop_event=FAKE * 12)
+    assert st == fg.FP8G_ERR_INVALID_ARG and "y is null" in fg.fp8_gemm_last_error()
+    st = fg.fp8_gemm_scaled_act_timed(FAKE * 2, FAKE * 4, FAKE * 6, 0, FAKE * 8, 16, 16, 64, activation=9)
+    assert st == fg.FP8G_ERR_INVALID_ARG and "activation" in fg.fp8_gemm_last_error()
+
+
 def test_empty_extent_is_a_no_op_even_with_null_pointers():
     assert fg.fp8_gemm_scaled(0, 0, 0, 0, 0, 16, 16, 0) == fg.FP8G_OK
     assert fg.fp8_gemm_scaled(0, 0, 0, 0, 16, 0, 16, 0) == fg.FP8G_OK
