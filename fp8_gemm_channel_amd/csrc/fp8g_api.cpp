@@ -146,6 +146,61 @@ int auto_main_variant(int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
+int64_t slice_bytes(int64_t K, int64_t S) {
+  const int64_t chunk = fp8g::skinny_chunk_bytes();
+  return cdiv(cdiv(K, S), chunk) * chunk;
+}
+
+// Rows per workgroup (16 * rb), K slices S and kernel of the split-K path when
+// nothing is forced.  Rules fitted to measurements on MI355X (cold cache,
+// M = 1 .. 64, N = 1024 .. 28672, K = 4096 .. 28672; within 1.2% of the best
+// configuration on geometric mean, 9% at worst): up to 32 rows of x, the
+// 8-wave kernel with the most w rows per workgroup that still gives at least
+// 160 workgroups without splitting K (a K split costs ~3 us of partial
+// hand-off); otherwise the most rows for which K slices of at least 4 KiB
+// reach 160 workgroups; otherwise 16 rows unsplit.  With 33 .. 64 rows of x
+// (re-read from L2 by every workgroup), the 4-wave kernel with 32 rows, or 16
+// when 32 cannot reach 256 workgroups, splitting K while slices keep at least
+// 2 KiB per 16 rows.
+void auto_splitk(int64_t M, int64_t N, int64_t K, int64_t *rb_out, int64_t *S_out, int *kind_base) {
+  auto grow = [&](int64_t nb, int64_t target, int64_t min_slice) {
+    int64_t S = 1;
+    while (nb * S < target && S < kMaxSplit && slice_bytes(K, 2 * S) >= min_slice) S *= 2;
+    return S;
+  };
+  if (M <= 32) {
+    const int max_rb = fp8g::skinny_max_row_blocks((int)M, fp8g::SkinnyKind::kRing8);
+    constexpr int64_t kMinWorkgroups = 160;
+    *kind_base = 20;
+    for (int rb = max_rb; rb >= 2; --rb)
+      if (cdiv(N, 16 * rb) >= kMinWorkgroups) {
+        *rb_out = rb;
+        *S_out = 1;
+        return;
+      }
+    for (int rb = max_rb; rb >= 1; --rb) {
+      const int64_t nb = cdiv(N, 16 * rb), S = grow(nb, kMinWorkgroups, 4096);
+      if (nb * S >= kMinWorkgroups) {
+        *rb_out = rb;
+        *S_out = S;
+        return;
+      }
+    }
+    *rb_out = 1;
+    *S_out = 1;
+    return;
+  }
+  *kind_base = 0;
+  for (int rb = 2; rb >= 1; --rb) {
+    const int64_t nb = cdiv(N, 16 * rb), S = grow(nb, kNumCUs, 2048 * rb);
+    if (nb * S >= kNumCUs || rb == 1) {
+      *rb_out = rb;
+      *S_out = S;
+      return;
+    }
+  }
+}
+
 int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, int32_t split_k, fp8g_plan *p) {
   if (!p) return fail(FP8G_ERR_INVALID_ARG, "plan output pointer is null");
   int st = check_dims(M, N, K);
@@ -173,18 +228,22 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     if (split_k > kMaxSplit)
       return fail(FP8G_ERR_INVALID_ARG, "split-K path takes split_k 0..%d (split_k=%d)", kMaxSplit, split_k);
     // Variants 1-5 force the LDS-ring kernel with 16 * variant w rows per
-    // workgroup, 11-15 the direct-to-register kernel with 16 * (variant - 10);
-    // 0 lets the planner choose the rows for the LDS-ring kernel, which streams
-    // w faster on MI355X (measured: M=32, N=12288, K=4096 at 15 us against
-    // 20 us for the direct kernel's best row count).  The direct kernel
-    // assembles a K tail from 16-byte loads that end inside the row, so it
-    // needs K >= 16.
-    if (variant > 10 && K < 16)
+    // workgroup, 11-15 the direct-to-register kernel with 16 * (variant - 10),
+    // 21-24 the LDS-ring kernel with 8 waves and 16 * (variant - 20) rows;
+    // 0 lets the planner choose the rows for the 4-wave LDS-ring kernel, which
+    // streams w faster on MI355X than the direct kernel (measured: M=32,
+    // N=12288, K=4096 at 15 us against 20 us for the direct kernel's best row
+    // count).  The direct kernel assembles a K tail from 16-byte loads that end
+    // inside the row, so it needs K >= 16.
+    if (variant > 10 && variant < 16 && K < 16)
       return fail(FP8G_ERR_INVALID_ARG, "split-K variant %d needs K >= 16 (K=%lld)", variant, (long long)K);
-    const bool direct = variant > 10;
-    const int forced_rb = variant > 10 ? variant - 10 : variant;
-    const int max_rb = fp8g::skinny_max_row_blocks((int)M, direct);
-    if (forced_rb > max_rb || (variant > 5 && variant < 11) || variant > 15)
+    const fp8g::SkinnyKind kind = variant > 20   ? fp8g::SkinnyKind::kRing8
+                                  : variant > 10 ? fp8g::SkinnyKind::kDirect
+                                                 : fp8g::SkinnyKind::kRing4;
+    const int kind_base = variant > 20 ? 20 : variant > 10 ? 10 : 0;
+    const int forced_rb = variant - kind_base;
+    const int max_rb = fp8g::skinny_max_row_blocks((int)M, kind);
+    if (forced_rb > max_rb || (variant > 5 && variant < 11) || (variant > 15 && variant < 21) || variant > 24)
       return fail(FP8G_ERR_INVALID_ARG, "split-K variant %d not available for M=%lld", variant, (long long)M);
     const int64_t chunk = fp8g::skinny_chunk_bytes();
     const int64_t nchunks = cdiv(K, chunk);
@@ -196,7 +255,12 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     // reduction by one workgroup per column tile (about 2 us of one CU's share
     // of HBM bandwidth, ~48 KiB).
     int64_t best_cost = -1, best_rb = 1, best_S = 1;
-    for (int rb = 1; rb <= max_rb; ++rb) {
+    int kbase = kind_base;
+    if (variant == 0 && split_k == 0) {
+      auto_splitk(M, N, K, &best_rb, &best_S, &kbase);
+      best_cost = 0;  // chosen: skip the model below
+    }
+    for (int rb = 1; rb <= max_rb && best_cost != 0; ++rb) {
       if (forced_rb != 0 && rb != forced_rb) continue;
       const int64_t nb = cdiv(N, 16 * rb);
       for (int64_t S0 = 1; S0 <= kMaxSplit; S0 *= 2) {
@@ -215,7 +279,7 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
         if (S >= nchunks) break;
       }
     }
-    const fp8g::SkinnyConfig *c = fp8g::skinny_config((int)best_rb + (direct ? 10 : 0));
+    const fp8g::SkinnyConfig *c = fp8g::skinny_config((int)best_rb + kbase);
     if (!c) return fail(FP8G_ERR_INVALID_ARG, "unknown split-K variant %d", variant);
     const int64_t k_slice = cdiv(cdiv(K, best_S), chunk) * chunk;
     const int64_t S = cdiv(K, k_slice);  // no empty slices
@@ -311,7 +375,7 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
 // 18 (all the planner picks) and the LDS-ring split-K kernel.
 bool supports_formats(const fp8g_plan &p) {
   if (p.path == FP8G_PATH_MAIN) return p.variant == 3 || p.variant == 10 || p.variant == 17 || p.variant == 18;
-  if (p.path == FP8G_PATH_SPLITK) return p.variant <= 5;
+  if (p.path == FP8G_PATH_SPLITK) return p.variant <= 5 || p.variant >= 21;
   return true;
 }
 

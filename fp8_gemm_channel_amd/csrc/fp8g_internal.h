@@ -74,7 +74,10 @@ struct SkinnyConfig {
 const MainConfig *main_config(int id);      // nullptr if unknown
 const SkinnyConfig *skinny_config(int id);  // nullptr if unknown
 int skinny_tile_n(const SkinnyConfig &c);   // output columns per workgroup
-int skinny_max_row_blocks(int M, bool direct);  // limit on row_blocks for this M and kernel
+// The split-K kernels: LDS ring with 4 waves (variants 1-5), direct to
+// registers (11-15), LDS ring with 8 waves (21-24).
+enum class SkinnyKind { kRing4, kDirect, kRing8 };
+int skinny_max_row_blocks(int M, SkinnyKind kind);  // limit on row_blocks for this M and kernel
 int skinny_chunk_bytes();                   // K granularity of one wave iteration
 
 hipError_t launch_main(const MainLaunch &l, hipStream_t stream);

@@ -95,9 +95,11 @@ static const MainConfig kMainConfigs[] = {
     {17, 128, 256, 128, 3}, // 8 waves, wave tile 64 x 64: grids of 128 x 256 tiles (mid M)
     {18, 128, 128, 128, 4}, // 8 waves, wave tile 64 (m) x 32 (n): grids of 128 x 128 tiles (mid M)
 };
-// ids 1-5: LDS-ring kernel, 11-15: direct-to-register kernel; 16 * row_blocks w rows per workgroup
+// ids 1-5: LDS-ring kernel (4 waves), 11-15: direct-to-register kernel, 21-24:
+// LDS-ring kernel with 8 waves; 16 * row_blocks w rows per workgroup
 static const SkinnyConfig kSkinnyConfigs[] = {
-    {1, 1}, {2, 2}, {3, 3}, {4, 4}, {5, 5}, {11, 1}, {12, 2}, {13, 3}, {14, 4}, {15, 5},
+    {1, 1},  {2, 2},  {3, 3},  {4, 4},  {5, 5},  {11, 1}, {12, 2},
+    {13, 3}, {14, 4}, {15, 5}, {21, 1}, {22, 2}, {23, 3}, {24, 4},
 };
 
 const MainConfig *main_config(int id) {
@@ -111,9 +113,12 @@ const SkinnyConfig *skinny_config(int id) {
   return nullptr;
 }
 int skinny_tile_n(const SkinnyConfig &c) { return 16 * c.row_blocks; }
-int skinny_max_row_blocks(int M, bool direct) {
-  if (direct) return 5;  // register ring: (RB + MB) * 8 * 4 VGPRs of operands
-  return M <= 16 ? 5 : (M <= 32 ? 4 : 2);  // LDS ring of the other kernel
+int skinny_max_row_blocks(int M, SkinnyKind kind) {
+  switch (kind) {
+    case SkinnyKind::kDirect: return 5;  // register ring: (RB + MB) * 8 * 4 VGPRs of operands
+    case SkinnyKind::kRing8: return M <= 16 ? 4 : (M <= 32 ? 3 : 1);  // 8 rings of 2 slots in LDS
+    default: return M <= 16 ? 5 : (M <= 32 ? 4 : 2);  // 4 rings of 3 slots in LDS
+  }
 }
 int skinny_chunk_bytes() { return 128; }
 

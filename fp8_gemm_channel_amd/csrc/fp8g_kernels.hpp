@@ -1131,16 +1131,17 @@ struct SkinnyArgs {
   int act;            // activation applied last (kAct*)
 };
 
-template <int RB, int MB>
+template <int RB, int MB, int WAVES = 4>
 struct SkinnyShape {
+  static constexpr int NW = WAVES;         // waves per workgroup
   static constexpr int R = 16 * RB;        // w rows per workgroup
   static constexpr int MX = 16 * MB;       // x rows staged per chunk
   static constexpr int ROWS = R + MX;
   static constexpr int SLOT = ROWS * 128;  // bytes per ring slot
   static constexpr int OPS = ROWS / 8;     // 1 KiB DMA instructions per chunk
-  static constexpr int D = 3;              // ring depth (chunks in flight per wave)
+  static constexpr int D = NW == 4 ? 3 : 2;  // ring depth (chunks in flight per wave)
   static constexpr int WAVE_LDS = D * SLOT;
-  static_assert(4 * WAVE_LDS <= 160 * 1024, "LDS");
+  static_assert(NW * WAVE_LDS <= 160 * 1024, "LDS");
   static_assert((D - 1) * OPS < 64, "vmcnt range");
 };
 
@@ -1259,11 +1260,11 @@ __device__ __forceinline__ void splitk_finish(const SkinnyArgs &a, int n0, int *
   }
 }
 
-// End of a skinny workgroup: the four waves' sums are added through LDS (`red`,
-// 4*RB*MB*4*64 floats) in wave order, so the result does not depend on timing;
-// wave v finishes blocks v, v+4, ...  One K slice: scale and bf16 store; several:
-// unscaled fp32 partials, which the column tile's last workgroup adds.
-template <int RB, int MB, bool EPI>
+// End of a skinny workgroup: the NW waves' sums are added through LDS (`red`,
+// NW*RB*MB*4*64 floats) in wave order, so the result does not depend on timing;
+// wave v finishes blocks v, v+NW, ...  One K slice: scale and bf16 store;
+// several: unscaled fp32 partials, which the column tile's last workgroup adds.
+template <int RB, int MB, bool EPI, int NW = 4>
 __device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const SkinnyArgs &a, float *red, int n0,
                                               int s, int wave, int lane) {
   const int g = lane >> 4, lr = lane & 15;
@@ -1277,14 +1278,14 @@ __device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const Sk
   __syncthreads();
   const v4i rsrc_s = make_rsrc(a.scale, (uint32_t)a.N * 4u);
   const v4i rsrc_b = make_rsrc(a.bias, a.bias ? (uint32_t)a.N * 4u : 0u);
-  for (int b = wave; b < RB * MB; b += 4) {
+  for (int b = wave; b < RB * MB; b += NW) {
     const int rb = b / MB, mb = b % MB;
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float t = red[((b) * 4 + e) * 64 + lane];
 #pragma unroll
-      for (int o = 1; o < 4; ++o) t += red[((o * RB * MB + b) * 4 + e) * 64 + lane];
+      for (int o = 1; o < NW; ++o) t += red[((o * RB * MB + b) * 4 + e) * 64 + lane];
       v[e] = t;
     }
     const int n = n0 + 16 * rb + 4 * g;
@@ -1320,11 +1321,12 @@ __device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const Sk
   if (gridDim.y > 1) splitk_finish<RB, EPI>(a, n0, (int *)red);
 }
 
-template <int RB, int MB, int FMT = 0, bool EPI = false>
-__global__ __launch_bounds__(256, 1) void fp8g_splitk_partial_kernel(SkinnyArgs a) {
-  using S = SkinnyShape<RB, MB>;
+template <int RB, int MB, int FMT = 0, bool EPI = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 1) void fp8g_splitk_partial_kernel(SkinnyArgs a) {
+  using S = SkinnyShape<RB, MB, NW>;
   constexpr int R = S::R, OPS = S::OPS, D = S::D, SLOT = S::SLOT, W_OPS = R / 8;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * S::WAVE_LDS];
+  static_assert(NW * RB * MB * 4 * 64 * 4 <= NW * S::WAVE_LDS, "the cross-wave sum fits in the ring");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NW * S::WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1335,7 +1337,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_splitk_partial_kernel(SkinnyArgs 
   const int kbeg = s * a.k_slice;
   const int kend = min(K, kbeg + a.k_slice);
   const int nch = (kend - kbeg + 127) >> 7;
-  const int my = nch > wave ? (nch - wave + 3) >> 2 : 0;  // chunks of this wave
+  const int my = nch > wave ? (nch - wave + NW - 1) / NW : 0;  // chunks of this wave
 
   const v4i rsrc_w = make_rsrc(a.w + (size_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
   const v4i rsrc_x = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)K);
@@ -1354,9 +1356,9 @@ __global__ __launch_bounds__(256, 1) void fp8g_splitk_partial_kernel(SkinnyArgs 
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem + (uint32_t)wave * S::WAVE_LDS;
   uint8_t *ring = smem + wave * S::WAVE_LDS;
 
-  // Local chunk j (global chunk wave + 4j) -> slot j % D.
+  // Local chunk j (global chunk wave + NW j) -> slot j % D.
   auto issue = [&](int j) __attribute__((always_inline)) {
-    const int kc = kbeg + ((wave + 4 * j) << 7);
+    const int kc = kbeg + ((wave + NW * j) << 7);
     const int slot = j % D;
     if (kc + 128 <= kend) {
 #pragma unroll
@@ -1416,7 +1418,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_splitk_partial_kernel(SkinnyArgs 
       for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = mfma16<FMT>(af[rb], bf[mb], acc[rb][mb]);
   }
 
-  skinny_finish<RB, MB, EPI>(acc, a, (float *)smem, n0, s, wave, lane);
+  skinny_finish<RB, MB, EPI, NW>(acc, a, (float *)smem, n0, s, wave, lane);
 }
 
 // Direct variant of the skinny kernel: no LDS in the K loop.  Every lane
@@ -1633,27 +1635,32 @@ static hipError_t launch_main5_dp(const MainLaunch &l, hipStream_t stream) {
   });
 }
 
-template <int RB, int MB, bool DIRECT, bool EPI>
+template <int RB, int MB, bool DIRECT, bool EPI, int NW = 4>
 static hipError_t launch_skinny_cfg(const SkinnyLaunch &l, hipStream_t stream) {
   SkinnyArgs a{l.x, l.w, l.scale, l.y, l.partials, l.tickets, l.epoch, l.M, l.N, l.K, l.k_slice, l.vec,
                l.bias, l.act};
-  const dim3 grid((unsigned)((l.N + 16 * RB - 1) / (16 * RB)), (unsigned)l.S), block(256);
+  const dim3 grid((unsigned)((l.N + 16 * RB - 1) / (16 * RB)), (unsigned)l.S), block(64 * NW);
   if constexpr (DIRECT) {
     if (l.fmt != 0) return hipErrorInvalidValue;
     return dispatch(fp8g_skinny_direct_kernel<RB, MB, 4, EPI>, grid, block, stream, l.ev, a);
   } else {
     return with_format(l.fmt, [&](auto fmt) {
       constexpr int F = decltype(fmt)::value;
-      return dispatch(fp8g_splitk_partial_kernel<RB, MB, F, EPI>, grid, block, stream, l.ev, a);
+      return dispatch(fp8g_splitk_partial_kernel<RB, MB, F, EPI, NW>, grid, block, stream, l.ev, a);
     });
   }
 }
 
-// Split-K variants 1-5 (LDS ring) and, with EPI, 11-15 (direct to registers,
-// always built with the general epilogue).
+// Split-K variants 1-5 (LDS ring, 4 waves), 21-24 (LDS ring, 8 waves, rings two
+// chunks deep) and, with EPI, 11-15 (direct to registers, always built with the
+// general epilogue).
 template <int MB, bool EPI>
 static hipError_t launch_skinny_mb(const SkinnyLaunch &l, hipStream_t stream) {
   switch (l.variant) {
+    case 21: return launch_skinny_cfg<1, MB, false, EPI, 8>(l, stream);
+    case 22: if constexpr (MB <= 2) return launch_skinny_cfg<2, MB, false, EPI, 8>(l, stream); else break;
+    case 23: if constexpr (MB <= 2) return launch_skinny_cfg<3, MB, false, EPI, 8>(l, stream); else break;
+    case 24: if constexpr (MB == 1) return launch_skinny_cfg<4, MB, false, EPI, 8>(l, stream); else break;
     case 1: return launch_skinny_cfg<1, MB, false, EPI>(l, stream);
     case 2: return launch_skinny_cfg<2, MB, false, EPI>(l, stream);
     case 3: if constexpr (MB <= 2) return launch_skinny_cfg<3, MB, false, EPI>(l, stream); else break;

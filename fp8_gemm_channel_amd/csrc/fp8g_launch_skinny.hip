@@ -6,7 +6,7 @@
 namespace fp8g {
 
 hipError_t launch_skinny(const SkinnyLaunch &l, hipStream_t stream) {
-  if (has_epilogue(l) || l.variant > 10) return launch_skinny_epi(l, stream);
+  if (has_epilogue(l) || (l.variant > 10 && l.variant < 21)) return launch_skinny_epi(l, stream);
   return launch_skinny_t<false>(l, stream);
 }
 

@@ -81,6 +81,11 @@ def test_plan_overrides():
     # split_k larger than the number of 128-byte chunks collapses to non-empty slices
     p = fg.fp8_gemm_plan_ex(8, 100, 300, fg.PATH_SPLITK, 0, 8)
     assert p["split_k"] == 3 and p["k_slice"] == 128
+    # 8-wave LDS-ring variants: 16 * (variant - 20) w rows, fewer rows for wider x
+    p = fg.fp8_gemm_plan_ex(32, 12288, 4096, fg.PATH_SPLITK, 23, 1)
+    assert p["variant"] == 23 and p["tile_n"] == 48 and p["grid"] == 256 and p["workspace_bytes"] == 0
+    assert fg.fp8_gemm_plan_ex(16, 1000, 4096, fg.PATH_SPLITK, 24, 0)["tile_n"] == 64
+    assert fg.fp8_gemm_plan_ex(64, 1000, 4096, fg.PATH_SPLITK, 21, 0)["tile_m"] == 64
 
 
 @pytest.mark.parametrize("args", [
@@ -113,6 +118,8 @@ def test_plan_row_realignment():
 @pytest.mark.parametrize("kw", [
     dict(path=7), dict(path=fg.PATH_SPLITK, M=65), dict(variant=99), dict(split_k=65),
     dict(split_k=-1), dict(path=fg.PATH_MAIN, split_k=3), dict(path=fg.PATH_SPLITK, variant=9),
+    dict(path=fg.PATH_SPLITK, variant=18), dict(path=fg.PATH_SPLITK, variant=25),
+    dict(path=fg.PATH_SPLITK, variant=24), dict(path=fg.PATH_SPLITK, variant=22, M=40),
 ])
 def test_plan_rejects_bad_overrides(kw):
     M = kw.pop("M", 32)

@@ -70,7 +70,7 @@ def test_main_variants_all_formats(variant, fmts):
     _case(129, 70, 1000, fg.ACT_SILU, *fmts, path=fg.PATH_MAIN, variant=variant)
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 21, 22, 23, 24])
 @pytest.mark.parametrize("fmts", FORMATS[1:], ids=lambda f: f"x{f[0]}w{f[1]}")
 def test_splitk_ring_variants_all_formats(variant, fmts):
     for M in (1, 16, 40, 64):

@@ -99,6 +99,21 @@ def test_splitk_variants(variant):
     _full_case(16, 1000, 4127, path=fg.PATH_SPLITK, variant=variant, split_k=2)
 
 
+@pytest.mark.parametrize("variant", [21, 22, 23, 24])
+def test_splitk_eight_wave_variants(variant):
+    """The LDS-ring kernel with 8 waves (16 * (variant - 20) rows per
+    workgroup), every x-row staging width it supports, with and without
+    split-K, with a K tail and chunk counts that are not multiples of 8."""
+    for M in (1, 16, 32, 40, 64):
+        try:
+            fg.fp8_gemm_plan_ex(M, 777, 3000, path=fg.PATH_SPLITK, variant=variant)
+        except fg.Fp8gError:
+            continue  # more w rows than this M allows
+        _full_case(M, 777, 3000, path=fg.PATH_SPLITK, variant=variant, split_k=3)
+        _full_case(M, 1000, 4127, path=fg.PATH_SPLITK, variant=variant, split_k=1)
+        _full_case(M, 264, 600, path=fg.PATH_SPLITK, variant=variant, split_k=1)
+
+
 @pytest.mark.parametrize("variant", [11, 12, 13, 14, 15])
 @pytest.mark.parametrize("M", [1, 16, 17, 32, 40, 64])
 def test_splitk_direct_variants(variant, M):
