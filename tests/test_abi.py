@@ -88,6 +88,40 @@ def test_plan_overrides():
     assert fg.fp8_gemm_plan_ex(64, 1000, 4096, fg.PATH_SPLITK, 21, 0)["tile_m"] == 64
 
 
+# Split-K picks of the planner on shapes measured on MI355X (cold, events attached to
+# the kernel); each is the best or within 9% of the best of every (variant, S) tried.
+@pytest.mark.parametrize("shape,pick", [
+    ((32, 12288, 4096), (23, 1)),   # decode: 48 rows, 8 waves, 256 workgroups
+    ((1, 12288, 4096), (24, 1)),    # 64 rows when x is at most 16 rows
+    ((32, 1536, 4096), (21, 1)),    # few columns and short K: no K split (96 workgroups)
+    ((8, 1024, 28672), (21, 4)),    # few columns, long K: 4 slices of 7 KiB
+    ((16, 4096, 16384), (24, 4)),
+    ((32, 8192, 8192), (23, 1)),
+    ((64, 12288, 4096), (2, 1)),    # 64 x rows: 4-wave kernel, 32 w rows
+    ((64, 1536, 4096), (1, 2)),
+    ((64, 1024, 28672), (1, 4)),
+])
+def test_plan_splitk_rule(shape, pick):
+    p = fg.fp8_gemm_plan(*shape)
+    assert p["path_name"] == "splitk" and (p["variant"], p["split_k"]) == pick
+
+
+@pytest.mark.parametrize("M", [1, 16, 17, 32, 33, 64])
+@pytest.mark.parametrize("N", [1, 100, 4096, 65536])
+@pytest.mark.parametrize("K", [1, 4127, 100000])
+def test_plan_splitk_invariants(M, N, K):
+    """Every automatic split-K plan: a kernel that exists for this M, slices of
+    whole 128-byte chunks covering K with none empty, and a grid of column tiles
+    times slices."""
+    p = fg.fp8_gemm_plan(M, N, K)
+    v, S = p["variant"], p["split_k"]
+    assert (v in (21, 22, 23, 24)) if M <= 32 else (v in (1, 2))
+    assert p["tile_n"] == 16 * (v - 20 if v > 20 else v)
+    assert p["k_slice"] % 128 == 0 and (S - 1) * p["k_slice"] < K <= S * p["k_slice"]
+    assert p["grid"] == -(-N // p["tile_n"]) * S
+    assert p["workspace_bytes"] == (_splitk_workspace(p, M, N) if S > 1 else 0)
+
+
 @pytest.mark.parametrize("args", [
     (-1, 4, 4), (4, -1, 4), (4, 4, -1), (4, 4, (1 << 24)), (2**31, 4, 4),
 ])
