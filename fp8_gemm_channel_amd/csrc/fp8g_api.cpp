@@ -153,24 +153,25 @@ int64_t slice_bytes(int64_t K, int64_t S) {
 
 // Rows per workgroup (16 * rb), K slices S and kernel of the split-K path when
 // nothing is forced.  Rules fitted to measurements on MI355X (cold cache,
-// M = 1 .. 64, N = 1024 .. 28672, K = 4096 .. 28672; within 1.2% of the best
-// configuration on geometric mean, 9% at worst): up to 32 rows of x, the
-// 8-wave kernel with the most w rows per workgroup that still gives at least
-// 160 workgroups without splitting K (a K split costs ~3 us of partial
-// hand-off); otherwise the most rows for which K slices of at least 4 KiB
-// reach 160 workgroups; otherwise 16 rows unsplit.  With 33 .. 64 rows of x
-// (re-read from L2 by every workgroup), the 4-wave kernel with 32 rows, or 16
-// when 32 cannot reach 256 workgroups, splitting K while slices keep at least
-// 2 KiB per 16 rows.
+// every configuration of a shape timed in interleaved rounds; M = 1 .. 64,
+// N = 1024 .. 28672, K = 2048 .. 28672; within 1.3% of the best configuration
+// on geometric mean, 9% at worst): up to 32 rows of x, the 8-wave kernel with
+// the most w rows per workgroup that still gives at least 160 workgroups
+// without splitting K (a K split costs ~3 us of partial hand-off); otherwise
+// the most rows for which K slices of at least 4 KiB reach 160 workgroups;
+// otherwise 16 rows unsplit.  With 33 .. 64 rows of x (re-read from L2 by
+// every workgroup), the 4-wave kernel with 32 rows, or 16 when 32 cannot
+// reach 160 workgroups, splitting K while slices keep at least 2 KiB per 16
+// rows.
 void auto_splitk(int64_t M, int64_t N, int64_t K, int64_t *rb_out, int64_t *S_out, int *kind_base) {
   auto grow = [&](int64_t nb, int64_t target, int64_t min_slice) {
     int64_t S = 1;
     while (nb * S < target && S < kMaxSplit && slice_bytes(K, 2 * S) >= min_slice) S *= 2;
     return S;
   };
+  constexpr int64_t kMinWorkgroups = 160;
   if (M <= 32) {
     const int max_rb = fp8g::skinny_max_row_blocks((int)M, fp8g::SkinnyKind::kRing8);
-    constexpr int64_t kMinWorkgroups = 160;
     *kind_base = 20;
     for (int rb = max_rb; rb >= 2; --rb)
       if (cdiv(N, 16 * rb) >= kMinWorkgroups) {
@@ -192,8 +193,8 @@ void auto_splitk(int64_t M, int64_t N, int64_t K, int64_t *rb_out, int64_t *S_ou
   }
   *kind_base = 0;
   for (int rb = 2; rb >= 1; --rb) {
-    const int64_t nb = cdiv(N, 16 * rb), S = grow(nb, kNumCUs, 2048 * rb);
-    if (nb * S >= kNumCUs || rb == 1) {
+    const int64_t nb = cdiv(N, 16 * rb), S = grow(nb, kMinWorkgroups, 2048 * rb);
+    if (nb * S >= kMinWorkgroups || rb == 1) {
       *rb_out = rb;
       *S_out = S;
       return;

@@ -100,6 +100,7 @@ def test_plan_overrides():
     ((64, 12288, 4096), (2, 1)),    # 64 x rows: 4-wave kernel, 32 w rows
     ((64, 1536, 4096), (1, 2)),
     ((64, 1024, 28672), (1, 4)),
+    ((64, 7168, 2048), (2, 1)),     # 32 rows reach 160 workgroups: 16 rows would re-read x twice as often
 ])
 def test_plan_splitk_rule(shape, pick):
     p = fg.fp8_gemm_plan(*shape)
