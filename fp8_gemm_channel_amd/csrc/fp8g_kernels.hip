@@ -115,9 +115,9 @@ const SkinnyConfig *skinny_config(int id) {
 int skinny_tile_n(const SkinnyConfig &c) { return 16 * c.row_blocks; }
 int skinny_max_row_blocks(int M, SkinnyKind kind) {
   switch (kind) {
-    case SkinnyKind::kDirect: return 5;  // register ring: (RB + MB) * 8 * 4 VGPRs of operands
-    case SkinnyKind::kRing8: return M <= 16 ? 4 : (M <= 32 ? 3 : 1);  // 8 rings of 2 slots in LDS
-    default: return M <= 16 ? 5 : (M <= 32 ? 4 : 2);  // 4 rings of 3 slots in LDS
+    case SkinnyKind::kDirect: return M <= 64 ? 5 : 0;  // register ring: (RB + MB) * 8 * 4 VGPRs of operands
+    case SkinnyKind::kRing8: return M <= 16 ? 4 : (M <= 32 ? 3 : (M <= 64 ? 1 : 0));  // 8 rings of 2 slots
+    default: return M <= 16 ? 5 : (M <= 32 ? 4 : 2);  // 4 rings of 3 slots (2 with 128 x rows)
   }
 }
 int skinny_chunk_bytes() { return 128; }

@@ -1095,9 +1095,9 @@ __global__ __launch_bounds__(512, 1) void fp8g_main5_kernel(MainArgs a) {
 
 // ---------------------------------------------------------------- skinny path
 //
-// M <= 64 (decode-shaped): the time is the stream of w through HBM.  A workgroup
-// owns R = 16*RB rows of w (output columns) and one K slice.  Its four waves take
-// the slice's 128-byte K chunks round-robin (wave v: chunks v, v+4, v+8, ...), so
+// M <= 128 (decode-shaped): the time is the stream of w through HBM.  A workgroup
+// owns R = 16*RB rows of w (output columns) and one K slice.  Its NW waves (4 or
+// 8) take the slice's 128-byte K chunks round-robin (wave v: chunks v, v+NW, ...), so
 // together they read every w row front to back.  Each wave streams its chunks --
 // R rows of w and 16*MB rows of x, 128 bytes each -- into a private ring of D LDS
 // slots with LDS-DMA, one 1 KiB instruction per 8 rows, and multiplies them with
@@ -1105,7 +1105,7 @@ __global__ __launch_bounds__(512, 1) void fp8g_main5_kernel(MainArgs a) {
 // the non-temporal policy (read once; on gfx950 this roughly doubles streaming
 // read bandwidth), x without it (every workgroup re-reads x, so it should stay in
 // L2).  No barrier is needed in the K loop because no wave reads another wave's
-// slots; completion is tracked with vmcnt.  At the end the four per-wave sums are
+// slots; completion is tracked with vmcnt.  At the end the per-wave sums are
 // added through LDS in wave order, so results are deterministic.
 //
 // MFMA 16x16x128 layout (gfx950, checked on the hardware): operand lane l supplies
@@ -1139,7 +1139,8 @@ struct SkinnyShape {
   static constexpr int ROWS = R + MX;
   static constexpr int SLOT = ROWS * 128;  // bytes per ring slot
   static constexpr int OPS = ROWS / 8;     // 1 KiB DMA instructions per chunk
-  static constexpr int D = NW == 4 ? 3 : 2;  // ring depth (chunks in flight per wave)
+  // ring depth (chunks in flight per wave): 3 with 4 waves, 2 with 8 or with 128 x rows
+  static constexpr int D = NW * 3 * SLOT <= 160 * 1024 ? 3 : 2;
   static constexpr int WAVE_LDS = D * SLOT;
   static_assert(NW * WAVE_LDS <= 160 * 1024, "LDS");
   static_assert((D - 1) * OPS < 64, "vmcnt range");
@@ -1657,7 +1658,7 @@ static hipError_t launch_skinny_cfg(const SkinnyLaunch &l, hipStream_t stream) {
 template <int MB, bool EPI>
 static hipError_t launch_skinny_mb(const SkinnyLaunch &l, hipStream_t stream) {
   switch (l.variant) {
-    case 21: return launch_skinny_cfg<1, MB, false, EPI, 8>(l, stream);
+    case 21: if constexpr (MB <= 4) return launch_skinny_cfg<1, MB, false, EPI, 8>(l, stream); else break;
     case 22: if constexpr (MB <= 2) return launch_skinny_cfg<2, MB, false, EPI, 8>(l, stream); else break;
     case 23: if constexpr (MB <= 2) return launch_skinny_cfg<3, MB, false, EPI, 8>(l, stream); else break;
     case 24: if constexpr (MB == 1) return launch_skinny_cfg<4, MB, false, EPI, 8>(l, stream); else break;
@@ -1668,7 +1669,7 @@ static hipError_t launch_skinny_mb(const SkinnyLaunch &l, hipStream_t stream) {
     case 5: if constexpr (MB == 1) return launch_skinny_cfg<5, MB, false, EPI>(l, stream); else break;
     default: break;
   }
-  if constexpr (EPI) {
+  if constexpr (EPI && MB <= 4) {
     switch (l.variant) {
       case 11: return launch_skinny_cfg<1, MB, true, true>(l, stream);
       case 12: return launch_skinny_cfg<2, MB, true, true>(l, stream);
@@ -1685,7 +1686,8 @@ template <bool EPI>
 static hipError_t launch_skinny_t(const SkinnyLaunch &l, hipStream_t stream) {
   if (l.M <= 16) return launch_skinny_mb<1, EPI>(l, stream);
   if (l.M <= 32) return launch_skinny_mb<2, EPI>(l, stream);
-  return launch_skinny_mb<4, EPI>(l, stream);
+  if (l.M <= 64) return launch_skinny_mb<4, EPI>(l, stream);
+  return launch_skinny_mb<8, EPI>(l, stream);
 }
 
 }  // namespace fp8g

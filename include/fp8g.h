@@ -116,15 +116,19 @@ int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y,
 
 /* Same operation with parts of the plan forced, for tests and tuning.  Each
  * override is 0 for "let the planner choose":
- *   path    : FP8G_PATH_MAIN or FP8G_PATH_SPLITK (SPLITK needs M <= 64)
+ *   path    : FP8G_PATH_MAIN or FP8G_PATH_SPLITK (SPLITK needs M <= 128)
  *   variant : a configuration id valid for the path (fp8_gemm_plan_ex reports
  *             the tile it implies).  Main path: 10 = 256x256 tiles, five LDS
  *             slots (the large-grid default); 17 = 128x256 and 18 = 128x128
  *             (mid M); 3 = 64x64 (small problems); 2 = 128x128 four waves;
  *             1, 4-7, 9 = other 256x256 schedules; 16 = variant 10 with
  *             stream-K (opt-in).  Split-K path: 1-5 = 16*v w rows per
- *             workgroup through an LDS ring (default kernel), 11-15 = the
- *             same row counts loading straight into registers (K >= 16).
+ *             workgroup through per-wave LDS rings, 4 waves (the default for
+ *             M > 32); 21-24 = 16*(v-20) rows with 8 waves (the default for
+ *             M <= 32); 11-15 = 16*(v-10) rows loading straight into
+ *             registers (K >= 16).  Row counts are limited by M (the staged x
+ *             rows share the LDS): 1-5 up to 5/4/2 blocks for M <= 16/32/128,
+ *             21-24 up to 4/3/1 blocks for M <= 16/32/64, 11-15 need M <= 64.
  *   split_k : splitk path: 1..64 K slices; main path variant 16: 1..2048
  *             stream-K workgroups; other main variants, for K % 128 != 0:
  *             1 = read operand rows in place, 2 = realign them (pad_k)

@@ -45,7 +45,7 @@ def _splitk_workspace(p, M, N):
 @pytest.mark.parametrize("wl", synth.WORKLOADS, ids=lambda w: w.name)
 def test_plan_of_benchmark_shapes(wl):
     p = fg.fp8_gemm_plan(wl.M, wl.N, wl.K)
-    if wl.M <= 64:
+    if wl.M <= 128:
         assert p["path_name"] == "splitk"
         assert p["split_k"] >= 1 and p["k_slice"] * p["split_k"] >= wl.K
         assert (p["split_k"] - 1) * p["k_slice"] < wl.K, "no empty slice"
@@ -68,8 +68,9 @@ def test_plan_special_extents():
     assert fg.fp8_gemm_plan(5, 6, 0)["path_name"] == "zero"
     p = fg.fp8_gemm_plan(1, 1, 1)
     assert p["path_name"] == "splitk" and p["split_k"] == 1 and p["k_tail"] == 1
-    p = fg.fp8_gemm_plan(65, 1, 1)
+    p = fg.fp8_gemm_plan(129, 1, 1)
     assert p["path_name"] == "main" and p["k_tail"] == 1
+    assert fg.fp8_gemm_plan(128, 1, 1)["path_name"] == "splitk"
 
 
 def test_plan_overrides():
@@ -107,7 +108,7 @@ def test_plan_splitk_rule(shape, pick):
     assert p["path_name"] == "splitk" and (p["variant"], p["split_k"]) == pick
 
 
-@pytest.mark.parametrize("M", [1, 16, 17, 32, 33, 64])
+@pytest.mark.parametrize("M", [1, 16, 17, 32, 33, 64, 65, 128])
 @pytest.mark.parametrize("N", [1, 100, 4096, 65536])
 @pytest.mark.parametrize("K", [1, 4127, 100000])
 def test_plan_splitk_invariants(M, N, K):
@@ -151,10 +152,12 @@ def test_plan_row_realignment():
 
 
 @pytest.mark.parametrize("kw", [
-    dict(path=7), dict(path=fg.PATH_SPLITK, M=65), dict(variant=99), dict(split_k=65),
+    dict(path=7), dict(variant=99), dict(split_k=65),
     dict(split_k=-1), dict(path=fg.PATH_MAIN, split_k=3), dict(path=fg.PATH_SPLITK, variant=9),
     dict(path=fg.PATH_SPLITK, variant=18), dict(path=fg.PATH_SPLITK, variant=25),
     dict(path=fg.PATH_SPLITK, variant=24), dict(path=fg.PATH_SPLITK, variant=22, M=40),
+    dict(path=fg.PATH_SPLITK, M=129), dict(path=fg.PATH_SPLITK, variant=3, M=65),
+    dict(path=fg.PATH_SPLITK, variant=21, M=65), dict(path=fg.PATH_SPLITK, variant=11, M=65),
 ])
 def test_plan_rejects_bad_overrides(kw):
     M = kw.pop("M", 32)

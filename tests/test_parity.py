@@ -114,6 +114,17 @@ def test_splitk_eight_wave_variants(variant):
         _full_case(M, 264, 600, path=fg.PATH_SPLITK, variant=variant, split_k=1)
 
 
+@pytest.mark.parametrize("M", [65, 100, 128])
+def test_splitk_up_to_128_x_rows(M):
+    """The 4-wave ring kernel with 128 staged x rows (two chunks deep), forced
+    onto the split-K path: both row counts, with and without split-K and a
+    K tail, plus the planner's own pick."""
+    for variant in (1, 2):
+        _full_case(M, 777, 3000, path=fg.PATH_SPLITK, variant=variant, split_k=3)
+        _full_case(M, 1000, 4127, path=fg.PATH_SPLITK, variant=variant, split_k=1)
+    _full_case(M, 264, 600, path=fg.PATH_SPLITK)
+
+
 @pytest.mark.parametrize("variant", [11, 12, 13, 14, 15])
 @pytest.mark.parametrize("M", [1, 16, 17, 32, 40, 64])
 def test_splitk_direct_variants(variant, M):
