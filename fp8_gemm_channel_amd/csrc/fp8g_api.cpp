@@ -68,8 +68,10 @@ std::mutex g_pool_mutex;
 hipMemPool_t g_pools[kMaxDevices] = {};
 
 hipError_t workspace_alloc(void **ptr, size_t bytes, hipStream_t stream) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
+  // the pool of the device the stream runs on (the kernels run there too,
+  // whatever device is current)
+  hipDevice_t dev = -1;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   hipMemPool_t pool;

@@ -38,10 +38,11 @@
  * Ownership and threading: the caller owns every buffer.  The library keeps no
  * data between calls; its only globals are a thread-local copy of the last
  * error message, an atomic call counter (ids for split-K tickets) and one
- * memory pool per device for call workspaces (created on first use; freed
- * workspace memory stays in the pool for reuse until the process ends).  Calls are asynchronous: they enqueue kernels on
- * `stream` (a hipStream_t; NULL is the default stream) and return without
- * synchronising.  Buffers must stay valid until that work has finished.
+ * memory pool per device for call workspaces (created on first use, under a
+ * lock; freed workspace memory stays in the pool for reuse until the process
+ * ends).  Calls are asynchronous: they enqueue kernels on `stream` (a
+ * hipStream_t; NULL is the default stream) and return without synchronising.
+ * Buffers must stay valid until that work has finished.
  */
 #ifndef FP8G_H
 #define FP8G_H
@@ -105,7 +106,8 @@ typedef struct fp8g_plan {
  *                    x, w or scale.  y is fully overwritten.
  *   M, N, K        : 0 <= M, N <= FP8G_MAX_MN, 0 <= K <= FP8G_MAX_K.
  *                    M == 0 or N == 0 enqueues nothing; K == 0 writes +0.
- *   stream         : hipStream_t, or NULL for the default stream.
+ *   stream         : hipStream_t, or NULL for the default stream of the current
+ *                    device; the buffers must be on the stream's device.
  * Returns FP8G_OK, FP8G_ERR_INVALID_ARG (bad sizes, null pointers with non-zero
  * extent, misaligned scale/y, overlapping output), or FP8G_ERR_HIP (no device,
  * launch failure, or failure to allocate the call's workspace; that is
