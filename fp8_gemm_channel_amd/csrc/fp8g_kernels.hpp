@@ -146,13 +146,16 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// fp32 -> bf16 bits, round to nearest, ties to even; NaN -> 0x7FC0.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// fp32 pair -> bf16 bits packed (lo in bits 0-15), round to nearest, ties to
+// even, NaN stays NaN: one V_CVT_PK_BF16_F32 (bf16 keeps the fp32 exponent
+// range, so only the mantissa is rounded; denormals are kept).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+// One value: the low half of the pair.
+__device__ __forceinline__ uint32_t bf16_rne(float f) { return bf16x2_rne(f, 0.0f) & 0xFFFFu; }
 
 // Operand formats of the f8f6f4 MFMAs as one template parameter:
 // FMT = (w format << 1) | x format, with 0 = E4M3 and 1 = E5M2 (the
@@ -356,12 +359,10 @@ __device__ __forceinline__ void main_epilogue_t(const v16f (&acc)[BN / WN / 32][
 #pragma unroll
       for (int jm = 0; jm < FM; ++jm) {
         const int ml = wave_m * TM + 32 * jm + lr;
-        const uint32_t b0 = bf16_rne(val(acc[i][jm][4 * qd + 0], sc.x, bi.x));
-        const uint32_t b1 = bf16_rne(val(acc[i][jm][4 * qd + 1], sc.y, bi.y));
-        const uint32_t b2 = bf16_rne(val(acc[i][jm][4 * qd + 2], sc.z, bi.z));
-        const uint32_t b3 = bf16_rne(val(acc[i][jm][4 * qd + 3], sc.w, bi.w));
+        const uint32_t p01 = bf16x2_rne(val(acc[i][jm][4 * qd + 0], sc.x, bi.x), val(acc[i][jm][4 * qd + 1], sc.y, bi.y));
+        const uint32_t p23 = bf16x2_rne(val(acc[i][jm][4 * qd + 2], sc.z, bi.z), val(acc[i][jm][4 * qd + 3], sc.w, bi.w));
         const int off = ml * PITCH + (((nl >> 3) ^ (ml & (CPR - 1))) << 4) + ((nl & 7) << 1);
-        *(uint2 *)(smem + off) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        *(uint2 *)(smem + off) = make_uint2(p01, p23);
       }
     }
   }
