@@ -21,6 +21,9 @@ MI355X roofline t_roof / t, with t_roof = max(FLOPs / 5.0 PFLOP/s dense fp8,
 algorithmic bytes / 8.0 TB/s).  `value` is the geometric mean of the five
 fractions.  `roofline` describes the dominant kernel (the main kernel on the
 8192^3 shape); `cpu_baseline` times the CPU oracle on a bounded sample.
+After the timed steps, a shape whose plan realigns its operand rows by a copy
+(odd K) is also timed reading the rows in place, with no copy
+(`in_place_median_us`); that side run is not part of `value`.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
 """
@@ -220,6 +223,25 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # Outside the timed steps: where the plan realigns operand rows with a copy
+    # (K % 128 != 0 on a large GEMM), also time the same call reading the rows
+    # in place, with no copy (split_k override 1), cold, events attached.
+    in_place = {}
+    for wl in workloads:
+        if fg.fp8_gemm_plan(wl.M, wl.N, wl.K)["pad_k"] == 0:
+            continue
+        xd, wd, sd, yd = dev_bufs[wl.name]
+        k0, k1 = kev[wl.name]
+        ts = []
+        for i in range(max(3, min(args.steps, 20))):
+            if not args.no_flush:
+                flush.fill_(i)
+            fg.fp8_gemm(xd, wd, sd, out=yd, split_k=1, stream=stream, events=(k0, k1))
+            k1.synchronize()
+            ts.append(k0.elapsed_time(k1) * 1e-3)
+        in_place[wl.name] = float(np.median(ts[1:]))
+        log(f"{wl.name:>12}: rows read in place (no copy) {in_place[wl.name]*1e6:9.2f} us")
+
     per, fracs = [], []
     for wl in workloads:
         t = np.array(times[wl.name])
@@ -234,6 +256,8 @@ def main() -> int:
                     "min_us": round(float(t.min()) * 1e6, 2), "tflops": round(wl.flops / med / 1e12, 1),
                     "gbps": round(wl.bytes / med / 1e9, 1), "bound": bound_of(wl),
                     "fraction": round(frac, 4)})
+        if wl.name in in_place:
+            per[-1]["in_place_median_us"] = round(in_place[wl.name] * 1e6, 2)
         log(f"{wl.name:>12}: {med*1e6:9.2f} us  {wl.flops/med/1e12:7.1f} TFLOP/s  "
             f"{wl.bytes/med/1e9:7.1f} GB/s  frac {frac:.4f} ({bound_of(wl)})")
     geo = math.exp(sum(math.log(f) for f in fracs) / len(fracs))
@@ -275,7 +299,8 @@ def main() -> int:
         "config": {"workload": "5-shape sweep: " + ", ".join(f"{w.name} {w.M}x{w.N}x{w.K}" for w in workloads),
                    "cache": "warm" if args.no_flush else "cold (512 MiB rewrite before each GEMM)"},
         "timing": "HIP events attached to each call's first and last kernel (hipExtLaunchKernel); "
-                  "marker_median_us / value_marker_timed: a hipEventRecord pair around a second cold call",
+                  "marker_median_us / value_marker_timed: a hipEventRecord pair around a second cold call; "
+                  "in_place_median_us (untimed side run): the odd-K call without its row-realignment copy",
         "value_marker_timed": round(geo_marker, 4),
         "per_config": per,
         "roofline": roofline,
