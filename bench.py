@@ -59,12 +59,13 @@ def bound_of(wl) -> str:
     return "mfma" if wl.flops / (PEAK_FP8_TFLOPS * 1e12) >= wl.bytes / (PEAK_HBM_GBPS * 1e9) else "hbm"
 
 
-# Sources of the dominant kernel (the five-slot main kernel): its templates and
-# the unit that instantiates it.  A traffic summary taken on other sources is
-# not used.
+# Sources of the dominant kernel (the one-wave-per-SIMD main kernel): its
+# templates and the unit that instantiates it.  A traffic summary taken on
+# other sources is not used.
 KERNEL_SOURCES = [os.path.join(ROOT, "fp8_gemm_channel_amd", "csrc", f)
-                  for f in ("fp8g_kernels.hpp", "fp8g_launch_main5.hip")]
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_main5_kernel_square-8192_traffic.md")
+                  for f in ("fp8g_kernels.hpp", "fp8g_launch_main4w.hip")]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_main4w_kernel_square-8192_traffic.md")
+MAIN_KERNEL_NAMES = {10: "fp8g_main5_kernel", 16: "fp8g_main5_kernel", 19: "fp8g_main4w_kernel"}
 
 
 def kernel_source_hash() -> str:
@@ -270,7 +271,7 @@ def main() -> int:
     dom_t = float(np.mean(times[dom.name]))
     dom_plan = fg.fp8_gemm_plan(dom.M, dom.N, dom.K)
     roofline = {"bound": bound_of(dom),
-                "kernel": f"{'fp8g_main5_kernel' if dom_plan['variant'] == 10 else 'fp8g_main_kernel'} "
+                "kernel": f"{MAIN_KERNEL_NAMES.get(dom_plan['variant'], 'fp8g_main_kernel')} "
                           f"(main variant {dom_plan['variant']}) on {dom.name}"
                 if dom_plan["path_name"] == "main" else f"{dom_plan['path_name']} on {dom.name}",
                 "achieved": round(dom.flops / dom_t / 1e12, 1) if bound_of(dom) == "mfma"

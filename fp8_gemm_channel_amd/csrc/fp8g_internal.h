@@ -83,6 +83,8 @@ int skinny_chunk_bytes();                   // K granularity of one wave iterati
 hipError_t launch_main(const MainLaunch &l, hipStream_t stream);
 hipError_t launch_main5(const MainLaunch &l, hipStream_t stream);            // variants 10, 16
 hipError_t launch_main5_epi(const MainLaunch &l, hipStream_t stream);        // variant 10, bias / activation
+hipError_t launch_main4w(const MainLaunch &l, hipStream_t stream);           // variant 19
+hipError_t launch_main4w_epi(const MainLaunch &l, hipStream_t stream);       // variant 19, bias / activation
 hipError_t launch_main_tiles(const MainLaunch &l, hipStream_t stream);       // variants 3, 17, 18
 hipError_t launch_main_tiles_epi(const MainLaunch &l, hipStream_t stream);   // the same, bias / activation
 hipError_t launch_main_legacy(const MainLaunch &l, hipStream_t stream);      // variants 1, 2, 4-7, 9

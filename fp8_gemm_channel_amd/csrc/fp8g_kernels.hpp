@@ -1426,6 +1426,311 @@ __global__ __launch_bounds__(64 * NW, 1) void fp8g_splitk_partial_kernel(SkinnyA
   skinny_finish<RB, MB, EPI, NW>(acc, a, (float *)smem, n0, s, wave, lane);
 }
 
+// Epilogue for accumulators of V_MFMA_F32_16X16X128_F8F6F4 (A = w, B = x):
+// lane l, element e of block (i, j) is n = 16 i + 4 (l / 16) + e and
+// m = 16 j + l % 16 of the wave tile, four consecutive n of one m.  Same
+// arithmetic (scale, bias, activation in fp32), staging through LDS and
+// whole-row stores as main_epilogue_t.
+template <int BM, int BN, int WM, int WN, int ACT, bool BIAS>
+__device__ __forceinline__ void main_epilogue16_t(const v4f (&acc)[BN / WN / 16][BM / WM / 16], const MainArgs &a,
+                                                  uint8_t *smem, const float *s_lds, const float *b_lds, int m0,
+                                                  int n0, int wave, int lane, int tid) {
+  constexpr int NWAVES = WM * WN, TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+  constexpr int CPR = BN / 8, PITCH = 2 * BN, NTHREADS = NWAVES * 64;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int wave_m = wave % WM, wave_n = wave / WM;
+  __syncthreads();  // s_lds (and b_lds) are published
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    const int nl = wave_n * TN + 16 * i + 4 * g;
+    const float4 sc = *(const float4 *)(s_lds + nl);
+    float4 bi = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (BIAS) bi = *(const float4 *)(b_lds + nl);
+    auto val = [&](float v, float scl, float bs) __attribute__((always_inline)) {
+      float z = v * scl;
+      if constexpr (BIAS) z += bs;
+      return activation<ACT>(z);
+    };
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int ml = wave_m * TM + 16 * j + l16;
+      const uint32_t p01 = bf16x2_rne(val(acc[i][j][0], sc.x, bi.x), val(acc[i][j][1], sc.y, bi.y));
+      const uint32_t p23 = bf16x2_rne(val(acc[i][j][2], sc.z, bi.z), val(acc[i][j][3], sc.w, bi.w));
+      const int off = ml * PITCH + (((nl >> 3) ^ (ml & (CPR - 1))) << 4) + ((nl & 7) << 1);
+      *(uint2 *)(smem + off) = make_uint2(p01, p23);
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < BM * CPR; idx += NTHREADS) {
+    const int r = idx / CPR, c = idx % CPR;
+    const int m = m0 + r, n = n0 + 8 * c;
+    if (m >= a.M || n >= a.N) continue;
+    const uint4 v = *(const uint4 *)(smem + r * PITCH + ((c ^ (r & (CPR - 1))) << 4));
+    uint16_t *dst = a.y + (size_t)m * a.N + n;
+    if (a.ystore == 16) {  // whole 16-byte chunk, written once: non-temporal
+      __builtin_nontemporal_store(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, (v4i *)dst);
+    } else if (a.ystore == 8) {
+      *(uint2 *)dst = make_uint2(v.x, v.y);
+      if (n + 4 < a.N) *(uint2 *)(dst + 4) = make_uint2(v.z, v.w);
+    } else {
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < a.N) dst[e] = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+// main_epilogue16_t for the call's activation and bias (one uniform switch);
+// built without EPI, only the plain operation is compiled.
+template <int BM, int BN, int WM, int WN, bool EPI>
+__device__ __forceinline__ void main_epilogue16(const v4f (&acc)[BN / WN / 16][BM / WM / 16], const MainArgs &a,
+                                                uint8_t *smem, const float *s_lds, const float *b_lds, int m0,
+                                                int n0, int wave, int lane, int tid) {
+  if constexpr (!EPI) {
+    main_epilogue16_t<BM, BN, WM, WN, kActNone, false>(acc, a, smem, s_lds, b_lds, m0, n0, wave, lane, tid);
+    return;
+  }
+  const int sel = a.act * 2 + (a.bias != nullptr ? 1 : 0);
+#define FP8G_EPI(ACT, BIAS) \
+  main_epilogue16_t<BM, BN, WM, WN, ACT, BIAS>(acc, a, smem, s_lds, b_lds, m0, n0, wave, lane, tid)
+  switch (sel) {
+    case 1: FP8G_EPI(kActNone, true); break;
+    case 2: FP8G_EPI(kActRelu, false); break;
+    case 3: FP8G_EPI(kActRelu, true); break;
+    case 4: FP8G_EPI(kActSilu, false); break;
+    case 5: FP8G_EPI(kActSilu, true); break;
+    case 6: FP8G_EPI(kActGeluTanh, false); break;
+    case 7: FP8G_EPI(kActGeluTanh, true); break;
+    default: FP8G_EPI(kActNone, false); break;
+  }
+#undef FP8G_EPI
+}
+
+// ------------------------------------------- main path, one wave per SIMD
+//
+// 256 x 256 tiles and 128-byte K steps with four waves, each owning a 128 (m) x
+// 128 (n) quarter of the tile as 8 x 8 blocks of V_MFMA_F32_16X16X128_F8F6F4.
+// Per K step a quarter reads 32 KiB of operands from LDS, where two 64 x 128
+// wave tiles read 48 KiB.
+//
+// With one wave per SIMD nothing covers a wave's waits, so the feed must run
+// further ahead, in the same 160 KiB.  LDS holds ten 16 KiB units; a unit is
+// one K step of half the tile's w rows or half its x rows: L = rows 0-63 and
+// 128-191 (blocks 0-3 of both wave tiles), H = rows 64-127 and 192-255 (blocks
+// 4-7).  A step runs as four quadrants of 16 MFMAs, with a barrier after the
+// second and after the fourth:
+//
+//     Q1  w L x x L   reads x H (s)          DMA L units of s + 2 (first half)
+//     Q2  w L x x H   reads w H (s)          DMA L units of s + 2 (second half)
+//         barrier M_s: publishes w L, x L (s + 1); retires the H units of s
+//     Q3  w H x x L   reads w L (s + 1)      DMA H units of s + 3 (first half)
+//     Q4  w H x x H   reads x L (s + 1)      DMA H units of s + 3 (second half)
+//         barrier E_s: publishes the H units of s + 1; retires the L units of s + 1
+//
+// Operands are single-buffered in registers (A[8] w blocks, B[8] x blocks):
+// each read overwrites a block after its last use in the step.  An H unit is
+// requested 2-2.5 steps before it is published and an L unit 1-1.5 steps (H
+// units cycle through three slots per operand, L units through two: 3 + 3 + 2
+// + 2 = 10).  Every read and DMA is pinned next to its MFMA by a scheduling
+// barrier: left to the compiler, a quadrant's DMAs went out in one burst at its
+// start and the issuing wave -- the only one on its SIMD -- stalled behind
+// them (the kernel ran 8% slower).  Rows of a unit are stored with the 16-row
+// swizzle swz16.  K % 128 == 0 only (odd K runs on realigned rows).
+template <int FMT = 0, bool EPI = false>
+__global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
+  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2, NWAVES = 4;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+  constexpr int UNIT = 128 * BK;               // 16 KiB
+  constexpr int UDPW = UNIT / 1024 / NWAVES;   // LDS-DMA instructions per wave per unit (4)
+  static_assert(FM == 8 && FN == 8 && UDPW == 4, "the quadrant schedule assumes 8 x 8 blocks");
+  static_assert(2 * BM * BN + 2 * BN * 4 <= 10 * UNIT, "epilogue tile, scales and biases fit");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[10 * UNIT];
+
+  const int K = a.K;
+  const int nk = K / BK;
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+  auto u_wl = [&](int k) __attribute__((always_inline)) { return (uint32_t)((k & 1) * UNIT); };
+  auto u_xl = [&](int k) __attribute__((always_inline)) { return (uint32_t)((2 + (k & 1)) * UNIT); };
+  auto u_wh = [&](int k) __attribute__((always_inline)) { return (uint32_t)((4 + k % 3) * UNIT); };
+  auto u_xh = [&](int k) __attribute__((always_inline)) { return (uint32_t)((7 + k % 3) * UNIT); };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_m = wave % WM, wave_n = wave / WM;
+  int tm, tn;
+  tile_coords(a, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
+  // A tile's rows form one buffer range; rows past M or N read zero.
+  const v4i rw = make_rsrc(a.w + (size_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
+  const v4i rx = make_rsrc(a.x + (size_t)m0 * K, (uint32_t)rows_x * (uint32_t)K);
+  // The epilogue's scale for column n0 + tid (the oldest vector-memory load:
+  // every DMA wait below covers it).
+  const float my_scale = llvm_buffer_load_f32(make_rsrc(a.scale + n0, (uint32_t)(a.N - n0) * 4u), (uint32_t)tid * 4u, 0, 0);
+  float my_bias = 0.0f;
+  if (EPI && a.bias)
+    my_bias = llvm_buffer_load_f32(make_rsrc(a.bias + n0, (uint32_t)(a.N - n0) * 4u), (uint32_t)tid * 4u, 0, 0);
+
+  // DMA instruction t of a wave fills unit rows (4t + wave) * 8 .. + 7, lane l
+  // taking row (4t + wave) * 8 + l / 8 and logical chunk (l % 8) ^ swz16(row).
+  // Unit row i is tile row i (i < 64) or i + 64, plus 64 for an H unit; the row
+  // offset sits in the VGPR offset, which the buffer range check sees.
+  const int urow = wave * 8 + (lane >> 3);
+  const uint32_t dchunk = (uint32_t)(((lane & 7) ^ swz16(urow)) << 4);
+  uint32_t vo_l[UDPW], vo_h[UDPW];
+#pragma unroll
+  for (int t = 0; t < UDPW; ++t) {
+    const int i = t * NWAVES * 8 + urow;
+    vo_l[t] = (uint32_t)(i + (i >= 64 ? 64 : 0)) * (uint32_t)K + dchunk;
+    vo_h[t] = vo_l[t] + 64u * (uint32_t)K;
+  }
+  auto dma_l = [&](const v4i &rs, uint32_t unit, int k, int t) __attribute__((always_inline)) {
+    dma16(rs, smem_base + unit + (uint32_t)(t * NWAVES + wave) * 1024u, vo_l[t], (uint32_t)k * BK);
+  };
+  auto dma_h = [&](const v4i &rs, uint32_t unit, int k, int t) __attribute__((always_inline)) {
+    dma16(rs, smem_base + unit + (uint32_t)(t * NWAVES + wave) * 1024u, vo_h[t], (uint32_t)k * BK);
+  };
+  // The eight DMA instructions of a step's L (or H) units: w then x.
+  auto issue_l = [&](int k, int q) __attribute__((always_inline)) {
+    if (q < UDPW) dma_l(rw, u_wl(k), k, q);
+    else dma_l(rx, u_xl(k), k, q - UDPW);
+  };
+  auto issue_h = [&](int k, int q) __attribute__((always_inline)) {
+    if (q < UDPW) dma_h(rw, u_wh(k), k, q);
+    else dma_h(rx, u_xh(k), k, q - UDPW);
+  };
+
+  // Operand reads: lane l takes row l % 16 of a 16-row block and logical chunks
+  // 2g, 2g + 1 (g = l / 16), the 32 K bytes of its K group.  Block b of a wave
+  // tile is unit row (wave half) * 64 + (b % 4) * 16 + l % 16.
+  const int g = lane >> 4, l16 = lane & 15;
+  const int sw = swz16(l16);
+  const uint32_t c0 = (uint32_t)(((2 * g) ^ sw) << 4), c1 = (uint32_t)(((2 * g + 1) ^ sw) << 4);
+  const uint32_t ra = (uint32_t)(wave_n * 64 + l16) * BK, rb = (uint32_t)(wave_m * 64 + l16) * BK;
+  auto half16 = [&](uint32_t at, int hf, v8i &f) __attribute__((always_inline)) {
+    const uint4 v = *(const uint4 *)(smem + at + (hf ? c1 : c0));
+    f[4 * hf + 0] = (int)v.x; f[4 * hf + 1] = (int)v.y; f[4 * hf + 2] = (int)v.z; f[4 * hf + 3] = (int)v.w;
+  };
+
+  v4f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8i A[FN], B[FM];
+
+  // Prologue in the steady state's issue order: H(0), L(0), H(1), L(1), H(2);
+  // then wait for H(0) and L(0) (what came after them may stay in flight).
+#pragma unroll
+  for (int q = 0; q < 2 * UDPW; ++q) issue_h(0, q);
+#pragma unroll
+  for (int q = 0; q < 2 * UDPW; ++q) issue_l(0, q);
+  if (nk > 1) {
+#pragma unroll
+    for (int q = 0; q < 2 * UDPW; ++q) issue_h(1, q);
+#pragma unroll
+    for (int q = 0; q < 2 * UDPW; ++q) issue_l(1, q);
+  }
+  if (nk > 2) {
+#pragma unroll
+    for (int q = 0; q < 2 * UDPW; ++q) issue_h(2, q);
+  }
+  if (nk > 2) vm_wait<6 * UDPW>();
+  else if (nk > 1) vm_wait<4 * UDPW>();
+  else vm_wait<0>();
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    half16(u_wl(0) + ra + b * 16 * BK, 0, A[b]);
+    half16(u_wl(0) + ra + b * 16 * BK, 1, A[b]);
+    half16(u_xl(0) + rb + b * 16 * BK, 0, B[b]);
+    half16(u_xl(0) + rb + b * 16 * BK, 1, B[b]);
+  }
+
+  // Step s.  STEADY (s + 3 < nk): every read and DMA of the schedule exists,
+  // so the body has no branches; the last three steps take the guarded body.
+  // In each quadrant the eight reads go out with its first eight MFMAs (so they
+  // have landed by the barrier that retires their unit) and its four DMAs with
+  // MFMAs 1, 5, 9, 13; the MFMAs take their blocks in the order the previous
+  // quadrant read them, so every block is read at least eight MFMAs before its
+  // first use.
+  auto step = [&](const int s, auto steady) __attribute__((always_inline)) {
+    constexpr bool STEADY = decltype(steady)::value;
+    const bool more = STEADY || s + 1 < nk;
+    const bool more2 = STEADY || s + 2 < nk, more3 = STEADY || s + 3 < nk;
+    // Q1: w L x x L (x block-major: B[0..3] arrived in that order); read x H (s)
+    // into B[4..7]; DMA half of the L units of s + 2.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int mb = q >> 2, nb = q & 3;
+      acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
+      if (q < 8) half16(u_xh(s) + rb + (q >> 1) * 16 * BK, q & 1, B[4 + (q >> 1)]);
+      if ((q & 3) == 1 && more2) issue_l(s + 2, q >> 2);
+      __builtin_amdgcn_sched_barrier(0);  // keep the spread as written
+    }
+    // Q2: w L x x H (x block-major); read w H (s) into A[4..7]; DMA the other
+    // half of the L units of s + 2.
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int mb = 4 + (q >> 2), nb = q & 3;
+      acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
+      if (q < 8) half16(u_wh(s) + ra + (q >> 1) * 16 * BK, q & 1, A[4 + (q >> 1)]);
+      if ((q & 3) == 1 && more2) issue_l(s + 2, 4 + (q >> 2));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) {
+      // M_s publishes the L units of s + 1 (this wave issued H(s + 2) and L(s + 2)
+      // after them) and retires the H units of s (read in Q1 and Q2).
+      if (more2) vm_wait<4 * UDPW>();
+      else vm_wait<0>();
+      __syncthreads();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Q3: w H x x L (w block-major: A[4..7] arrived in that order); read w L
+    // (s + 1) into A[0..3]; DMA half of the H units of s + 3.
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int nb = 4 + (q >> 2), mb = q & 3;
+      acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
+      if (more && q < 8) half16(u_wl(s + 1) + ra + (q >> 1) * 16 * BK, q & 1, A[q >> 1]);
+      if ((q & 3) == 1 && more3) issue_h(s + 3, q >> 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Q4: w H x x H; read x L (s + 1) into B[0..3]; DMA the other half of the
+    // H units of s + 3.
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int nb = 4 + (q >> 2), mb = 4 + (q & 3);
+      acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
+      if (more && q < 8) half16(u_xl(s + 1) + rb + (q >> 1) * 16 * BK, q & 1, B[q >> 1]);
+      if ((q & 3) == 1 && more3) issue_h(s + 3, 4 + (q >> 2));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) {
+      // E_s publishes the H units of s + 1; issued after them: L(s + 1), and
+      // H(s + 2), L(s + 2), H(s + 3) where they exist.  Retires the L units of
+      // s + 1 (read in Q3 and Q4).
+      if (more3) vm_wait<8 * UDPW>();
+      else if (more2) vm_wait<6 * UDPW>();
+      else vm_wait<2 * UDPW>();
+      __syncthreads();
+    }
+  };
+  int s = 0;
+  for (; s + 3 < nk; ++s) step(s, std::true_type{});
+  for (; s < nk; ++s) step(s, std::false_type{});
+
+  // Scales (and biases) into LDS past the bf16 tile once every wave is done
+  // with the units.
+  float *s_lds = (float *)(smem + 2 * BM * BN), *b_lds = s_lds + BN;
+  __syncthreads();
+  s_lds[tid] = my_scale;
+  if constexpr (EPI) b_lds[tid] = my_bias;
+  main_epilogue16<BM, BN, WM, WN, EPI>(acc, a, smem, s_lds, b_lds, m0, n0, wave, lane, tid);
+}
+
 // Direct variant of the skinny kernel: no LDS in the K loop.  Every lane
 // loads its own MFMA operands from global memory straight into registers, so
 // neither w nor x passes through LDS and nothing but the final cross-wave sum
@@ -1629,6 +1934,16 @@ static hipError_t launch_main_tiles_t(const MainLaunch &l, hipStream_t stream) {
 }
 
 // The five-slot kernel without stream-K (variant 10).
+template <bool EPI>
+static hipError_t launch_main4w_t(const MainLaunch &l, hipStream_t stream) {
+  if (l.k_tail) return hipErrorInvalidValue;  // K % 128 == 0 (or realigned rows) only
+  const MainArgs a = main_args(l);
+  const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(256);
+  return with_format(l.fmt, [&](auto fmt) {
+    constexpr int F = decltype(fmt)::value;
+    return dispatch(fp8g_main4w_kernel<F, EPI>, grid, block, stream, l.ev, a);
+  });
+}
 template <bool EPI>
 static hipError_t launch_main5_dp(const MainLaunch &l, hipStream_t stream) {
   const MainArgs a = main_args(l);

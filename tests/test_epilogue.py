@@ -70,6 +70,15 @@ def test_main_variants_all_formats(variant, fmts):
     _case(129, 70, 1000, fg.ACT_SILU, *fmts, path=fg.PATH_MAIN, variant=variant)
 
 
+# the one-wave-per-SIMD kernel (K % 128 == 0), every format and activation
+@pytest.mark.parametrize("fmts", FORMATS, ids=lambda f: f"x{f[0]}w{f[1]}")
+def test_main_one_wave_per_simd_all_formats(fmts):
+    _case(300, 520, 256, fg.ACT_GELU_TANH, *fmts, path=fg.PATH_MAIN, variant=19)
+    _case(129, 70, 1024, fg.ACT_SILU, *fmts, path=fg.PATH_MAIN, variant=19)
+    _case(257, 300, 384, fg.ACT_RELU, *fmts, path=fg.PATH_MAIN, variant=19)
+    _case(260, 264, 128, fg.ACT_NONE, *fmts, path=fg.PATH_MAIN, variant=19)
+
+
 @pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 21, 22, 23, 24])
 @pytest.mark.parametrize("fmts", FORMATS[1:], ids=lambda f: f"x{f[0]}w{f[1]}")
 def test_splitk_ring_variants_all_formats(variant, fmts):

@@ -38,6 +38,31 @@ def test_main_variants_full(variant, shape):
     _full_case(*shape, path=fg.PATH_MAIN, variant=variant)
 
 
+# ------------------------- main path, one wave per SIMD (variant 19, K % 128 == 0) --
+# One to five 128-byte K steps (the guarded last three steps alone, then with
+# the branch-free body before them), rows past M and N, a long K, and an odd K
+# through the row realignment.
+V19_SHAPES = [(256, 256, 128), (257, 129, 256), (300, 300, 384), (300, 520, 512), (256, 256, 640),
+              (513, 777, 4096), (40, 700, 1024)]
+
+
+@pytest.mark.parametrize("shape", V19_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_main_one_wave_per_simd(shape):
+    _full_case(*shape, path=fg.PATH_MAIN, variant=19)
+
+
+def test_main_one_wave_per_simd_matches_eight_wave():
+    """Variants 19 and 10 add the same products in the same order: bit for bit
+    the same output, also with realigned rows (odd K)."""
+    for (M, N, K, sk) in [(300, 520, 1024, 0), (513, 264, 4127, 2)]:
+        x, w, s = synth.fp8_inputs(M, N, K, seed=13)
+        say(f"v19 vs v10 {M}x{N}x{K}")
+        a = run(x, w, s, path=fg.PATH_MAIN, variant=19, split_k=sk)
+        b = run(x, w, s, path=fg.PATH_MAIN, variant=10, split_k=sk)
+        assert np.array_equal(a, b)
+        compare(a, oracle.gemm_scaled(x, w, s), f"{M}x{N}x{K} v19")
+
+
 # ------------------------------------------- main path, stream-K (variant 16) --
 # Forced stream-K workgroup counts on small grids: ranges that end inside a
 # tile, ranges that cover several tiles, tiles with one to many contributors,
