@@ -12,7 +12,7 @@ from tests.gpu_util import compare, run, say
 
 pytestmark = pytest.mark.gpu
 
-MAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 16, 17, 18]
+MAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 16, 17, 18, 19]
 SPLITK_VARIANTS = [0, 1, 2, 3, 4, 5, 11, 12, 13, 14, 15, 21, 22, 23, 24]
 
 
