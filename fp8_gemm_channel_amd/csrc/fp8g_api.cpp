@@ -355,15 +355,13 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     }
   }
   p->k_tail = (kk % c->bk) != 0;
-  // Where the 256 x 256 tiles are chosen, they fill at least one wave of
-  // compute units and no K tail is left (K % 128 == 0, or rows realigned
-  // above), the one-wave-per-SIMD kernel runs them: same tiles and the same
-  // sums in the same order, measured 1-6% faster (interleaved with variant 10
-  // on one MI355X: 8192^3 393 vs 418 us, 4096^3 61.7 vs 63.5, 4096 x 8192 x
-  // 4096 123.7 vs 125.7).  With fewer tiles than compute units (3072^3: 144)
-  // its epilogue, half the threads for the same tile, is not hidden by other
-  // tiles' K loops and it measures 3-4% slower.
-  if (auto_variant && variant == 10 && !p->k_tail && tiles_m * tiles_n >= kNumCUs) {
+  // Where the 256 x 256 tiles are chosen and no K tail is left (K % 128 == 0,
+  // or rows realigned above), the one-wave-per-SIMD kernel runs them: same
+  // tiles and the same sums in the same order, measured faster or level
+  // (interleaved with variant 10 on one MI355X: 8192^3 393 vs 418 us,
+  // 1536 x 8192^2 100.5 vs 108.0, 2560 x 4096^2 50.7 vs 52.8, 3072^3 42.0 vs
+  // 42.7, 4096^3 level within 1%).
+  if (auto_variant && variant == 10 && !p->k_tail) {
     variant = 19;
     p->variant = 19;
   }

@@ -124,8 +124,8 @@ int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y,
  *             waves, five LDS slots (large grids); 17 = 128x256 and 18 = 128x128
  *             (mid M); 3 = 64x64 (small problems); 2 = 128x128 four waves;
  *             19 = 256x256 tiles on four waves of 128x128 (the default in
- *             place of 10 when the tiles fill the compute units and no K
- *             tail is left; K % 128 == 0 or realigned rows only);
+ *             place of 10 when no K tail is left; K % 128 == 0 or realigned
+ *             rows only);
  *             1, 4-7, 9 = other 256x256 schedules; 16 = variant 10 with
  *             stream-K (opt-in).  Split-K path: 1-5 = 16*v w rows per
  *             workgroup through per-wave LDS rings, 4 waves (the default for

@@ -152,14 +152,13 @@ def test_plan_row_realignment():
 
 
 def test_plan_main_kernel_choice():
-    """256 x 256 tiles over at least one wave of compute units with no K tail
-    left run on the one-wave-per-SIMD kernel (variant 19); fewer tiles, or a
-    K tail read in place, keep the eight-wave kernel (variant 10)."""
+    """256 x 256 tiles with no K tail left run on the one-wave-per-SIMD kernel
+    (variant 19); a K tail read in place keeps the eight-wave kernel (variant 10)."""
     assert fg.fp8_gemm_plan(8192, 8192, 8192)["variant"] == 19
     assert fg.fp8_gemm_plan(4096, 4096, 4096)["variant"] == 19      # 256 tiles
     odd = fg.fp8_gemm_plan(4096, 4096, 4127)                           # realigned rows
     assert odd["variant"] == 19 and odd["pad_k"] == 4224 and odd["k_tail"] == 0
-    assert fg.fp8_gemm_plan(3072, 3072, 3072)["variant"] == 10      # 144 tiles
+    assert fg.fp8_gemm_plan(3072, 3072, 3072)["variant"] == 19      # 144 tiles
     assert fg.fp8_gemm_plan_ex(4096, 4096, 4127, fg.PATH_MAIN, 0, 1)["variant"] == 10  # in place: tail
     forced = fg.fp8_gemm_plan_ex(300, 300, 384, fg.PATH_MAIN, 19, 0)
     assert forced["variant"] == 19 and forced["grid"] == 4 and forced["tile_k"] == 128
