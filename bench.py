@@ -16,14 +16,16 @@ start when the first kernel begins, stop when the last one ends, as a kernel
 trace times them).  Each step also times a second cold call of each shape
 between a hipEventRecord pair, reported as `marker_median_us` and
 `value_marker_timed`: that pair alone (nothing between the records) costs
-~4.4 us on MI355X, most of the time of a small GEMM.  Per shape: TFLOP/s (GB/s for the memory-bound M=32 shape) and the fraction of the
-MI355X roofline t_roof / t, with t_roof = max(FLOPs / 5.0 PFLOP/s dense fp8,
-algorithmic bytes / 8.0 TB/s).  `value` is the geometric mean of the five
-fractions.  `roofline` describes the dominant kernel (the main kernel on the
-8192^3 shape); `cpu_baseline` times the CPU oracle on a bounded sample.
-After the timed steps, a shape whose plan realigns its operand rows by a copy
-(odd K) is also timed reading the rows in place, with no copy
-(`in_place_median_us`); that side run is not part of `value`.
+~4.4 us on MI355X, most of the time of a small GEMM.  Per shape: TFLOP/s (GB/s
+for the memory-bound M=32 shape) and the fraction of the MI355X roofline
+t_roof / t, with t_roof = max(FLOPs / 5.0 PFLOP/s dense fp8, algorithmic bytes
+/ 8.0 TB/s).  `value` is the geometric mean of the five fractions.  `roofline`
+describes the dominant kernel (the main kernel on the 8192^3 shape): its
+launch time from the attached events of this run, and beside it the average
+from the committed rocprofv3 kernel trace of the same kernel source; the
+shader clock sampled (amdsmi) during the timed steps is reported with the
+fp8 peak it implies.  `cpu_baseline` times the CPU oracle on each full shape,
+one call each.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
 """
@@ -65,6 +67,7 @@ def bound_of(wl) -> str:
 KERNEL_SOURCES = [os.path.join(ROOT, "fp8_gemm_channel_amd", "csrc", f)
                   for f in ("fp8g_kernels.hpp", "fp8g_launch_main4w.hip")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_main4w_kernel_square-8192_traffic.md")
+TRACE_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_5shape_bench_kernel_trace.md")
 MAIN_KERNEL_NAMES = {10: "fp8g_main5_kernel", 16: "fp8g_main5_kernel", 19: "fp8g_main4w_kernel"}
 
 
@@ -77,17 +80,23 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def _summary_fields(path: str) -> dict:
+    """The machine-readable `- key: value` lines of a committed profile summary."""
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    return fields
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter summary, or None when the summary is missing, covers another
     workload, or was taken on a different kernel source."""
     try:
-        fields = {}
-        with open(TRAFFIC_SUMMARY) as f:
-            for line in f:
-                if line.startswith("- ") and ":" in line:
-                    k, v = line[2:].split(":", 1)
-                    fields[k.strip()] = v.strip().strip("`")
+        fields = _summary_fields(TRAFFIC_SUMMARY)
         if fields.get("workload") != workload or fields.get("kernel_source_sha256") != kernel_source_hash():
             return None
         return int(fields["hbm_bytes_per_launch"])
@@ -95,32 +104,82 @@ def measured_traffic(workload: str):
         return None
 
 
-def cpu_baseline(workloads, inputs, budget_fma: float) -> dict:
-    """The CPU oracle on a bounded sample of each shape's outputs: per shape,
-    as many output elements (seeded positions) as fit `budget_fma` products.
-    Its throughput stands in for the whole shape; reported in the same unit
-    as `value` (geomean fraction of the MI355X roofline)."""
+def traced_launch_us(workload: str):
+    """Average launch time (us) of the dominant kernel on `workload` from the
+    committed rocprofv3 kernel trace, or None when the trace is missing or was
+    taken on a different kernel source."""
+    try:
+        fields = _summary_fields(TRACE_SUMMARY)
+        if fields.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return float(fields[f"avg_us_{workload}"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+class ClockSampler:
+    """Samples the GPU's shader (GFX) clock with amdsmi from a background
+    thread while the timed steps run; None fields when amdsmi is unavailable."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.error = [], None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            try:
+                h = amdsmi.amdsmi_get_processor_handles()[0]
+                while not self._stop.is_set():
+                    info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+                    self.samples.append(float(info["clk"]))
+                    self._stop.wait(0.002)
+            finally:
+                amdsmi.amdsmi_shut_down()
+        except Exception as e:  # no amdsmi, no permission: report none
+            self.error = f"{type(e).__name__}: {e}"
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=5)
+
+    def summary(self) -> dict:
+        if not self.samples:
+            return {"sclk_mhz_median": None, "sclk_samples": 0, "sclk_error": self.error}
+        s = np.array(self.samples)
+        return {"sclk_mhz_median": float(np.median(s)), "sclk_mhz_min": float(s.min()),
+                "sclk_mhz_max": float(s.max()), "sclk_samples": int(s.size)}
+
+
+def cpu_baseline(workloads, inputs) -> dict:
+    """The CPU oracle (C, OpenMP, fp64, all host threads) on each full shape,
+    one timed call each (wall clock, inputs already generated); reported in
+    the same unit as `value` (geomean fraction of the MI355X roofline)."""
     import oracle
-    import synth
 
     fracs, per = [], []
+    total = 0.0
     for wl in workloads:
         x, w, s = inputs[wl.name]
-        count = int(max(64, min(wl.M * wl.N, budget_fma // wl.K)))
-        mi, ni = synth.sample_positions(wl.M, wl.N, count - 4, seed=99)
         t0 = time.perf_counter()
-        oracle.gemm_scaled_at(x, w, s, mi, ni)
+        oracle.gemm_scaled(x, w, s)
         dt = time.perf_counter() - t0
-        flops_per_s = 2.0 * wl.K * mi.size / dt
-        t_full = wl.flops / flops_per_s
-        fracs.append(roof_seconds(wl) / t_full)
-        per.append({"workload": wl.name, "outputs": int(mi.size), "seconds": round(dt, 3),
-                    "gflops": round(flops_per_s / 1e9, 2)})
+        total += dt
+        fracs.append(roof_seconds(wl) / dt)
+        per.append({"workload": wl.name, "seconds": round(dt, 3), "gflops": round(wl.flops / dt / 1e9, 2)})
+        log(f"cpu baseline {wl.name}: {dt:.3f} s ({wl.flops / dt / 1e9:.1f} GFLOP/s)")
     return {"value": math.exp(sum(math.log(f) for f in fracs) / len(fracs)),
             "unit": "fraction of MI355X roofline (geomean of 5 shapes)",
             "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": ("per shape, the oracle (C, OpenMP, fp64) on a seeded sample of output elements "
-                       f"sized to {budget_fma:.0e} products; full-shape time extrapolated from its rate"),
+            "sample": (f"the whole workload: each of the {len(workloads)} shapes computed in full by the "
+                       f"oracle (C, OpenMP, fp64), one call each, {total:.1f} s in all"),
             "cpu": _cpu_model(), "per_workload": per}
 
 
@@ -141,7 +200,6 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-flush", action="store_true", help="warm-cache timing (no 512 MiB rewrite)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=4e10, help="oracle products per shape")
     ap.add_argument("--only", default="", help="comma-separated workload names (default: all five)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (3 times); used to "
@@ -218,30 +276,12 @@ def main() -> int:
     for i in range(args.warmup):
         step(False, i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(True, i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # Outside the timed steps: where the plan realigns operand rows with a copy
-    # (K % 128 != 0 on a large GEMM), also time the same call reading the rows
-    # in place, with no copy (split_k override 1), cold, events attached.
-    in_place = {}
-    for wl in workloads:
-        if fg.fp8_gemm_plan(wl.M, wl.N, wl.K)["pad_k"] == 0:
-            continue
-        xd, wd, sd, yd = dev_bufs[wl.name]
-        k0, k1 = kev[wl.name]
-        ts = []
-        for i in range(max(3, min(args.steps, 20))):
-            if not args.no_flush:
-                flush.fill_(i)
-            fg.fp8_gemm(xd, wd, sd, out=yd, split_k=1, stream=stream, events=(k0, k1))
-            k1.synchronize()
-            ts.append(k0.elapsed_time(k1) * 1e-3)
-        in_place[wl.name] = float(np.median(ts[1:]))
-        log(f"{wl.name:>12}: rows read in place (no copy) {in_place[wl.name]*1e6:9.2f} us")
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(True, i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     per, fracs = [], []
     for wl in workloads:
@@ -257,8 +297,6 @@ def main() -> int:
                     "min_us": round(float(t.min()) * 1e6, 2), "tflops": round(wl.flops / med / 1e12, 1),
                     "gbps": round(wl.bytes / med / 1e9, 1), "bound": bound_of(wl),
                     "fraction": round(frac, 4)})
-        if wl.name in in_place:
-            per[-1]["in_place_median_us"] = round(in_place[wl.name] * 1e6, 2)
         log(f"{wl.name:>12}: {med*1e6:9.2f} us  {wl.flops/med/1e12:7.1f} TFLOP/s  "
             f"{wl.bytes/med/1e9:7.1f} GB/s  frac {frac:.4f} ({bound_of(wl)})")
     geo = math.exp(sum(math.log(f) for f in fracs) / len(fracs))
@@ -281,11 +319,24 @@ def main() -> int:
                 "avg_launch_us": round(dom_t * 1e6, 2),
                 "traffic": measured_traffic(dom.name)}
     roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
+    # the same kernel's average launch from the committed rocprofv3 trace
+    traced = traced_launch_us(dom.name)
+    roofline["trace_avg_launch_us"] = traced
+    if traced:
+        work = dom.flops if bound_of(dom) == "mfma" else dom.bytes
+        roofline["trace_frac"] = round(work / (traced * 1e-6) / (roofline["peak"] * 1e12 if bound_of(dom) == "mfma"
+                                                                  else roofline["peak"] * 1e9), 4)
+    clk = clocks.summary()
+    roofline.update(clk)
+    if clk.get("sclk_mhz_median") and bound_of(dom) == "mfma":
+        # dense fp8 peak at the sampled clock: 256 CUs x 8192 FLOP per clock
+        roofline["peak_at_sclk"] = round(256 * 8192 * clk["sclk_mhz_median"] * 1e6 / 1e12, 1)
+        roofline["frac_at_sclk"] = round(roofline["achieved"] / roofline["peak_at_sclk"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu baseline: oracle on sampled outputs ...")
-        cpu = cpu_baseline(workloads, inputs, args.cpu_budget)
+        log("cpu baseline: the oracle on each full shape ...")
+        cpu = cpu_baseline(workloads, inputs)
 
     line = {
         "metric": "fp8 GEMM TFLOPS (GB/s at M=32) + fraction of MI355X roofline, geomean 5 shapes",
@@ -299,9 +350,8 @@ def main() -> int:
         "data": "synthetic (seed 42; N(0,1)->e4m3fn saturating RNE; scale U[0.005,0.02])",
         "config": {"workload": "5-shape sweep: " + ", ".join(f"{w.name} {w.M}x{w.N}x{w.K}" for w in workloads),
                    "cache": "warm" if args.no_flush else "cold (512 MiB rewrite before each GEMM)"},
-        "timing": "HIP events attached to each call's first and last kernel (hipExtLaunchKernel); "
-                  "marker_median_us / value_marker_timed: a hipEventRecord pair around a second cold call; "
-                  "in_place_median_us (untimed side run): the odd-K call without its row-realignment copy",
+        "timing": "HIP events attached to each call's kernel (hipExtLaunchKernel); "
+                  "marker_median_us / value_marker_timed: a hipEventRecord pair around a second cold call",
         "value_marker_timed": round(geo_marker, 4),
         "per_config": per,
         "roofline": roofline,

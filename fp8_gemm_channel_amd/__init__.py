@@ -28,7 +28,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(_PKG, "libfp8g.so")
+# FP8G_LIBRARY selects another build of the same library (the LDS-poison debug
+# build, libfp8g_lds_poison.so); the default is the product build.
+LIBRARY = os.environ.get("FP8G_LIBRARY") or os.path.join(_PKG, "libfp8g.so")
 
 FP8G_OK = 0
 FP8G_ERR_INVALID_ARG = 1
@@ -53,7 +55,7 @@ class Plan(ctypes.Structure):
                 ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("k_slice", ctypes.c_int64), ("group_m", ctypes.c_int32), ("k_tail", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("dp_tiles", ctypes.c_int32), ("sk_groups", ctypes.c_int32), ("pad_k", ctypes.c_int32)]
+                ("dp_tiles", ctypes.c_int32), ("sk_groups", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         d = {name: getattr(self, name) for name, _ in self._fields_}

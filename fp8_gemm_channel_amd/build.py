@@ -1,6 +1,11 @@
 """Build libfp8g.so (the HIP library behind include/fp8g.h) in-tree for gfx950.
 
-    python fp8_gemm_channel_amd/build.py [--verbose]
+    python fp8_gemm_channel_amd/build.py [--verbose] [--lds-poison]
+
+--lds-poison builds the debug library libfp8g_lds_poison.so instead: every
+LDS-DMA is preceded by a NaN fill of its destination (FP8G_LDS_POISON), so a
+read that runs ahead of its DMA shows up as NaN outputs.  Load it by setting
+FP8G_LIBRARY to its path before importing the package.
 
 (run as a file: importing the package loads the library this builds)
 
@@ -16,6 +21,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libfp8g.so")
+POISON_LIBRARY = os.path.join(PKG, "libfp8g_lds_poison.so")
 SOURCES = [os.path.join(CSRC, "fp8g_api.cpp"), os.path.join(CSRC, "fp8g_kernels.hip")] + sorted(
     os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.startswith("fp8g_launch_") and f.endswith(".hip"))
 
@@ -35,23 +41,26 @@ def _filter(text: str) -> str:
                      if not any(n in l for n in _NOISE) and not l.strip().startswith(("9", "|")))
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
-    """Compile every translation unit (in parallel) and link libfp8g.so in-tree."""
+def build(verbose: bool = False, jobs: int = 0, lds_poison: bool = False) -> str:
+    """Compile every translation unit (in parallel) and link libfp8g.so in-tree
+    (or, with lds_poison, the debug library libfp8g_lds_poison.so)."""
     from concurrent.futures import ThreadPoolExecutor
 
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tag = ".tmp%d" % os.getpid()
+    target = POISON_LIBRARY if lds_poison else LIBRARY
+    tag = ".tmp%d%s" % (os.getpid(), "p" if lds_poison else "")
     objs = [os.path.join(CSRC, os.path.basename(src) + tag + ".o") for src in SOURCES]
+    defines = ["-DFP8G_LDS_POISON"] if lds_poison else []
 
     def compile_one(pair):
         src, obj = pair
-        cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", "-o", obj, src]
+        cmd = [hipcc, *HIPCC_FLAGS, *defines, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", "-o", obj, src]
         if verbose:
             print(" ".join(cmd), flush=True)
         return subprocess.run(cmd, capture_output=True, text=True)
 
     jobs = jobs or min(len(SOURCES), int(os.environ.get("MAX_JOBS", "0") or 0) or os.cpu_count() or 1)
-    tmp = LIBRARY + tag
+    tmp = target + tag
     try:
         with ThreadPoolExecutor(max_workers=jobs) as pool:
             results = list(pool.map(compile_one, zip(SOURCES, objs)))
@@ -65,13 +74,13 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         res = subprocess.run(link, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError("link failed:\n" + _filter(res.stdout + res.stderr))
-        os.replace(tmp, LIBRARY)
+        os.replace(tmp, target)
     finally:
         for f in objs + [tmp]:
             if os.path.exists(f):
                 os.remove(f)
-    return LIBRARY
+    return target
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    print(build(verbose="--verbose" in sys.argv, lds_poison="--lds-poison" in sys.argv))

@@ -58,11 +58,14 @@ int hip_fail(hipError_t e, const char *what) {
   return fail(FP8G_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
 }
 
-// Workspace memory (split-K partials and tickets, padded rows, stream-K
-// partials): stream-ordered allocations from one memory pool per device that
-// keeps freed blocks for reuse (release threshold unlimited).  With a pool that
-// returns memory at every synchronisation, each call mapped fresh pages: a
-// 34 MB workspace measured ~25 us of extra call time.  Created on first use.
+// Workspace memory (split-K partials and tickets, stream-K partials):
+// stream-ordered allocations from one memory pool per device.  The pool keeps
+// up to kPoolKeepBytes of freed blocks for reuse across synchronisations and
+// returns anything above that: with a pool that returns all memory at every
+// synchronisation, each call mapped fresh pages (a 34 MB workspace measured
+// ~25 us of extra call time), while an unbounded one would keep the largest
+// workspace ever used for the life of the process.  Created on first use.
+constexpr uint64_t kPoolKeepBytes = uint64_t(64) << 20;
 constexpr int kMaxDevices = 64;
 std::mutex g_pool_mutex;
 hipMemPool_t g_pools[kMaxDevices] = {};
@@ -86,7 +89,7 @@ hipError_t workspace_alloc(void **ptr, size_t bytes, hipStream_t stream) {
       hipMemPool_t created;
       e = hipMemPoolCreate(&created, &props);
       if (e != hipSuccess) return e;
-      uint64_t keep = UINT64_MAX;
+      uint64_t keep = kPoolKeepBytes;
       e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep);
       if (e != hipSuccess) {
         (void)hipMemPoolDestroy(created);
@@ -111,6 +114,19 @@ constexpr int kMaxSplit = 64;
 constexpr int kMaxStreamK = 2048;    // stream-K workgroups (2 partial tiles each must stay below 2 GiB)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Threads per workgroup of each kernel configuration.
+int64_t block_threads(int32_t path, int32_t variant) {
+  if (path == FP8G_PATH_SPLITK) return variant > 20 ? 512 : 256;
+  return (variant == 3 || variant == 19) ? 256 : 512;
+}
+
+// A launch's work-items along x must stay below 2^32 (HIP's grid limit).
+int check_grid(const fp8g_plan &p, int64_t grid_x) {
+  if (grid_x * block_threads(p.path, p.variant) > (int64_t)UINT32_MAX)
+    return fail(FP8G_ERR_UNSUPPORTED, "launch of %lld workgroups exceeds the grid limit", (long long)grid_x);
+  return FP8G_OK;
+}
 
 // Bytes of split-K tickets (one 128-byte line per column tile), padded so the
 // partials that follow start 256-byte aligned.
@@ -238,22 +254,13 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     if (split_k > kMaxSplit)
       return fail(FP8G_ERR_INVALID_ARG, "split-K path takes split_k 0..%d (split_k=%d)", kMaxSplit, split_k);
     // Variants 1-5 force the LDS-ring kernel with 16 * variant w rows per
-    // workgroup, 11-15 the direct-to-register kernel with 16 * (variant - 10),
-    // 21-24 the LDS-ring kernel with 8 waves and 16 * (variant - 20) rows;
-    // 0 lets the planner choose the rows for the 4-wave LDS-ring kernel, which
-    // streams w faster on MI355X than the direct kernel (measured: M=32,
-    // N=12288, K=4096 at 15 us against 20 us for the direct kernel's best row
-    // count).  The direct kernel assembles a K tail from 16-byte loads that end
-    // inside the row, so it needs K >= 16.
-    if (variant > 10 && variant < 16 && K < 16)
-      return fail(FP8G_ERR_INVALID_ARG, "split-K variant %d needs K >= 16 (K=%lld)", variant, (long long)K);
-    const fp8g::SkinnyKind kind = variant > 20   ? fp8g::SkinnyKind::kRing8
-                                  : variant > 10 ? fp8g::SkinnyKind::kDirect
-                                                 : fp8g::SkinnyKind::kRing4;
-    const int kind_base = variant > 20 ? 20 : variant > 10 ? 10 : 0;
+    // workgroup and 4 waves, 21-24 the same kernel with 8 waves and
+    // 16 * (variant - 20) rows; 0 lets the planner choose.
+    const fp8g::SkinnyKind kind = variant > 20 ? fp8g::SkinnyKind::kRing8 : fp8g::SkinnyKind::kRing4;
+    const int kind_base = variant > 20 ? 20 : 0;
     const int forced_rb = variant - kind_base;
     const int max_rb = fp8g::skinny_max_row_blocks((int)M, kind);
-    if (forced_rb > max_rb || (variant > 5 && variant < 11) || (variant > 15 && variant < 21) || variant > 24)
+    if (forced_rb > max_rb || (variant > 5 && variant < 21) || variant > 24)
       return fail(FP8G_ERR_INVALID_ARG, "split-K variant %d not available for M=%lld", variant, (long long)M);
     const int64_t chunk = fp8g::skinny_chunk_bytes();
     const int64_t nchunks = cdiv(K, chunk);
@@ -307,12 +314,12 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     p->workspace_bytes = S > 1 ? splitk_ticket_bytes(cdiv(N, p->tile_n)) +
                                      cdiv(N, p->tile_n) * S * M * p->tile_n * (int64_t)sizeof(float)
                                : 0;
-    return FP8G_OK;
+    return check_grid(*p, cdiv(N, p->tile_n));  // the launch grid is (column tiles, S)
   }
   const bool auto_variant = variant == 0;
   if (auto_variant) variant = auto_main_variant(M, N, K);
-  if (split_k > 2 && variant != 16)
-    return fail(FP8G_ERR_INVALID_ARG, "main variant %d takes split_k 0..2 (row realignment choice)", variant);
+  if (split_k != 0 && variant != 16)
+    return fail(FP8G_ERR_INVALID_ARG, "main variant %d takes no split_k (split_k=%d)", variant, split_k);
 
   const fp8g::MainConfig *c = fp8g::main_config(variant);
   if (!c) return fail(FP8G_ERR_INVALID_ARG, "unknown main variant %d", variant);
@@ -324,49 +331,21 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
   p->tile_n = c->bn;
   p->tile_k = c->bk;
   p->group_m = (int32_t)(tiles_m < 8 ? tiles_m : 8);
-  // Rows whose length is not a multiple of 128 bytes start off the cache-line
-  // grid, and every 128-byte K chunk the kernels stage then spans two lines.
-  // Measured on MI355X (4096 x 4096, cold): K = 4096 or 4224 63.7 us, 4160
-  // (rows at 64-byte offsets) 73.4, 4112 / 4128 (16 / 32) ~83, 4127 (any
-  // byte) 94.  Copying x and w once into rows zero-padded to a multiple of 128
-  // bytes costs one read and one write of the operands and gives the same
-  // sums (zero bytes add nothing, and the K steps stay in order).  Measured
-  // (in place -> copied): 4096^2 x 4127 96 -> 84 us, 8192^2 x 8191 664 -> 521,
-  // 3072^2 x 3073 72 -> 60, 512 x 8192 x 8193 91 -> 76, 1024 x 4096 x 4100
-  // 42.7 -> 40.7; but 2048^2 x 2049 27 -> 31 and 1024^2 x 1025 11 -> 18, where
-  // the copy's fixed cost (launch, a latency-bound small copy) dominates.  So
-  // copy for GEMMs of at least 30 GFLOP with at least 512 flops per operand
-  // byte copied (2 M N / (M + N)).  split_k (not variant 16) forces the
-  // choice: 1 = read rows in place, 2 = copy.
-  int64_t kk = K;
-  if (K % 128 != 0) {
-    const int64_t kp = cdiv(K, 128) * 128;
-    // (the copy must also stay a modest workspace, at most 4 GiB, and the padded
-    // K within FP8G_MAX_K: a tile's rows form one buffer range of 256 * K
-    // bytes, which must stay below 2^32)
-    const bool fits = (M + N) * kp <= (int64_t(4) << 30) && kp <= FP8G_MAX_K;
-    const double flops = 2.0 * (double)M * (double)N * (double)K;
-    const bool pad_auto = fits && flops >= 3e10 && 2.0 * (double)M * (double)N / (double)(M + N) >= 512.0;
-    const bool pad = variant == 16 ? pad_auto : ((split_k == 2 && fits) || (split_k == 0 && pad_auto));
-    if (pad) {
-      kk = kp;
-      p->pad_k = (int32_t)kk;
-      p->workspace_bytes = (M + N) * kk;
-    }
-  }
-  p->k_tail = (kk % c->bk) != 0;
-  // Where the 256 x 256 tiles are chosen and no K tail is left (K % 128 == 0,
-  // or rows realigned above), the one-wave-per-SIMD kernel runs them: same
-  // tiles and the same sums in the same order, measured faster or level
-  // (interleaved with variant 10 on one MI355X: 8192^3 393 vs 418 us,
-  // 1536 x 8192^2 100.5 vs 108.0, 2560 x 4096^2 50.7 vs 52.8, 3072^3 42.0 vs
-  // 42.7, 4096^3 level within 1%).
+  // Operand rows are always read where they are: K need not be a multiple of
+  // anything, and the last K step is masked inside the kernel (bytes at or
+  // past K load as zeros).  Nothing is copied or padded.
+  p->k_tail = (K % c->bk) != 0;
+  // Where the 256 x 256 tiles are chosen and there is no K tail (K % 128 ==
+  // 0), the one-wave-per-SIMD kernel runs them: same tiles and the same sums
+  // in the same order, measured faster or level (interleaved with variant 10
+  // on one MI355X: 8192^3 393 vs 418 us, 1536 x 8192^2 100.5 vs 108.0,
+  // 2560 x 4096^2 50.7 vs 52.8, 3072^3 42.0 vs 42.7, 4096^3 level within 1%).
   if (auto_variant && variant == 10 && !p->k_tail) {
     variant = 19;
     p->variant = 19;
   }
   if (variant == 19 && p->k_tail)
-    return fail(FP8G_ERR_INVALID_ARG, "main variant 19 needs K %% 128 == 0 or realigned rows (K=%lld)", (long long)K);
+    return fail(FP8G_ERR_INVALID_ARG, "main variant 19 needs K %% 128 == 0 (K=%lld)", (long long)K);
   p->grid = tiles_m * tiles_n;
   p->dp_tiles = (int32_t)(tiles_m * tiles_n);
   if (variant == 16) {
@@ -375,7 +354,7 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     // splits the (tile, K step) units of those tiles evenly, so every compute
     // unit gets between one and two tiles' worth (less than one when the tiles
     // do not fill a wave).  split_k forces the number of stream-K workgroups.
-    const int64_t T = tiles_m * tiles_n, nk = cdiv(kk, c->bk);
+    const int64_t T = tiles_m * tiles_n, nk = cdiv(K, c->bk);
     const int64_t n_dp = T > kNumCUs ? (T / kNumCUs - 1) * kNumCUs : 0;
     if (T * nk >= INT32_MAX) return fail(FP8G_ERR_UNSUPPORTED, "stream-K needs tiles x K steps below 2^31");
     int64_t n_sk = split_k > 0 ? split_k : kNumCUs;
@@ -383,9 +362,9 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     p->dp_tiles = (int32_t)n_dp;
     p->sk_groups = (int32_t)n_sk;
     p->grid = n_dp + n_sk;
-    p->workspace_bytes += splitk_ticket_bytes(T - n_dp) + 2 * n_sk * fp8g::kMainPartialBytes;
+    p->workspace_bytes = splitk_ticket_bytes(T - n_dp) + 2 * n_sk * fp8g::kMainPartialBytes;
   }
-  return FP8G_OK;
+  return check_grid(*p, p->grid);
 }
 
 bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
@@ -394,14 +373,9 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
-// Configurations built for every operand format: main variants 3, 10, 17,
-// 18 (all the planner picks) and the LDS-ring split-K kernel.
-bool supports_formats(const fp8g_plan &p) {
-  if (p.path == FP8G_PATH_MAIN)
-    return p.variant == 3 || p.variant == 10 || p.variant == 17 || p.variant == 18 || p.variant == 19;
-  if (p.path == FP8G_PATH_SPLITK) return p.variant <= 5 || p.variant >= 21;
-  return true;
-}
+// Every configuration is built for every operand format except stream-K
+// (main variant 16, E4M3 only).
+bool supports_formats(const fp8g_plan &p) { return !(p.path == FP8G_PATH_MAIN && p.variant == 16); }
 
 int run(const void *x, const void *w, const float *scale, const float *bias, void *y, int64_t M, int64_t N,
         int64_t K, int32_t x_format, int32_t w_format, int32_t act, int32_t path, int32_t variant, int32_t split_k,
@@ -459,31 +433,16 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
     l.ev = events;
     void *ws = nullptr;
     if (p.workspace_bytes > 0) {
-      // [padded x rows | padded w rows] (pad plan), then, for stream-K, the
-      // tickets of the stream-K tiles and two partial tiles per stream-K
-      // workgroup; uninitialized (the pad kernel writes every padded byte,
-      // tickets carry the call id, partials are written before they are read)
+      // stream-K: the tickets of the stream-K tiles, then two partial tiles per
+      // stream-K workgroup; uninitialized (tickets carry the call id, partials
+      // are written before they are read)
       e = workspace_alloc(&ws, (size_t)p.workspace_bytes, stream);
       if (e != hipSuccess) return hip_fail(e, "workspace allocation (main path)");
-    }
-    char *wsp = (char *)ws;
-    if (p.pad_k > 0) {
-      uint8_t *xp = (uint8_t *)wsp, *wp = xp + (size_t)M * (size_t)p.pad_k;
-      // two kernels: the start event goes with the copy, the stop event with the GEMM
-      e = fp8g::launch_pad_rows((const uint8_t *)x, (const uint8_t *)w, xp, M, N, K, p.pad_k, stream,
-                                fp8g::DispatchEvents{events.start, nullptr});
-      l.ev.start = nullptr;
-      l.x = xp;
-      l.w = wp;
-      l.K = p.pad_k;
-      wsp += (size_t)(M + N) * (size_t)p.pad_k;
-    }
-    if (e == hipSuccess && p.sk_groups > 0) {
       const int64_t sk_tiles = cdiv(M, p.tile_m) * cdiv(N, p.tile_n) - p.dp_tiles;
       l.n_dp = p.dp_tiles;
       l.n_sk = p.sk_groups;
-      l.tickets = (unsigned long long *)wsp;
-      l.partials = (float *)(wsp + splitk_ticket_bytes(sk_tiles));
+      l.tickets = (unsigned long long *)ws;
+      l.partials = (float *)((char *)ws + splitk_ticket_bytes(sk_tiles));
       l.epoch = call_id();
     }
     if (e == hipSuccess) e = fp8g::launch_main(l, stream);

@@ -68,15 +68,14 @@ struct MainConfig {
   int id, bm, bn, bk, stages;
 };
 struct SkinnyConfig {
-  int id, row_blocks;  // w rows per workgroup = 16 * row_blocks; ids >= 11: direct-to-register kernel
+  int id, row_blocks;  // w rows per workgroup = 16 * row_blocks
 };
 
 const MainConfig *main_config(int id);      // nullptr if unknown
 const SkinnyConfig *skinny_config(int id);  // nullptr if unknown
 int skinny_tile_n(const SkinnyConfig &c);   // output columns per workgroup
-// The split-K kernels: LDS ring with 4 waves (variants 1-5), direct to
-// registers (11-15), LDS ring with 8 waves (21-24).
-enum class SkinnyKind { kRing4, kDirect, kRing8 };
+// The split-K kernel: LDS rings with 4 waves (variants 1-5) or 8 waves (21-24).
+enum class SkinnyKind { kRing4, kRing8 };
 int skinny_max_row_blocks(int M, SkinnyKind kind);  // limit on row_blocks for this M and kernel
 int skinny_chunk_bytes();                   // K granularity of one wave iteration
 
@@ -87,14 +86,9 @@ hipError_t launch_main4w(const MainLaunch &l, hipStream_t stream);           // 
 hipError_t launch_main4w_epi(const MainLaunch &l, hipStream_t stream);       // variant 19, bias / activation
 hipError_t launch_main_tiles(const MainLaunch &l, hipStream_t stream);       // variants 3, 17, 18
 hipError_t launch_main_tiles_epi(const MainLaunch &l, hipStream_t stream);   // the same, bias / activation
-hipError_t launch_main_legacy(const MainLaunch &l, hipStream_t stream);      // variants 1, 2, 4-7, 9
-hipError_t launch_skinny_epi(const SkinnyLaunch &l, hipStream_t stream);     // bias / activation, variants 11-15
+hipError_t launch_skinny_epi(const SkinnyLaunch &l, hipStream_t stream);     // bias / activation
 hipError_t launch_skinny(const SkinnyLaunch &l, hipStream_t stream);
 hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream, const DispatchEvents &ev);
-// Copies x [M, K] and w [N, K] (rows at any byte alignment) into dst as
-// [M + N, K16] rows, bytes K .. K16-1 zero (K16: K rounded up to a multiple of 16).
-hipError_t launch_pad_rows(const uint8_t *x, const uint8_t *w, uint8_t *dst, int64_t M, int64_t N, int64_t K,
-                           int64_t Kp, hipStream_t stream, const DispatchEvents &ev);
 // K = 0 with a bias or an activation: y[m, n] = bf16(act(bias[n])).
 hipError_t launch_empty_k(uint16_t *y, const float *bias, int act, int64_t M, int64_t N, hipStream_t stream,
                           const DispatchEvents &ev);

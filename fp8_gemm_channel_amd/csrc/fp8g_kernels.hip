@@ -6,8 +6,8 @@
 //
 // x [M,K] and w [N,K] are FP8 E4M3 (OCP) codes, row-major; scale [N] fp32;
 // y [M,N] bf16.  The products run on the CDNA4 f8f6f4 matrix cores
-// (V_MFMA_F32_32X32X64_F8F6F4, format code 0 = E4M3 for both operands, no block
-// scale) into fp32 accumulators; the per-output-channel scale multiplies each
+// (V_MFMA_F32_32X32X64_F8F6F4 or V_MFMA_F32_16X16X128_F8F6F4, format code 0 =
+// E4M3 for both operands, no block scale) into fp32 accumulators; the per-output-channel scale multiplies each
 // finished fp32 sum once in the epilogue, which rounds to bf16 (nearest, ties
 // to even).  Sources on the pages (kernelbench.com model pages, cells named by
 // the kernel they audit): fp8 x fp8 with fp32 accumulation and bf16 output,
@@ -31,12 +31,13 @@
 //
 // Memory access.  All global reads are raw buffer loads.  A buffer's range is
 // set to the valid rows of the tile, so rows past M or N read as zero without
-// branches, and a fully out-of-range 16-byte load returns zeros.  Loads need no
-// alignment: rows of an odd K (e.g. K = 4127) start at any byte.  The K tail
-// (a K step that ends past K) is assembled in registers with the bytes past K
-// forced to zero: zero bytes add nothing to a dot product, which is why the
-// pages could pad with zeros ("Kimi K3 (256k)", SM100 persistent-TMA Triton
-// cell); here nothing is copied and nothing is padded in memory.
+// branches, and a fully out-of-range 16-byte load returns zeros.  Operand rows
+// are read where they lie: rows of an odd K (e.g. K = 4127) start at any byte
+// and no kernel needs them aligned.  The K tail (a K step that ends past K) is
+// masked inside the kernel, the bytes past K entering as zeros: zero bytes add
+// nothing to a dot product, which is why the pages could pad with zeros
+// ("Kimi K3 (256k)", SM100 persistent-TMA Triton cell).  No operand is ever
+// copied, padded or cached.
 #include "fp8g_kernels.hpp"
 
 namespace fp8g {
@@ -44,30 +45,6 @@ namespace fp8g {
 __global__ __launch_bounds__(256) void fp8g_zero_kernel(uint16_t *__restrict__ y, int64_t count) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = 0;
-}
-
-// Row realignment (rows of K bytes whose starts are not 128-byte aligned): one
-// wave per row (x rows, then w rows), lane l copying 16-byte chunks l, l + 64,
-// ...; the source row is one buffer of K bytes (so the descriptor is uniform),
-// bytes at or past K read zero and the chunk that straddles K is rebuilt by a
-// shifted load.  Sources are read once (non-temporal); the padded rows are
-// written with ordinary aligned 16-byte stores, since the GEMM reads them next.
-__global__ __launch_bounds__(256) void fp8g_pad_rows_kernel(const uint8_t *__restrict__ x,
-                                                            const uint8_t *__restrict__ w, uint8_t *__restrict__ dst,
-                                                            int64_t rows, int64_t M, int K, int Kp) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
-  const uint8_t *src = row < M ? x + row * K : w + (row - M) * K;
-  const v4i rsrc = make_rsrc(src, (uint32_t)K);
-  uint4 *out = (uint4 *)(dst + row * Kp);
-  for (int c = lane; c < Kp / 16; c += 64) {
-    const int valid = K - 16 * c;
-    uint4 v;
-    if (valid >= 16) v = as_u4(llvm_buffer_load_v4i32(rsrc, (uint32_t)c * 16u, 0, 2));
-    else v = load16_masked(rsrc, (uint32_t)c * 16u, valid, K);
-    out[c] = v;
-  }
 }
 
 // K = 0 with a bias or an activation: the empty sum is +0, so
@@ -82,25 +59,17 @@ __global__ __launch_bounds__(256) void fp8g_empty_k_kernel(uint16_t *__restrict_
 
 // ------------------------------------------------------------------ launchers
 static const MainConfig kMainConfigs[] = {
-    {1, 256, 256, 64, 4},  // 8 waves, wave tile 64 (m) x 128 (n)
-    {2, 128, 128, 64, 4},  // 4 waves, two workgroups per CU
     {3, 64, 64, 128, 3},   // 4 waves, small problems
-    {4, 256, 256, 64, 4},  // 8 waves, wave tile 128 (m) x 64 (n)
-    {5, 256, 256, 64, 4},  // 4 waves, one per SIMD
-    {6, 256, 256, 128, 2}, // 8 waves, wave tile 64 (m) x 128 (n), 128-byte K steps
-    {7, 256, 256, 128, 2}, // 8 waves, wave tile 128 (m) x 64 (n), 128-byte K steps
-    {9, 256, 256, 64, 4},  // 8 waves in two ping-pong groups, wave tile 64 (m) x 128 (n)
     {10, 256, 256, 128, 2}, // 8 waves, five half-step LDS slots (x two steps ahead)
     {16, 256, 256, 128, 2}, // variant 10 with stream-K over the tiles past the full waves
     {17, 128, 256, 128, 3}, // 8 waves, wave tile 64 x 64: grids of 128 x 256 tiles (mid M)
     {18, 128, 128, 128, 4}, // 8 waves, wave tile 64 (m) x 32 (n): grids of 128 x 128 tiles (mid M)
     {19, 256, 256, 128, 2}, // 4 waves, wave tile 128 x 128, ten 16 KiB LDS units (K % 128 == 0)
 };
-// ids 1-5: LDS-ring kernel (4 waves), 11-15: direct-to-register kernel, 21-24:
-// LDS-ring kernel with 8 waves; 16 * row_blocks w rows per workgroup
+// ids 1-5: LDS-ring kernel with 4 waves, 21-24: with 8 waves; 16 * row_blocks
+// w rows per workgroup
 static const SkinnyConfig kSkinnyConfigs[] = {
-    {1, 1},  {2, 2},  {3, 3},  {4, 4},  {5, 5},  {11, 1}, {12, 2},
-    {13, 3}, {14, 4}, {15, 5}, {21, 1}, {22, 2}, {23, 3}, {24, 4},
+    {1, 1}, {2, 2}, {3, 3}, {4, 4}, {5, 5}, {21, 1}, {22, 2}, {23, 3}, {24, 4},
 };
 
 const MainConfig *main_config(int id) {
@@ -116,7 +85,6 @@ const SkinnyConfig *skinny_config(int id) {
 int skinny_tile_n(const SkinnyConfig &c) { return 16 * c.row_blocks; }
 int skinny_max_row_blocks(int M, SkinnyKind kind) {
   switch (kind) {
-    case SkinnyKind::kDirect: return M <= 64 ? 5 : 0;  // register ring: (RB + MB) * 8 * 4 VGPRs of operands
     case SkinnyKind::kRing8: return M <= 16 ? 4 : (M <= 32 ? 3 : (M <= 64 ? 1 : 0));  // 8 rings of 2 slots
     default: return M <= 16 ? 5 : (M <= 32 ? 4 : 2);  // 4 rings of 3 slots (2 with 128 x rows)
   }
@@ -131,7 +99,7 @@ hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
     case 3:
     case 17:
     case 18: return launch_main_tiles(l, stream);
-    default: return launch_main_legacy(l, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -140,14 +108,6 @@ hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream, const Dis
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   return dispatch(fp8g_zero_kernel, dim3((unsigned)blocks), dim3(256), stream, ev, y, count);
-}
-
-hipError_t launch_pad_rows(const uint8_t *x, const uint8_t *w, uint8_t *dst, int64_t M, int64_t N, int64_t K,
-                           int64_t Kp, hipStream_t stream, const DispatchEvents &ev) {
-  const int64_t rows = M + N;
-  if (rows <= 0) return hipSuccess;
-  return dispatch(fp8g_pad_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), stream, ev, x, w, dst, rows, M,
-                  (int)K, (int)Kp);
 }
 
 hipError_t launch_empty_k(uint16_t *y, const float *bias, int act, int64_t M, int64_t N, hipStream_t stream,

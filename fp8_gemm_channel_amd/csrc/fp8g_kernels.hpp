@@ -7,8 +7,8 @@
 //
 // x [M,K] and w [N,K] are FP8 E4M3 (OCP) codes, row-major; scale [N] fp32;
 // y [M,N] bf16.  The products run on the CDNA4 f8f6f4 matrix cores
-// (V_MFMA_F32_32X32X64_F8F6F4, format code 0 = E4M3 for both operands, no block
-// scale) into fp32 accumulators; the per-output-channel scale multiplies each
+// (V_MFMA_F32_32X32X64_F8F6F4 or V_MFMA_F32_16X16X128_F8F6F4, format code 0 =
+// E4M3 for both operands, no block scale) into fp32 accumulators; the per-output-channel scale multiplies each
 // finished fp32 sum once in the epilogue, which rounds to bf16 (nearest, ties
 // to even).  Sources on the pages (kernelbench.com model pages, cells named by
 // the kernel they audit): fp8 x fp8 with fp32 accumulation and bf16 output,
@@ -32,12 +32,13 @@
 //
 // Memory access.  All global reads are raw buffer loads.  A buffer's range is
 // set to the valid rows of the tile, so rows past M or N read as zero without
-// branches, and a fully out-of-range 16-byte load returns zeros.  Loads need no
-// alignment: rows of an odd K (e.g. K = 4127) start at any byte.  The K tail
-// (a K step that ends past K) is assembled in registers with the bytes past K
-// forced to zero: zero bytes add nothing to a dot product, which is why the
-// pages could pad with zeros ("Kimi K3 (256k)", SM100 persistent-TMA Triton
-// cell); here nothing is copied and nothing is padded in memory.
+// branches, and a fully out-of-range 16-byte load returns zeros.  Operand rows
+// are read where they lie: rows of an odd K (e.g. K = 4127) start at any byte
+// and no kernel needs them aligned.  The K tail (a K step that ends past K) is
+// masked inside the kernel, the bytes past K entering as zeros: zero bytes add
+// nothing to a dot product, which is why the pages could pad with zeros
+// ("Kimi K3 (256k)", SM100 persistent-TMA Triton cell).  No operand is ever
+// copied, padded or cached.
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -124,14 +125,31 @@ __device__ __forceinline__ uint4 load16_masked(v4i rsrc, uint32_t off, int valid
   return load16_partial(rsrc, off, valid);
 }
 
+// Debug build (FP8G_LDS_POISON): before every LDS-DMA, each lane writes 16
+// bytes of 0xFF -- a NaN as E4M3, as E5M2 and as fp32 -- where its DMA will
+// land, and waits until that write is done.  A read that runs ahead of its
+// DMA (a miscounted vm_wait, a missing barrier) then sees NaN operands or
+// scales instead of stale bytes that might pass by luck, and parity tests
+// fail on the NaN outputs.  Off in the product build.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_poison16(uint32_t lds_base) {
+#ifdef FP8G_LDS_POISON
+  const uint32_t at = lds_base + 16u * __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const v4i nan = {-1, -1, -1, -1};
+  asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(at), "v"(nan) : "memory");
+#else
+  (void)lds_base;
+#endif
+}
+
 // LDS-DMA: 16 bytes per lane from global (voffset + soffset) into LDS at
 // lds_base + 16 * lane.  Written as inline asm so the compiler does not treat
 // it as an LDS store it must wait for before every LDS read; completion is
 // tracked by hand with vm_wait() below.  m0 is set inside the same statement.
 // (m0 is otherwise unused by these kernels, so clobbering it is safe.)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_base, uint32_t voffset, uint32_t soffset) {
+  lds_poison16(lds_base);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
@@ -225,11 +243,7 @@ __device__ __forceinline__ float activation_rt(float z, int act) {
 // conflicts whether LDS serves 128 or 256 bytes per cycle.  A DMA instruction
 // writes 1 KiB contiguously; the swizzle is applied on the global side by
 // choosing which chunk each lane fetches.
-template <int BK>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (BK == 128) return (r & 7) ^ ((r >> 3) & 1);
-  else return ((r >> 1) ^ (r >> 2)) & 3;  // BK == 64: four chunks per row
-}
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 struct MainArgs {
   const uint8_t *x;
@@ -452,8 +466,8 @@ __device__ __forceinline__ void main_epilogue(const v16f (&acc)[BN / WN / 32][BM
 #undef FP8G_EPI
 }
 
-// Software pipeline.  A K step is BK bytes (one stage buffer), worked as BK/64
-// MFMA sub-steps; F[u & 1] holds the operands of sub-step u.  Sub-step u:
+// Software pipeline.  A K step is 128 bytes (one stage buffer), worked as two
+// 64-byte MFMA sub-steps; F[u & 1] holds the operands of sub-step u.  Sub-step u:
 //
 //     [last sub-step of step s only] wait for this wave's DMA of step s+1,
 //         workgroup barrier, LDS-DMA of step s+DIST into a retired buffer
@@ -461,17 +475,18 @@ __device__ __forceinline__ void main_epilogue(const v16f (&acc)[BN / WN / 32][BM
 //     reads of sub-step u+1's operands into F[(u+1) & 1]
 //
 // The barrier publishes step s+1 (every wave's DMA has landed) and retires the
-// buffer of step s (every wave has read its operands).  BK = 128 halves the
-// barriers and has each DMA instruction fetch 8 rows x 128 bytes instead of
-// 16 rows x 64 bytes, which the global-to-LDS path serves faster (measured on
-// MI355X: ~7% on 4096^3 and 8192^3).
+// buffer of step s (every wave has read its operands).  128-byte steps (rather
+// than 64) halve the barriers and have each DMA instruction fetch 8 rows x 128
+// bytes instead of 16 rows x 64 bytes, which the global-to-LDS path serves
+// faster (measured on MI355X: ~7% on 4096^3 and 8192^3).
 // With 8 waves per workgroup two waves share each SIMD, so one wave's MFMAs
 // cover the other's barrier and LDS waits; a single wave per SIMD can neither
 // keep the matrix pipe full nor keep enough LDS reads in flight (measured on
 // MI355X: ~4.0-4.5 vs ~4.8 PFLOP/s for back-to-back MFMAs, ~110 vs ~200
 // B/clk/CU for 16-byte LDS reads).
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool KTAIL, bool PP, int FMT = 0, bool EPI = false>
+template <int BM, int BN, int STAGES, int WM, int WN, bool KTAIL, int FMT = 0, bool EPI = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) {
+  constexpr int BK = 128;
   constexpr int NWAVES = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
   constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 blocks per wave
@@ -484,12 +499,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   constexpr int W_DPW = (BN / ROWS_PER_KB) / NWAVES;  // of which fill w rows
   constexpr int NMFMA = FN * FM;             // MFMAs per wave per 64-byte sub-step
   constexpr int NREAD = (FN + FM) * 2;       // 16-byte LDS reads per wave per sub-step
-  // Prefetch distance in steps.  BK = 64: step k+STAGES-1 goes into the buffer
-  // retired one barrier earlier (issuing one step further ahead measured no
-  // faster).  BK = 128: step k+STAGES goes into the buffer of step k itself,
-  // which a step's last sub-step retires.
-  constexpr int DIST = SUB == 1 ? STAGES - 1 : STAGES;
-  static_assert(BK == 64 || BK == 128, "BK");
+  // Prefetch distance in steps: step k+STAGES goes into the buffer of step k
+  // itself, which a step's last sub-step retires.
+  constexpr int DIST = STAGES;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
   static_assert(BLOCKS % NWAVES == 0 && (BN / ROWS_PER_KB) % NWAVES == 0, "DMA split");
   static_assert(DIST >= 2 && DIST <= 5 && (DIST - 1) * DPW < 64, "vmcnt range");
@@ -540,7 +552,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   // match, so rows past M / N still read zero).
   static_assert(NWAVES % 2 == 0 && BN % 16 == 0, "block-invariant swizzle");
   const int dma_lrow = wave * ROWS_PER_KB + lane / CH;  // row within block t = 0
-  const int dma_chunk = (lane % CH) ^ swz<BK>(dma_lrow);
+  const int dma_chunk = (lane % CH) ^ swz(dma_lrow);
   const uint32_t laneff = (uint32_t)dma_lrow * (uint32_t)K + (uint32_t)dma_chunk * 16u;
   const uint32_t blk_stride = (uint32_t)(NWAVES * ROWS_PER_KB) * (uint32_t)K;
   v4i rs[DPW];
@@ -604,7 +616,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   // chunks 4j + 2(l/32) + {0,1} of 64-byte sub-step j.
   const int aw_row = wave_n * TN + lr;  // w row of block 0 (block i adds 32 i rows)
   const int bx_row = wave_m * TM + lr;  // x row of block 0
-  const int sa = swz<BK>(aw_row), sbx = swz<BK>(bx_row);  // 32 i leaves the swizzle unchanged
+  const int sa = swz(aw_row), sbx = swz(bx_row);  // 32 i leaves the swizzle unchanged
 
   // Operand registers of two sub-steps: F[u & 1] holds sub-step u.
   v8i fa[2][FN], fb[2][FM];
@@ -657,61 +669,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
   }
   __syncthreads();
 
-  if constexpr (PP) {
-    // Ping-pong schedule.  Waves are dealt to the four SIMDs round-robin, so
-    // waves 0-3 (group 0) and 4-7 (group 1) put one wave of each group on every
-    // SIMD.  The groups alternate between two kinds of phase, separated by
-    // workgroup barriers: a compute phase issues the wave's 8 MFMAs of one K step
-    // back to back from registers; a memory phase reads the next K step's
-    // operands from LDS and issues the wave's LDS-DMA share of the step three
-    // ahead.  While one wave of a SIMD computes, the other one loads, so the
-    // matrix pipe of every SIMD is fed by one wave or the other and a barrier
-    // does not drain it.
-    //
-    //   phase 2k  : group 0 memory(k)            group 1 compute(k-1)
-    //   phase 2k+1: group 0 compute(k)           group 1 memory(k)
-    //
-    // Step k lives in stage k % 4.  Memory(k) issues step k+3 into the stage of
-    // step k-1, which both groups finished reading by the end of phase 2k-1.
-    // The barrier ending phase 2k+1 publishes step k+1: before it every wave
-    // waits for its own DMA of step k+1 (steps k+2 and k+3 may stay in flight).
-    static_assert(SUB == 1 && STAGES == 4 && NWAVES == 8 && DIST == 3, "ping-pong layout");
-    const int grp = wave >> 2;
-    auto mem = [&](int k) __attribute__((always_inline)) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < NREAD; ++q) read_one(k % STAGES, 0, q, fa[0], fb[0]);
-      issue(k + DIST);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto comp = [&]() __attribute__((always_inline)) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < NMFMA; ++q) {
-        const int i = q / FM, jm = q % FM;
-        acc[i][jm] = mfma32<FMT>(fa[0][i], fb[0][jm], acc[i][jm]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // Both groups run the same body, memory(k) then compute(k); group 1 runs
-    // it one phase later (an extra barrier first, none after its last compute),
-    // so every wave executes the same number of barriers.  The wait that
-    // publishes step k+1 belongs to phase 2k+1, which is group 0's compute and
-    // group 1's memory phase.
-    auto publish = [&](int k) __attribute__((always_inline)) {
-      wait_ahead(min(2, nk - 2 - k));
-      if (KTAIL && k + 1 == nk_full) fix_tail((k + 1) % STAGES);
-    };
-    if (grp == 1) __syncthreads();
-    for (int k = 0; k < nk; ++k) {
-      mem(k);
-      if (grp == 1) publish(k);
-      __syncthreads();
-      comp();
-      if (grp == 0) publish(k);
-      if (grp == 0 || k + 1 < nk) __syncthreads();
-    }
-  } else {
 #pragma unroll
   for (int q = 0; q < NREAD; ++q) read_one(0, 0, q, fa[0], fb[0]);
 
@@ -752,20 +709,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void fp8g_main_kernel(MainArgs a) 
     interleave_mfma_reads<0, NMFMA, NREAD>();
     __builtin_amdgcn_sched_barrier(0);
   };
-  if constexpr (SUB == 1) {
-    int u = 0;
-    for (; u + 1 < nsub; u += 2) {
-      substep(u, 0, true);
-      substep(u + 1, 1, true);
-    }
-    if (u < nsub) substep(u, 0, true);
-  } else {
-    for (int s = 0; s < nk; ++s) {
-      substep(2 * s, 0, false);
-      substep(2 * s + 1, 1, true);
-    }
+  for (int s = 0; s < nk; ++s) {
+    substep(2 * s, 0, false);
+    substep(2 * s + 1, 1, true);
   }
-  }  // PP
 
   static_assert(2 * BM * BN <= STAGES * STAGE_BYTES, "the bf16 tile fits in the stage buffers");
   main_epilogue<BM, BN, WM, WN, EPI>(acc, a, smem, (const float *)(smem + STAGES * STAGE_BYTES),
@@ -881,13 +828,13 @@ __global__ __launch_bounds__(512, 1) void fp8g_main5_kernel(MainArgs a) {
     // (l % 8) ^ swz(row); descriptor t starts at the block's first row (rows past
     // M / N read zero).
     const int dma_lrow = wave * ROWS_PER_KB + lane / CH;
-    const int dma_chunk = (lane % CH) ^ swz<BK>(dma_lrow);
+    const int dma_chunk = (lane % CH) ^ swz(dma_lrow);
     const uint32_t laneff = (uint32_t)dma_lrow * (uint32_t)K + (uint32_t)dma_chunk * 16u;
     const uint32_t blk_stride = (uint32_t)(NWAVES * ROWS_PER_KB) * (uint32_t)K;
     // Fragment reads: lane l reads row (l % 32) of each 32-row block, chunks
     // 4j + 2(l/32) + {0,1} of 64-byte sub-step j; blocks in first-use order.
     const int aw_row = wave_n * TN + lr, bx_row = wave_m * TM + lr;
-    const int sa = swz<BK>(aw_row), sbx = swz<BK>(bx_row);
+    const int sa = swz(aw_row), sbx = swz(bx_row);
     int tm, tn;
     raster(a, tile, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -1191,6 +1138,7 @@ struct SkinnyShape {
 __device__ __forceinline__ int swz16(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ void dma16_nt(v4i rsrc, uint32_t lds_base, uint32_t voffset, uint32_t soffset) {
+  lds_poison16(lds_base);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                :
                : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
@@ -1554,7 +1502,7 @@ __device__ __forceinline__ void main_epilogue16(const v4f (&acc)[BN / WN / 16][B
 // barrier: left to the compiler, a quadrant's DMAs went out in one burst at its
 // start and the issuing wave -- the only one on its SIMD -- stalled behind
 // them (the kernel ran 8% slower).  Rows of a unit are stored with the 16-row
-// swizzle swz16.  K % 128 == 0 only (odd K runs on realigned rows).
+// swizzle swz16.  K % 128 == 0 only (other K run on the five-slot kernel).
 template <int FMT = 0, bool EPI = false>
 __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
   constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2, NWAVES = 4;
@@ -1749,143 +1697,6 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
   main_epilogue16<BM, BN, WM, WN, EPI>(acc, a, smem, s_lds, b_lds, m0, n0, wave, lane, tid);
 }
 
-// Direct variant of the skinny kernel: no LDS in the K loop.  Every lane
-// loads its own MFMA operands from global memory straight into registers, so
-// neither w nor x passes through LDS and nothing but the final cross-wave sum
-// needs it.  For V_MFMA_F32_16X16X128_F8F6F4 lane l supplies row l % 16 of a
-// 16-row block and 32 bytes of K.  Any permutation of K inside one MFMA is
-// harmless as long as A and B use the same one, so lane l (r = l % 16,
-// g = l / 16) takes bytes [16g, 16g+16) and [64 + 16g, 64 + 16g + 16) of the
-// 128-byte chunk: the four lanes of a row then read 64 contiguous bytes per
-// load instruction.  Wave v takes chunks v, v+4, v+8, ... of the workgroup's K
-// slice and keeps D chunks in flight (register ring, loads issued D chunks
-// ahead of the MFMAs that use them); w is read with the non-temporal policy,
-// x (re-read by every workgroup, so best kept in L2) without.
-template <int RB, int MB, int D, bool EPI = true>
-__global__ __launch_bounds__(256, 1) void fp8g_skinny_direct_kernel(SkinnyArgs a) {
-  constexpr int NB = RB + MB;  // 16-row blocks per chunk: RB of w, then MB of x
-  __shared__ __attribute__((aligned(16))) float red[4 * RB * MB * 4 * 64];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int K = a.K;
-  const int n0 = blockIdx.x * 16 * RB;
-  const int rows_w = min(16 * RB, a.N - n0);
-  const int s = blockIdx.y;
-  const int kbeg = s * a.k_slice;
-  const int kend = min(K, kbeg + a.k_slice);
-  const int nch = (kend - kbeg + 127) >> 7;
-  const int my = nch > wave ? (nch - wave + 3) >> 2 : 0;  // chunks of this wave
-
-  const v4i rsrc_w = make_rsrc(a.w + (size_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
-  const v4i rsrc_x = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)K);
-  const int g = lane >> 4, r = lane & 15;
-  uint32_t off[NB];  // lane's row start + 16g, per block (rows past N or M read as zero)
-#pragma unroll
-  for (int b = 0; b < NB; ++b) off[b] = (uint32_t)(16 * (b < RB ? b : b - RB) + r) * (uint32_t)K + 16u * g;
-
-  // Only the slice's last chunk can end past kend; it belongs to wave
-  // (nch - 1) % 4 as its last chunk.  Its loads are issued before everything
-  // else and it is used last, so the main loop has no tail logic.
-  const bool has_tail = ((kend - kbeg) & 127) != 0 && ((nch - 1) & 3) == wave;
-  const int my_full = my - (has_tail ? 1 : 0);
-
-  // Chunk j of this wave into registers: bb[b][h] = 16 bytes at k = kc + 64h + 16g.
-  // Every load is issued unconditionally: a chunk past the wave's share is
-  // pointed 2^31 bytes past the buffer, beyond its range (rows * K < 2^31), so
-  // it reads zeros without touching memory and its MFMAs add nothing.  With no
-  // load under a branch the compiler can wait for exactly the chunk it needs
-  // (a conditional load would force it to wait for all of them).  The
-  // scheduling barriers keep the loads in chunk order.
-  auto load = [&](int j, v4i (&bb)[NB][2]) __attribute__((always_inline)) {
-    const uint32_t kc = j < my_full ? (uint32_t)(kbeg + ((wave + 4 * j) << 7)) : 0x80000000u;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        bb[b][h] = b < RB ? llvm_buffer_load_v4i32(rsrc_w, off[b] + 64u * h, kc, 2)
-                          : llvm_buffer_load_v4i32(rsrc_x, off[b] + 64u * h, kc, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  v4f acc[RB][MB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const v4i (&bb)[NB][2]) __attribute__((always_inline)) {
-    v8i op[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const v4i lo = bb[b][0], hi = bb[b][1];
-      op[b] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = mfma16<0>(op[rb], op[RB + mb], acc[rb][mb]);
-  };
-
-  // Tail chunk: a piece with valid bytes 0 < v < 16 is loaded as the 16 bytes
-  // ending at its last valid byte (within its row, since K >= 16) and moved
-  // into place at the end; a piece with none is zeroed there.
-  v4i tail[NB][2];
-  int tvalid[2] = {0, 0};
-  if (has_tail) {
-    const int kc = kbeg + ((wave + 4 * my_full) << 7);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) tvalid[h] = kend - (kc + 64 * h + 16 * g);
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int v = tvalid[h];
-        const uint32_t o = off[b] + (uint32_t)(kc + 64 * h) + (uint32_t)(v >= 16 ? 0 : v > 0 ? v - 16 : 0);
-        tail[b][h] = llvm_buffer_load_v4i32(b < RB ? rsrc_w : rsrc_x, o, 0, b < RB ? 2 : 0);
-      }
-  }
-  // D chunks in flight: chunk j lives in slot j % D and is refilled with chunk
-  // j + D right after its MFMAs; the last round issues no refills.
-  v4i buf[D][NB][2];
-#pragma unroll
-  for (int d = 0; d < D; ++d) load(d, buf[d]);
-  const int rounds = (my_full + D - 1) / D;
-  for (int rd = 0; rd + 1 < rounds; ++rd) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      mma(buf[d]);
-      load(rd * D + d + D, buf[d]);
-    }
-  }
-#pragma unroll
-  for (int d = 0; d < D; ++d) mma(buf[d]);
-  if (has_tail) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int v = tvalid[h];
-        if (v >= 16) continue;
-        if (v <= 0) {
-          tail[b][h] = v4i{0, 0, 0, 0};
-          continue;
-        }
-        const int sh = 16 - v, q = sh >> 2, r8 = sh & 3;
-        const uint32_t d0 = (uint32_t)tail[b][h].x, d1 = (uint32_t)tail[b][h].y;
-        const uint32_t d2 = (uint32_t)tail[b][h].z, d3 = (uint32_t)tail[b][h].w;
-        const uint32_t e0 = q == 0 ? d0 : q == 1 ? d1 : q == 2 ? d2 : d3;
-        const uint32_t e1 = q == 0 ? d1 : q == 1 ? d2 : q == 2 ? d3 : 0u;
-        const uint32_t e2 = q == 0 ? d2 : q == 1 ? d3 : 0u;
-        const uint32_t e3 = q == 0 ? d3 : 0u;
-        tail[b][h] = v4i{(int)__builtin_amdgcn_alignbyte(e1, e0, r8), (int)__builtin_amdgcn_alignbyte(e2, e1, r8),
-                         (int)__builtin_amdgcn_alignbyte(e3, e2, r8), (int)__builtin_amdgcn_alignbyte(0u, e3, r8)};
-      }
-    mma(tail);
-  }
-  skinny_finish<RB, MB, EPI>(acc, a, red, n0, s, wave, lane);
-}
-
 // ------------------------------------------------------- launch templates
 // Instantiated by the fp8g_launch_*.hip units.  EPI = the call has a bias or
 // an activation (kernels built without it compile only the plain epilogue).
@@ -1925,28 +1736,24 @@ static inline hipError_t with_format(int fmt, F &&f) {
 
 // The generic main kernel for one configuration.  Operand formats other than
 // E4M3 x E4M3 are built for the configurations the planner chooses (ALLFMT).
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool PP, bool ALLFMT, bool EPI>
+template <int BM, int BN, int STAGES, int WM, int WN, bool EPI>
 static hipError_t launch_main_cfg(const MainLaunch &l, hipStream_t stream) {
   const MainArgs a = main_args(l);
   const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(WM * WN * 64);
-  auto go = [&](auto fmt) {
+  return with_format(l.fmt, [&](auto fmt) {
     constexpr int F = decltype(fmt)::value;
-    if (l.k_tail) return dispatch(fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, true, PP, F, EPI>, grid, block, stream,
-                                  l.ev, a);
-    return dispatch(fp8g_main_kernel<BM, BN, BK, STAGES, WM, WN, false, PP, F, EPI>, grid, block, stream, l.ev, a);
-  };
-  if constexpr (ALLFMT) return with_format(l.fmt, go);
-  if (l.fmt != 0) return hipErrorInvalidValue;
-  return go(std::integral_constant<int, 0>{});
+    if (l.k_tail) return dispatch(fp8g_main_kernel<BM, BN, STAGES, WM, WN, true, F, EPI>, grid, block, stream, l.ev, a);
+    return dispatch(fp8g_main_kernel<BM, BN, STAGES, WM, WN, false, F, EPI>, grid, block, stream, l.ev, a);
+  });
 }
 
 // Tile sizes the planner chooses besides 256 x 256 (variants 3, 17, 18).
 template <bool EPI>
 static hipError_t launch_main_tiles_t(const MainLaunch &l, hipStream_t stream) {
   switch (l.variant) {
-    case 3: return launch_main_cfg<64, 64, 128, 3, 2, 2, false, true, EPI>(l, stream);
-    case 17: return launch_main_cfg<128, 256, 128, 3, 2, 4, false, true, EPI>(l, stream);
-    case 18: return launch_main_cfg<128, 128, 128, 4, 2, 4, false, true, EPI>(l, stream);
+    case 3: return launch_main_cfg<64, 64, 3, 2, 2, EPI>(l, stream);
+    case 17: return launch_main_cfg<128, 256, 3, 2, 4, EPI>(l, stream);
+    case 18: return launch_main_cfg<128, 128, 4, 2, 4, EPI>(l, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1954,7 +1761,7 @@ static hipError_t launch_main_tiles_t(const MainLaunch &l, hipStream_t stream) {
 // The five-slot kernel without stream-K (variant 10).
 template <bool EPI>
 static hipError_t launch_main4w_t(const MainLaunch &l, hipStream_t stream) {
-  if (l.k_tail) return hipErrorInvalidValue;  // K % 128 == 0 (or realigned rows) only
+  if (l.k_tail) return hipErrorInvalidValue;  // K % 128 == 0 only
   const MainArgs a = main_args(l);
   const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(256);
   return with_format(l.fmt, [&](auto fmt) {
@@ -1973,48 +1780,32 @@ static hipError_t launch_main5_dp(const MainLaunch &l, hipStream_t stream) {
   });
 }
 
-template <int RB, int MB, bool DIRECT, bool EPI, int NW = 4>
+template <int RB, int MB, bool EPI, int NW = 4>
 static hipError_t launch_skinny_cfg(const SkinnyLaunch &l, hipStream_t stream) {
   SkinnyArgs a{l.x, l.w, l.scale, l.y, l.partials, l.tickets, l.epoch, l.M, l.N, l.K, l.k_slice, l.vec,
                l.bias, l.act};
   const dim3 grid((unsigned)((l.N + 16 * RB - 1) / (16 * RB)), (unsigned)l.S), block(64 * NW);
-  if constexpr (DIRECT) {
-    if (l.fmt != 0) return hipErrorInvalidValue;
-    return dispatch(fp8g_skinny_direct_kernel<RB, MB, 4, EPI>, grid, block, stream, l.ev, a);
-  } else {
-    return with_format(l.fmt, [&](auto fmt) {
-      constexpr int F = decltype(fmt)::value;
-      return dispatch(fp8g_splitk_partial_kernel<RB, MB, F, EPI, NW>, grid, block, stream, l.ev, a);
-    });
-  }
+  return with_format(l.fmt, [&](auto fmt) {
+    constexpr int F = decltype(fmt)::value;
+    return dispatch(fp8g_splitk_partial_kernel<RB, MB, F, EPI, NW>, grid, block, stream, l.ev, a);
+  });
 }
 
-// Split-K variants 1-5 (LDS ring, 4 waves), 21-24 (LDS ring, 8 waves, rings two
-// chunks deep) and, with EPI, 11-15 (direct to registers, always built with the
-// general epilogue).
+// Split-K variants 1-5 (LDS rings, 4 waves) and 21-24 (LDS rings two chunks
+// deep, 8 waves).
 template <int MB, bool EPI>
 static hipError_t launch_skinny_mb(const SkinnyLaunch &l, hipStream_t stream) {
   switch (l.variant) {
-    case 21: if constexpr (MB <= 4) return launch_skinny_cfg<1, MB, false, EPI, 8>(l, stream); else break;
-    case 22: if constexpr (MB <= 2) return launch_skinny_cfg<2, MB, false, EPI, 8>(l, stream); else break;
-    case 23: if constexpr (MB <= 2) return launch_skinny_cfg<3, MB, false, EPI, 8>(l, stream); else break;
-    case 24: if constexpr (MB == 1) return launch_skinny_cfg<4, MB, false, EPI, 8>(l, stream); else break;
-    case 1: return launch_skinny_cfg<1, MB, false, EPI>(l, stream);
-    case 2: return launch_skinny_cfg<2, MB, false, EPI>(l, stream);
-    case 3: if constexpr (MB <= 2) return launch_skinny_cfg<3, MB, false, EPI>(l, stream); else break;
-    case 4: if constexpr (MB <= 2) return launch_skinny_cfg<4, MB, false, EPI>(l, stream); else break;
-    case 5: if constexpr (MB == 1) return launch_skinny_cfg<5, MB, false, EPI>(l, stream); else break;
+    case 21: if constexpr (MB <= 4) return launch_skinny_cfg<1, MB, EPI, 8>(l, stream); else break;
+    case 22: if constexpr (MB <= 2) return launch_skinny_cfg<2, MB, EPI, 8>(l, stream); else break;
+    case 23: if constexpr (MB <= 2) return launch_skinny_cfg<3, MB, EPI, 8>(l, stream); else break;
+    case 24: if constexpr (MB == 1) return launch_skinny_cfg<4, MB, EPI, 8>(l, stream); else break;
+    case 1: return launch_skinny_cfg<1, MB, EPI>(l, stream);
+    case 2: return launch_skinny_cfg<2, MB, EPI>(l, stream);
+    case 3: if constexpr (MB <= 2) return launch_skinny_cfg<3, MB, EPI>(l, stream); else break;
+    case 4: if constexpr (MB <= 2) return launch_skinny_cfg<4, MB, EPI>(l, stream); else break;
+    case 5: if constexpr (MB == 1) return launch_skinny_cfg<5, MB, EPI>(l, stream); else break;
     default: break;
-  }
-  if constexpr (EPI && MB <= 4) {
-    switch (l.variant) {
-      case 11: return launch_skinny_cfg<1, MB, true, true>(l, stream);
-      case 12: return launch_skinny_cfg<2, MB, true, true>(l, stream);
-      case 13: return launch_skinny_cfg<3, MB, true, true>(l, stream);
-      case 14: return launch_skinny_cfg<4, MB, true, true>(l, stream);
-      case 15: return launch_skinny_cfg<5, MB, true, true>(l, stream);
-      default: break;
-    }
   }
   return hipErrorInvalidValue;
 }

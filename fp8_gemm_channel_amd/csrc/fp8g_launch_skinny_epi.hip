@@ -1,5 +1,5 @@
-// fp8g_launch_skinny_epi.hip -- the split-K kernels with the general epilogue
-// (bias, activation), and the direct-to-register variants 11-15.
+// fp8g_launch_skinny_epi.hip -- the split-K kernel with the general epilogue
+// (bias, activation).
 #include "fp8g_kernels.hpp"
 
 namespace fp8g {

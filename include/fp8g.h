@@ -27,20 +27,18 @@
  *     step: "Claude Fable 5", Triton split-K cell; "Kimi K3 (256k)", SM120
  *     cell (skinny path with a scaled finalize kernel).  Here the step runs in
  *     the same launch, by the last workgroup to finish each column tile.
- *   - K need not be a multiple of any tile size: the pages zero-pad copies of
+ *   - K need not be a multiple of any tile size.  The pages zero-pad copies of
  *     the operands ("Kimi K3 (256k)", SM100 persistent-TMA Triton cell: zero
- *     bytes add nothing to the dot).  This library masks the K tail inside the
- *     kernel; for K % 128 != 0 on large main-path calls it also copies x and
- *     w, on every call, into rows padded to 128 bytes (cache-line-aligned rows
- *     stream much faster), see fp8g_plan.pad_k.  Nothing is cached between
- *     calls.
+ *     bytes add nothing to the dot); this library reads the operand rows where
+ *     they lie, at any byte alignment, and masks the last K step inside the
+ *     kernel (bytes past K enter as zeros).  No operand is copied or padded.
  *
  * Ownership and threading: the caller owns every buffer.  The library keeps no
  * data between calls; its only globals are a thread-local copy of the last
  * error message, an atomic call counter (ids for split-K tickets) and one
  * memory pool per device for call workspaces (created on first use, under a
- * lock; freed workspace memory stays in the pool for reuse until the process
- * ends).  Calls are asynchronous: they enqueue kernels on `stream` (a
+ * lock; it keeps up to 64 MiB of freed workspace for reuse and returns the
+ * rest).  Calls are asynchronous: they enqueue kernels on `stream` (a
  * hipStream_t; NULL is the default stream) and return without synchronising.
  * Buffers must stay valid until that work has finished.
  */
@@ -63,8 +61,10 @@ extern "C" {
 /* Largest supported K (bytes per operand row).  Kernels address a tile of up
  * to 256 rows through 32-bit buffer offsets. */
 #define FP8G_MAX_K ((int64_t)16777215)
-/* Largest supported M and N. */
-#define FP8G_MAX_MN ((int64_t)2147483647)
+/* Largest supported M and N: 2^30 - 1, so that a byte range of N fp32 scales
+ * or biases (4 N bytes) fits a 32-bit buffer range.  Shapes whose launch grid
+ * would exceed the device's limits are rejected with FP8G_ERR_UNSUPPORTED. */
+#define FP8G_MAX_MN ((int64_t)1073741823)
 
 /* Execution paths a plan can choose. */
 #define FP8G_PATH_NONE 0   /* M == 0 or N == 0: nothing to do */
@@ -93,11 +93,6 @@ typedef struct fp8g_plan {
                                each (all tiles unless stream-K) */
     int32_t sk_groups;      /* main path variant 16: stream-K workgroups that
                                share the remaining tiles; 0 otherwise */
-    int32_t pad_k;          /* main path, K % 128 != 0: x and w are first
-                               copied into rows of pad_k = K rounded up to 128
-                               bytes (zero-filled; part of the workspace) so
-                               that the kernel reads cache-line-aligned rows;
-                               0 otherwise */
 } fp8g_plan;
 
 /* y = bf16_rne((x . w^T) * scale), as defined above.
@@ -121,22 +116,19 @@ int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y,
  *   path    : FP8G_PATH_MAIN or FP8G_PATH_SPLITK (SPLITK needs M <= 128)
  *   variant : a configuration id valid for the path (fp8_gemm_plan_ex reports
  *             the tile it implies).  Main path: 10 = 256x256 tiles, eight
- *             waves, five LDS slots (large grids); 17 = 128x256 and 18 = 128x128
- *             (mid M); 3 = 64x64 (small problems); 2 = 128x128 four waves;
- *             19 = 256x256 tiles on four waves of 128x128 (the default in
- *             place of 10 when no K tail is left; K % 128 == 0 or realigned
- *             rows only);
- *             1, 4-7, 9 = other 256x256 schedules; 16 = variant 10 with
- *             stream-K (opt-in).  Split-K path: 1-5 = 16*v w rows per
- *             workgroup through per-wave LDS rings, 4 waves (the default for
- *             M > 32); 21-24 = 16*(v-20) rows with 8 waves (the default for
- *             M <= 32); 11-15 = 16*(v-10) rows loading straight into
- *             registers (K >= 16).  Row counts are limited by M (the staged x
- *             rows share the LDS): 1-5 up to 5/4/2 blocks for M <= 16/32/128,
- *             21-24 up to 4/3/1 blocks for M <= 16/32/64, 11-15 need M <= 64.
+ *             waves, five LDS slots, any K (the default for 256x256 tiles
+ *             with a K tail); 19 = 256x256 tiles on four waves of 128x128
+ *             (the default for 256x256 tiles when K % 128 == 0; needs it);
+ *             17 = 128x256 and 18 = 128x128 (mid M); 3 = 64x64 (small
+ *             problems); 16 = variant 10 with stream-K (opt-in).  Split-K
+ *             path: 1-5 = 16*v w rows per workgroup through per-wave LDS
+ *             rings, 4 waves (the default for M > 32); 21-24 = 16*(v-20)
+ *             rows with 8 waves (the default for M <= 32).  Row counts are
+ *             limited by M (the staged x rows share the LDS): 1-5 up to
+ *             5/4/2 blocks for M <= 16/32/128, 21-24 up to 4/3/1 blocks for
+ *             M <= 16/32/64.
  *   split_k : splitk path: 1..64 K slices; main path variant 16: 1..2048
- *             stream-K workgroups; other main variants, for K % 128 != 0:
- *             1 = read operand rows in place, 2 = realign them (pad_k)
+ *             stream-K workgroups; must be 0 for the other main variants.
  * Invalid overrides give FP8G_ERR_INVALID_ARG.  The result is the same
  * operation to within fp32 summation order. */
 int fp8_gemm_scaled_ex(const void *x, const void *w, const float *scale, void *y,
@@ -187,9 +179,9 @@ int fp8_gemm_scaled_act(const void *x, const void *w, const float *scale, const 
                         int32_t activation, void *stream);
 
 /* With forced plan parts as fp8_gemm_scaled_ex.  Operands other than E4M3 x
- * E4M3 are built for main variants 3, 10, 17, 18 and split-K variants 1-5
- * (everything the planner chooses); other forced variants give
- * FP8G_ERR_INVALID_ARG.  Bias and activation work with every variant. */
+ * E4M3 are built for every variant except stream-K (main variant 16), which
+ * gives FP8G_ERR_INVALID_ARG for them.  Bias and activation work with every
+ * variant. */
 int fp8_gemm_scaled_act_ex(const void *x, const void *w, const float *scale, const float *bias, void *y,
                            int64_t M, int64_t N, int64_t K, int32_t x_format, int32_t w_format,
                            int32_t activation, int32_t path, int32_t variant, int32_t split_k,
@@ -199,8 +191,8 @@ int fp8_gemm_scaled_act_ex(const void *x, const void *w, const float *scale, con
  * fp8_gemm_scaled_act_ex with two HIP events attached to the call's own
  * kernels (hipExtLaunchKernel): start_event is recorded when the call's first
  * kernel begins and stop_event when its last kernel has ended, so
- * hipEventElapsedTime(start, stop) is the GPU time of the call (one kernel, or
- * the row copy plus the GEMM when K is realigned) without the marker packets
+ * hipEventElapsedTime(start, stop) is the GPU time of the call's kernel
+ * without the marker packets
  * that hipEventRecord adds around it.  The stream-ordered workspace allocation
  * and release are not kernels and fall outside that window.
  *   start_event, stop_event : hipEvent_t handles created by the caller (with

@@ -54,12 +54,12 @@ def test_plan_of_benchmark_shapes(wl):
     else:
         assert p["path_name"] == "main"
         assert p["grid"] == -(-wl.M // p["tile_m"]) * -(-wl.N // p["tile_n"])
-        kk = p["pad_k"] or wl.K  # the kernel's K (rows realigned into pad_k bytes)
-        assert p["k_tail"] == (kk % p["tile_k"] != 0)
+        assert p["k_tail"] == (wl.K % p["tile_k"] != 0)
+        assert p["workspace_bytes"] == 0, "the main path copies nothing"
     if wl.M >= 4096:
         assert (p["tile_m"], p["tile_n"]) == (256, 256) and p["grid"] >= 256
     if wl.name == "odd-k-4127":
-        assert p["pad_k"] == 4224 and p["k_tail"] == 0
+        assert p["k_tail"] == 1
 
 
 def test_plan_special_extents():
@@ -77,7 +77,7 @@ def test_plan_overrides():
     p = fg.fp8_gemm_plan_ex(32, 12288, 4096, fg.PATH_SPLITK, 1, 4)
     assert p["split_k"] == 4 and p["k_slice"] == 1024
     assert p["workspace_bytes"] == _splitk_workspace(p, 32, 12288)
-    p = fg.fp8_gemm_plan_ex(32, 4096, 4096, fg.PATH_MAIN, 2, 0)
+    p = fg.fp8_gemm_plan_ex(32, 4096, 4096, fg.PATH_MAIN, 18, 0)
     assert p["path_name"] == "main" and p["tile_m"] == 128
     # split_k larger than the number of 128-byte chunks collapses to non-empty slices
     p = fg.fp8_gemm_plan_ex(8, 100, 300, fg.PATH_SPLITK, 0, 8)
@@ -125,7 +125,7 @@ def test_plan_splitk_invariants(M, N, K):
 
 
 @pytest.mark.parametrize("args", [
-    (-1, 4, 4), (4, -1, 4), (4, 4, -1), (4, 4, (1 << 24)), (2**31, 4, 4),
+    (-1, 4, 4), (4, -1, 4), (4, 4, -1), (4, 4, (1 << 24)), (2**31, 4, 4), (4, 2**30, 4), (2**30, 4, 4),
 ])
 def test_plan_rejects_bad_dims(args):
     with pytest.raises(fg.Fp8gError) as e:
@@ -133,45 +133,54 @@ def test_plan_rejects_bad_dims(args):
     assert e.value.status == fg.FP8G_ERR_INVALID_ARG
 
 
-def test_plan_row_realignment():
-    """K % 16 != 0: large main-path calls copy x and w into 16-byte rows first."""
-    p = fg.fp8_gemm_plan(4096, 4096, 4127)
-    assert p["pad_k"] == 4224 and p["workspace_bytes"] == 8192 * 4224 and p["k_tail"] == 0
-    assert fg.fp8_gemm_plan(4096, 4096, 4112)["pad_k"] == 4224    # 16-byte rows still straddle lines
-    assert fg.fp8_gemm_plan(4096, 4096, 4096)["pad_k"] == 0       # aligned rows
-    assert fg.fp8_gemm_plan(256, 256, 257)["pad_k"] == 0           # copy not worth it
-    assert fg.fp8_gemm_plan(2048, 2048, 2049)["pad_k"] == 0        # (measured slower)
-    assert fg.fp8_gemm_plan(32, 12288, 4127)["pad_k"] == 0         # split-K path reads in place
-    forced = fg.fp8_gemm_plan_ex(256, 256, 257, fg.PATH_MAIN, 0, 2)
-    assert forced["pad_k"] == 384 and forced["workspace_bytes"] == 512 * 384
-    assert fg.fp8_gemm_plan_ex(4096, 4096, 4127, fg.PATH_MAIN, 0, 1)["pad_k"] == 0
-    # the padded K must stay within the largest K (a tile's rows are one 32-bit range)
-    assert fg.fp8_gemm_plan_ex(256, 256, (1 << 24) - 1, fg.PATH_MAIN, 0, 2)["pad_k"] == 0
-    sk = fg.fp8_gemm_plan_ex(4096, 4352, 4127, fg.PATH_MAIN, 16, 0)
-    assert sk["pad_k"] == 4224 and sk["workspace_bytes"] > (4096 + 4352) * 4224
+def test_plan_limits():
+    """The largest M and N are accepted where the launch fits the grid limit;
+    a launch of 2^32 work-items or more is refused as unsupported."""
+    big = 2**30 - 1
+    p = fg.fp8_gemm_plan(big, 256, 128)
+    assert p["path_name"] == "main" and p["grid"] * 512 < 2**32
+    with pytest.raises(fg.Fp8gError) as e:
+        fg.fp8_gemm_plan(1, big, 128)          # 2^26 split-K workgroups of 256+ threads
+    assert e.value.status == fg.FP8G_ERR_UNSUPPORTED
+    with pytest.raises(fg.Fp8gError) as e:
+        fg.fp8_gemm_plan(big, big, 128)        # too many tiles
+    assert e.value.status == fg.FP8G_ERR_UNSUPPORTED
+
+
+def test_plan_odd_k_reads_rows_in_place():
+    """K % 128 != 0: no copy and no workspace on any path; the last K step is
+    masked in the kernel."""
+    for shape in [(4096, 4096, 4127), (4096, 4096, 4112), (256, 256, 257), (2048, 2048, 2049),
+                  (32, 12288, 4127), (8192, 8192, 8191)]:
+        p = fg.fp8_gemm_plan(*shape)
+        assert p["workspace_bytes"] == 0 and p["k_tail"] == 1, (shape, p)
+    assert fg.fp8_gemm_plan(4096, 4096, 4096)["k_tail"] == 0
+    # the main path takes no split_k outside stream-K
+    for sk in (1, 2):
+        with pytest.raises(fg.Fp8gError):
+            fg.fp8_gemm_plan_ex(4096, 4096, 4127, fg.PATH_MAIN, 0, sk)
 
 
 def test_plan_main_kernel_choice():
-    """256 x 256 tiles with no K tail left run on the one-wave-per-SIMD kernel
-    (variant 19); a K tail read in place keeps the eight-wave kernel (variant 10)."""
+    """256 x 256 tiles without a K tail run on the one-wave-per-SIMD kernel
+    (variant 19); with a K tail on the eight-wave kernel (variant 10)."""
     assert fg.fp8_gemm_plan(8192, 8192, 8192)["variant"] == 19
     assert fg.fp8_gemm_plan(4096, 4096, 4096)["variant"] == 19      # 256 tiles
-    odd = fg.fp8_gemm_plan(4096, 4096, 4127)                           # realigned rows
-    assert odd["variant"] == 19 and odd["pad_k"] == 4224 and odd["k_tail"] == 0
+    odd = fg.fp8_gemm_plan(4096, 4096, 4127)
+    assert odd["variant"] == 10 and odd["k_tail"] == 1
     assert fg.fp8_gemm_plan(3072, 3072, 3072)["variant"] == 19      # 144 tiles
-    assert fg.fp8_gemm_plan_ex(4096, 4096, 4127, fg.PATH_MAIN, 0, 1)["variant"] == 10  # in place: tail
     forced = fg.fp8_gemm_plan_ex(300, 300, 384, fg.PATH_MAIN, 19, 0)
     assert forced["variant"] == 19 and forced["grid"] == 4 and forced["tile_k"] == 128
     assert fg.fp8_gemm_plan_ex(4096, 4096, 4096, fg.PATH_MAIN, 10, 0)["variant"] == 10
-    # variant 19 has no K tail: an unaligned K needs the row realignment
-    assert fg.fp8_gemm_plan_ex(256, 256, 257, fg.PATH_MAIN, 19, 2)["pad_k"] == 384
+    # variant 19 has no K tail
     with pytest.raises(fg.Fp8gError):
-        fg.fp8_gemm_plan_ex(256, 256, 257, fg.PATH_MAIN, 19, 1)
+        fg.fp8_gemm_plan_ex(256, 256, 257, fg.PATH_MAIN, 19, 0)
 
 
 @pytest.mark.parametrize("kw", [
     dict(path=7), dict(variant=99), dict(split_k=65),
-    dict(split_k=-1), dict(path=fg.PATH_MAIN, split_k=3), dict(path=fg.PATH_SPLITK, variant=9),
+    dict(split_k=-1), dict(path=fg.PATH_MAIN, split_k=1), dict(path=fg.PATH_SPLITK, variant=9),
+    dict(path=fg.PATH_MAIN, variant=1), dict(path=fg.PATH_MAIN, variant=6), dict(path=fg.PATH_MAIN, variant=9),
     dict(path=fg.PATH_SPLITK, variant=18), dict(path=fg.PATH_SPLITK, variant=25),
     dict(path=fg.PATH_SPLITK, variant=24), dict(path=fg.PATH_SPLITK, variant=22, M=40),
     dict(path=fg.PATH_SPLITK, M=129), dict(path=fg.PATH_SPLITK, variant=3, M=65),

@@ -161,12 +161,12 @@ def test_splitk_back_to_back_calls_without_sync():
 
 
 def test_workspace_calls_on_two_streams():
-    """Workspace-using calls (split-K partials and tickets, realigned rows,
-    stream-K partials) queued on two streams that run concurrently: each call's
+    """Workspace-using calls (split-K partials and tickets, stream-K partials)
+    queued on two streams that run concurrently: each call's
     workspace is its own, so every output matches the oracle and the repeats
     match bit for bit."""
     cases = [((32, 1000, 4127), dict(path=fg.PATH_SPLITK, split_k=4)),
-             ((300, 520, 4127), dict(path=fg.PATH_MAIN, split_k=2)),
+             ((300, 520, 4127), dict(path=fg.PATH_MAIN, variant=16, split_k=3)),
              ((64, 264, 600), dict(path=fg.PATH_SPLITK, split_k=3)),
              ((512, 768, 1000), dict(path=fg.PATH_MAIN, variant=16, split_k=7))]
     data = [synth.fp8_inputs(M, N, K, seed=40 + i) for i, ((M, N, K), _) in enumerate(cases)]
@@ -241,7 +241,7 @@ def test_status_codes_on_gpu():
 
 @pytest.mark.parametrize("shape,kw", [
     ((130, 136, 1_000_003), {}),                               # main path, long odd rows
-    ((130, 136, 1_000_003), dict(path=fg.PATH_MAIN, split_k=2)),  # ... realigned first
+    ((300, 264, 1_000_003), dict(path=fg.PATH_MAIN, variant=10)),  # 256 x 256 tiles, in place
     ((3, 200, 2_000_001), {}),                                 # split-K path
     ((40, 300, 1_048_576 + 17), dict(path=fg.PATH_SPLITK, split_k=7)),
 ])

@@ -12,8 +12,8 @@ from tests.gpu_util import compare, run, say
 
 pytestmark = pytest.mark.gpu
 
-MAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 16, 17, 18, 19]
-SPLITK_VARIANTS = [0, 1, 2, 3, 4, 5, 11, 12, 13, 14, 15, 21, 22, 23, 24]
+MAIN_VARIANTS = [0, 3, 10, 16, 17, 18, 19]
+SPLITK_VARIANTS = [0, 1, 2, 3, 4, 5, 21, 22, 23, 24]
 
 
 def _draw_plan(rng, M, N, K):
@@ -26,7 +26,7 @@ def _draw_plan(rng, M, N, K):
             split_k = int(rng.choice([0, 1, 2, 3, 5, 8]))
         else:
             path, variant = fg.PATH_MAIN, int(rng.choice(MAIN_VARIANTS))
-            split_k = int(rng.integers(1, 40)) if variant == 16 and rng.random() < 0.7 else int(rng.choice([0, 1, 2]))
+            split_k = int(rng.integers(1, 40)) if variant == 16 and rng.random() < 0.7 else 0
         try:
             fg.fp8_gemm_plan_ex(M, N, K, path, variant, split_k)
             return path, variant, split_k

@@ -3,8 +3,7 @@
 Callers that replay work through graphs capture a call once and replay it.
 Every path that uses a workspace is captured here: split-K with several
 slices (partials and call-id tickets: the ticket words must not need zeroing
-between replays), the realigned-rows plan (row copy, then the GEMM) and
-stream-K.  Each graph is replayed several times with the program's own eager
+between replays) and stream-K, plus a main-path call with a K tail.  Each graph is replayed several times with the program's own eager
 work (a different GEMM, a synchronisation) in between, and every replay is
 compared with the eager result bit for bit, after the inputs were rewritten in
 place, so that a replay that reused stale data would show.
@@ -22,7 +21,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("splitk-S4", (32, 1000, 4127), dict(path=fg.PATH_SPLITK, split_k=4)),
     ("splitk-S8-bias-silu", (17, 777, 3000), dict(path=fg.PATH_SPLITK, split_k=8)),
-    ("realigned-rows", (2304, 2560, 3001), dict()),
+    ("main-odd-k", (700, 520, 3001), dict(path=fg.PATH_MAIN, variant=10)),
     ("stream-k", (513, 520, 1000), dict(path=fg.PATH_MAIN, variant=16, split_k=40)),
     ("main-v18-gelu", (300, 520, 1000), dict(path=fg.PATH_MAIN, variant=18)),
 ]

@@ -1,11 +1,11 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 same seeded inputs, element by element, within 1e-2 + 1e-2 * |ref|.
 
-Sizes the oracle finishes in seconds are compared in full; they span several
-tiles and ragged tails on every path and configuration.  The five benchmark
-shapes run with the default plan (the launch configuration bench.py times);
-the large ones are compared on sampled outputs that the oracle computes one
-by one, always including full rows and columns at the tile edges.
+Every comparison covers every element.  Small shapes span several tiles and
+ragged tails on every path and configuration; the five benchmark shapes run
+at their full sizes with the default plan (the launch configuration bench.py
+times), the oracle computing all of their outputs (about 17 s for 8192^3 on
+16 host threads).
 """
 import numpy as np
 import pytest
@@ -32,7 +32,7 @@ MAIN_SHAPES = [(300, 520, 4127), (257, 129, 200), (128, 128, 128), (65, 70, 33),
                (70, 300, 1), (40, 33, 17), (256, 256, 257), (300, 300, 384)]
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 9, 10, 16, 17, 18])
+@pytest.mark.parametrize("variant", [3, 10, 16, 17, 18])
 @pytest.mark.parametrize("shape", MAIN_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_main_variants_full(variant, shape):
     _full_case(*shape, path=fg.PATH_MAIN, variant=variant)
@@ -40,8 +40,7 @@ def test_main_variants_full(variant, shape):
 
 # ------------------------- main path, one wave per SIMD (variant 19, K % 128 == 0) --
 # One to five 128-byte K steps (the guarded last three steps alone, then with
-# the branch-free body before them), rows past M and N, a long K, and an odd K
-# through the row realignment.
+# the branch-free body before them), rows past M and N, a long K.
 V19_SHAPES = [(256, 256, 128), (257, 129, 256), (300, 300, 384), (300, 520, 512), (256, 256, 640),
               (513, 777, 4096), (40, 700, 1024)]
 
@@ -53,12 +52,12 @@ def test_main_one_wave_per_simd(shape):
 
 def test_main_one_wave_per_simd_matches_eight_wave():
     """Variants 19 and 10 add the same products in the same order: bit for bit
-    the same output, also with realigned rows (odd K)."""
-    for (M, N, K, sk) in [(300, 520, 1024, 0), (513, 264, 4127, 2)]:
+    the same output."""
+    for (M, N, K) in [(300, 520, 1024), (513, 264, 4224)]:
         x, w, s = synth.fp8_inputs(M, N, K, seed=13)
         say(f"v19 vs v10 {M}x{N}x{K}")
-        a = run(x, w, s, path=fg.PATH_MAIN, variant=19, split_k=sk)
-        b = run(x, w, s, path=fg.PATH_MAIN, variant=10, split_k=sk)
+        a = run(x, w, s, path=fg.PATH_MAIN, variant=19)
+        b = run(x, w, s, path=fg.PATH_MAIN, variant=10)
         assert np.array_equal(a, b)
         compare(a, oracle.gemm_scaled(x, w, s), f"{M}x{N}x{K} v19")
 
@@ -150,47 +149,16 @@ def test_splitk_up_to_128_x_rows(M):
     _full_case(M, 264, 600, path=fg.PATH_SPLITK)
 
 
-@pytest.mark.parametrize("variant", [11, 12, 13, 14, 15])
-@pytest.mark.parametrize("M", [1, 16, 17, 32, 40, 64])
-def test_splitk_direct_variants(variant, M):
-    """The direct-to-register kernel (16 * (variant - 10) rows per workgroup)
-    for every x-row block count, with ragged N, a K tail whose last chunk has
-    pieces with 0, 1..15 and 16 valid bytes, and 1..3 K slices."""
-    _full_case(M, 777, 3000, path=fg.PATH_SPLITK, variant=variant, split_k=3)
-    _full_case(M, 1024, 4096, path=fg.PATH_SPLITK, variant=variant, split_k=1)
-    _full_case(M, 1000, 4127, path=fg.PATH_SPLITK, variant=variant, split_k=2)
-    _full_case(M, 264, 600, path=fg.PATH_SPLITK, variant=variant, split_k=1)
-
-
 # ---------------------------------------------------- the benchmark shapes ----
-def _sampled(x, w, s, got, seed, count=6000, edges=()):
-    M, N = got.shape
-    mi, ni = synth.sample_positions(M, N, count, seed)
-    rows = [r for r in edges if r < M]
-    cols = [c for c in edges if c < N]
-    for r in rows:                           # full rows
-        mi = np.concatenate([mi, np.full(N, r)])
-        ni = np.concatenate([ni, np.arange(N)])
-    for c in cols:                           # full columns
-        mi = np.concatenate([mi, np.arange(M)])
-        ni = np.concatenate([ni, np.full(M, c)])
-    ref = oracle.gemm_scaled_at(x, w, s, mi, ni)
-    return compare(got[mi, ni], ref, f"sampled {M}x{N}")
-
-
 @pytest.mark.parametrize("wl", synth.WORKLOADS, ids=lambda w: w.name)
 def test_benchmark_shape(wl):
+    """Full size, default plan, every element against the oracle."""
     x, w, s = synth.fp8_inputs(wl.M, wl.N, wl.K, seed=42)
     plan = fg.fp8_gemm_plan(wl.M, wl.N, wl.K)
     say(f"{wl.name} default plan {plan}")
     got = run(x, w, s)
-    if wl.M * wl.N * wl.K <= 10**11:
-        compare(got, oracle.gemm_scaled(x, w, s), wl.name)
-    else:
-        # first/last rows and columns of tiles, plus random positions
-        t = 256
-        edges = (0, t - 1, t, wl.M - 1, wl.N - 1)
-        _sampled(x, w, s, got, seed=7, edges=edges)
+    diag = compare(got, oracle.gemm_scaled(x, w, s), wl.name)
+    say(f"{wl.name}: {diag}")
 
 
 @pytest.mark.parametrize("seed", [123, 456])
@@ -199,47 +167,33 @@ def test_benchmark_shape_other_seeds(name, seed):
     wl = synth.WORKLOAD_BY_NAME[name]
     x, w, s = synth.fp8_inputs(wl.M, wl.N, wl.K, seed=seed)
     say(f"{name} seed={seed}")
-    got = run(x, w, s)
-    if wl.M * wl.N * wl.K <= 10**11:
-        compare(got, oracle.gemm_scaled(x, w, s), name)
-    else:
-        _sampled(x, w, s, got, seed=seed, edges=(0, 255, 256, wl.M - 1))
+    compare(run(x, w, s), oracle.gemm_scaled(x, w, s), f"{name} seed={seed}")
 
 
-# ------------------------------------- odd K: operand rows realigned first ----
-@pytest.mark.parametrize("variant", [2, 3, 10, 17, 18])
-@pytest.mark.parametrize("shape", [(300, 520, 4127), (70, 300, 1), (40, 33, 17), (256, 256, 257), (129, 300, 1003)],
-                         ids=lambda s: "x".join(map(str, s)))
-def test_row_realignment_matches_in_place(variant, shape):
-    """split_k = 2 copies x and w into zero-padded 128-byte rows before the
-    kernel; the sums are the same as reading the rows in place (split_k = 1),
-    bit for bit, and both match the oracle."""
-    M, N, K = shape
-    x, w, s = synth.fp8_inputs(M, N, K, seed=9)
-    say(f"realign {shape} variant {variant}")
-    padded = run(x, w, s, path=fg.PATH_MAIN, variant=variant, split_k=2)
-    in_place = run(x, w, s, path=fg.PATH_MAIN, variant=variant, split_k=1)
-    compare(padded, oracle.gemm_scaled(x, w, s), f"{shape} v{variant} padded")
-    assert np.array_equal(padded, in_place), "padded rows changed the sums"
+# ------------------------------------------------- odd K, rows read in place ----
+def test_odd_k_no_workspace_plan():
+    """The odd-K benchmark shape runs one kernel on the operand rows as they
+    lie: no workspace, nothing copied."""
+    p = fg.fp8_gemm_plan(4096, 4096, 4127)
+    assert p["path_name"] == "main" and p["workspace_bytes"] == 0 and p["k_tail"] == 1
 
 
-def test_row_realignment_unaligned_pointers():
-    """Operand pointers at odd byte addresses with an odd K, default plan (pads)."""
+def test_odd_k_unaligned_pointers():
+    """Operand pointers at odd byte addresses with an odd K on 256 x 256 tiles,
+    every element."""
     import torch
     M, N, K = 2304, 2560, 3001
     x, w, s = synth.fp8_inputs(M, N, K, seed=10)
-    assert fg.fp8_gemm_plan(M, N, K)["pad_k"] == 3072
     xb = torch.zeros(M * K + 3, dtype=torch.uint8, device="cuda")
     wb = torch.zeros(N * K + 5, dtype=torch.uint8, device="cuda")
     xb[3:].copy_(torch.from_numpy(x.reshape(-1)))
     wb[5:].copy_(torch.from_numpy(w.reshape(-1)))
     sd = torch.from_numpy(s).cuda()
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    say("realign with unaligned operand pointers")
+    say("odd K with unaligned operand pointers")
     st = fg.fp8_gemm_scaled(xb.data_ptr() + 3, wb.data_ptr() + 5, sd.data_ptr(), y.data_ptr(), M, N, K,
                             torch.cuda.current_stream().cuda_stream)
     assert st == fg.FP8G_OK, fg.fp8_gemm_last_error()
     torch.cuda.synchronize()
     got = y.view(torch.int16).cpu().numpy().view(np.uint16)
-    mi, ni = synth.sample_positions(M, N, 4000, seed=11)
-    compare(got[mi, ni], oracle.gemm_scaled_at(x, w, s, mi, ni), "unaligned + realigned")
+    compare(got, oracle.gemm_scaled(x, w, s), "unaligned odd K")
