@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
     fp8_gemm_scaled_act_ex(..., path, variant, split_k, stream)
     fp8_gemm_scaled_act_timed(..., stream, start_event, stop_event)
                                                               events on the call's kernels
+    fp8_gemm_scaled_noalloc(x, w, scale, y, M, N, K, path, variant, split_k, stream)
+                                                              no allocation (library scratch)
     fp8_gemm_plan(M, N, K) / fp8_gemm_plan_ex(...)           host-only planner
     fp8_gemm_strerror(status), fp8_gemm_last_error()
 and the tensor-level convenience wrapper
@@ -45,7 +47,10 @@ ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_TANH = 0, 1, 2, 3
 
 #: Every symbol include/fp8g.h declares.
 EXPORTED_SYMBOLS = ("fp8_gemm_scaled", "fp8_gemm_scaled_ex", "fp8_gemm_scaled_act", "fp8_gemm_scaled_act_ex",
-                    "fp8_gemm_scaled_act_timed", "fp8_gemm_plan", "fp8_gemm_plan_ex", "fp8_gemm_strerror", "fp8_gemm_last_error")
+                    "fp8_gemm_scaled_act_timed", "fp8_gemm_scaled_noalloc", "fp8_gemm_plan", "fp8_gemm_plan_ex",
+                    "fp8_gemm_strerror", "fp8_gemm_last_error")
+#: Size of the device array the allocation-free entry point uses as workspace.
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class Plan(ctypes.Structure):
@@ -91,6 +96,8 @@ def _load() -> ctypes.CDLL:
     lib.fp8_gemm_scaled_act_timed.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32,
                                               vp, vp, vp]
     lib.fp8_gemm_scaled_act_timed.restype = ctypes.c_int
+    lib.fp8_gemm_scaled_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    lib.fp8_gemm_scaled_noalloc.restype = ctypes.c_int
     lib.fp8_gemm_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
     lib.fp8_gemm_plan.restype = ctypes.c_int
     lib.fp8_gemm_plan_ex.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(Plan)]
@@ -138,6 +145,13 @@ def fp8_gemm_scaled_act_timed(x: int, w: int, scale: int, bias: int, y: int, M: 
     first and last kernels (0 = none)."""
     return _lib.fp8_gemm_scaled_act_timed(x, w, scale, bias or None, y, M, N, K, x_format, w_format, activation,
                                           path, variant, split_k, stream, start_event or None, stop_event or None)
+
+
+def fp8_gemm_scaled_noalloc(x: int, w: int, scale: int, y: int, M: int, N: int, K: int,
+                            path: int = 0, variant: int = 0, split_k: int = 0, stream: int = 0) -> int:
+    """The allocation-free entry point (workspace from the library's device
+    array, at most NOALLOC_SCRATCH_BYTES); device addresses; returns the status."""
+    return _lib.fp8_gemm_scaled_noalloc(x, w, scale, y, M, N, K, path, variant, split_k, stream)
 
 
 def fp8_gemm_plan(M: int, N: int, K: int) -> dict:

@@ -22,7 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libfp8g.so")
 POISON_LIBRARY = os.path.join(PKG, "libfp8g_lds_poison.so")
-SOURCES = [os.path.join(CSRC, "fp8g_api.cpp"), os.path.join(CSRC, "fp8g_kernels.hip")] + sorted(
+SOURCES = [os.path.join(CSRC, f) for f in ("fp8g_api.cpp", "fp8g_kernels.hip", "fp8g_noalloc.hip")] + sorted(
     os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.startswith("fp8g_launch_") and f.endswith(".hip"))
 
 # Packed-fp32 VALU instructions are kept out of every device build.

@@ -377,9 +377,19 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
 // (main variant 16, E4M3 only).
 bool supports_formats(const fp8g_plan &p) { return !(p.path == FP8G_PATH_MAIN && p.variant == 16); }
 
+// Workspace of one call: from the pool (stream-ordered allocation, freed on
+// the stream after the kernel), or -- with `fixed` -- the caller's buffer.
+hipError_t call_workspace(const fp8g::FixedWorkspace *fixed, void **ws, size_t bytes, hipStream_t stream) {
+  return fixed ? fixed->get(stream, ws) : workspace_alloc(ws, bytes, stream);
+}
+hipError_t release_workspace(const fp8g::FixedWorkspace *fixed, void *ws, hipStream_t stream) {
+  return (fixed || !ws) ? hipSuccess : hipFreeAsync(ws, stream);
+}
+
 int run(const void *x, const void *w, const float *scale, const float *bias, void *y, int64_t M, int64_t N,
         int64_t K, int32_t x_format, int32_t w_format, int32_t act, int32_t path, int32_t variant, int32_t split_k,
-        void *stream_ptr, void *start_event = nullptr, void *stop_event = nullptr) {
+        void *stream_ptr, void *start_event = nullptr, void *stop_event = nullptr,
+        const fp8g::FixedWorkspace *fixed = nullptr) {
   g_last_error.clear();
   if ((x_format != FP8G_FMT_E4M3 && x_format != FP8G_FMT_E5M2) ||
       (w_format != FP8G_FMT_E4M3 && w_format != FP8G_FMT_E5M2))
@@ -389,6 +399,11 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
   fp8g_plan p;
   int st = plan_impl(M, N, K, path, variant, split_k, &p);
   if (st) return st;
+  if (fixed && (uint64_t)p.workspace_bytes > fixed->capacity)
+    return fail(FP8G_ERR_UNSUPPORTED,
+                "the plan needs %lld bytes of workspace; the allocation-free entry point has %llu "
+                "(choose fewer K slices or stream-K workgroups)",
+                (long long)p.workspace_bytes, (unsigned long long)fixed->capacity);
   if (fmt != 0 && !supports_formats(p))
     return fail(FP8G_ERR_INVALID_ARG, "%s variant %d is built for E4M3 operands only", p.path == FP8G_PATH_MAIN ? "main" : "split-K",
                 p.variant);
@@ -436,8 +451,8 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
       // stream-K: the tickets of the stream-K tiles, then two partial tiles per
       // stream-K workgroup; uninitialized (tickets carry the call id, partials
       // are written before they are read)
-      e = workspace_alloc(&ws, (size_t)p.workspace_bytes, stream);
-      if (e != hipSuccess) return hip_fail(e, "workspace allocation (main path)");
+      e = call_workspace(fixed, &ws, (size_t)p.workspace_bytes, stream);
+      if (e != hipSuccess) return hip_fail(e, "workspace (main path)");
       const int64_t sk_tiles = cdiv(M, p.tile_m) * cdiv(N, p.tile_n) - p.dp_tiles;
       l.n_dp = p.dp_tiles;
       l.n_sk = p.sk_groups;
@@ -446,10 +461,8 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
       l.epoch = call_id();
     }
     if (e == hipSuccess) e = fp8g::launch_main(l, stream);
-    if (ws) {
-      hipError_t f = hipFreeAsync(ws, stream);
-      if (e == hipSuccess && f != hipSuccess) return hip_fail(f, "hipFreeAsync(main-path workspace)");
-    }
+    const hipError_t f = release_workspace(fixed, ws, stream);
+    if (e == hipSuccess && f != hipSuccess) return hip_fail(f, "hipFreeAsync(main-path workspace)");
     return e == hipSuccess ? FP8G_OK : hip_fail(e, "main kernel launch");
   }
   // split-K
@@ -457,8 +470,8 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
   float *partials = nullptr;
   unsigned long long *tickets = nullptr;
   if (p.split_k > 1) {
-    e = workspace_alloc(&ws, (size_t)p.workspace_bytes, stream);
-    if (e != hipSuccess) return hip_fail(e, "workspace allocation (split-K)");
+    e = call_workspace(fixed, &ws, (size_t)p.workspace_bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "workspace (split-K)");
     // The workspace is not initialized: a ticket carries the call id, so stale
     // values are harmless, and every partial is written before it is read.
     tickets = (unsigned long long *)ws;
@@ -472,14 +485,20 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
   l.fmt = fmt;
   l.ev = events;
   e = fp8g::launch_skinny(l, stream);
-  if (ws) {
-    hipError_t f = hipFreeAsync(ws, stream);
-    if (e == hipSuccess && f != hipSuccess) return hip_fail(f, "hipFreeAsync(split-K workspace)");
-  }
+  const hipError_t f = release_workspace(fixed, ws, stream);
+  if (e == hipSuccess && f != hipSuccess) return hip_fail(f, "hipFreeAsync(split-K workspace)");
   return e == hipSuccess ? FP8G_OK : hip_fail(e, "split-K kernel launch");
 }
 
 }  // namespace
+
+namespace fp8g {
+int run_fixed_workspace(const void *x, const void *w, const float *scale, void *y, int64_t M, int64_t N, int64_t K,
+                        int32_t path, int32_t variant, int32_t split_k, void *stream, const FixedWorkspace &ws) {
+  return run(x, w, scale, nullptr, y, M, N, K, FP8G_FMT_E4M3, FP8G_FMT_E4M3, FP8G_ACT_NONE, path, variant, split_k,
+             stream, nullptr, nullptr, &ws);
+}
+}  // namespace fp8g
 
 extern "C" {
 

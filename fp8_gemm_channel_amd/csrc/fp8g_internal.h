@@ -79,6 +79,18 @@ enum class SkinnyKind { kRing4, kRing8 };
 int skinny_max_row_blocks(int M, SkinnyKind kind);  // limit on row_blocks for this M and kernel
 int skinny_chunk_bytes();                   // K granularity of one wave iteration
 
+// A workspace the caller owns, in place of the library's pool: `get` returns
+// its device address for the stream's device; `capacity` is its size.
+struct FixedWorkspace {
+  uint64_t capacity;
+  hipError_t (*get)(hipStream_t stream, void **ptr);
+};
+// fp8_gemm_scaled_ex with the call's workspace taken from `ws` (no
+// allocation); plans that need more than ws.capacity bytes are refused with
+// FP8G_ERR_UNSUPPORTED before anything is enqueued.
+int run_fixed_workspace(const void *x, const void *w, const float *scale, void *y, int64_t M, int64_t N, int64_t K,
+                        int32_t path, int32_t variant, int32_t split_k, void *stream, const FixedWorkspace &ws);
+
 hipError_t launch_main(const MainLaunch &l, hipStream_t stream);
 hipError_t launch_main5(const MainLaunch &l, hipStream_t stream);            // variants 10, 16
 hipError_t launch_main5_epi(const MainLaunch &l, hipStream_t stream);        // variant 10, bias / activation

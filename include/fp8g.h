@@ -207,6 +207,28 @@ int fp8_gemm_scaled_act_timed(const void *x, const void *w, const float *scale, 
                               int32_t activation, int32_t path, int32_t variant, int32_t split_k,
                               void *stream, void *start_event, void *stop_event);
 
+/* ---------------------------------------------------- allocation-free -----
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same
+ * operation and arguments as fp8_gemm_scaled_ex (path, variant, split_k: 0 =
+ * the planner's choice), but the call allocates nothing: where its plan needs
+ * a workspace (split-K with split_k > 1: fp32 partials and tickets; stream-K:
+ * partial tiles and tickets) it uses a device array inside the library of
+ * FP8G_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends.
+ *   Plans that need more workspace than that (fp8_gemm_plan_ex reports
+ *   workspace_bytes) give FP8G_ERR_UNSUPPORTED before anything is enqueued.
+ *   Nothing in the array has to be cleared between calls (tickets carry the
+ *   id of their call; partials are written before they are read).
+ *   All calls on one GPU share its array: calls whose kernels may overlap on
+ *   one GPU (different streams with no ordering between them) race on it and
+ *   must not be issued; calls ordered on one stream are safe.
+ * Errors as fp8_gemm_scaled; FP8G_ERR_HIP also if the array's device address
+ * cannot be obtained (looked up on the first call on each device). */
+#define FP8G_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+int fp8_gemm_scaled_noalloc(const void *x, const void *w, const float *scale, void *y,
+                            int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant,
+                            int32_t split_k, void *stream);
+
 /* Static description of a status code. */
 const char *fp8_gemm_strerror(int status);
 

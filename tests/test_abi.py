@@ -224,6 +224,18 @@ def test_timed_entry_checks_arguments_like_the_others():
     assert st == fg.FP8G_ERR_INVALID_ARG and "activation" in fg.fp8_gemm_last_error()
 
 
+def test_noalloc_refuses_oversized_workspace_without_hip():
+    """The allocation-free entry point checks the plan's workspace against its
+    device array before any HIP call."""
+    M, N, K, plan = 128, 65536, 4096, (fg.PATH_SPLITK, 0, 8)
+    assert fg.fp8_gemm_plan_ex(M, N, K, *plan)["workspace_bytes"] > fg.NOALLOC_SCRATCH_BYTES
+    st = fg.fp8_gemm_scaled_noalloc(FAKE * 2, FAKE * 4, FAKE * 6, FAKE * 40, M, N, K, *plan, 0)
+    assert st == fg.FP8G_ERR_UNSUPPORTED and "allocation-free" in fg.fp8_gemm_last_error()
+    # argument checks come first, as for the other entry points
+    st = fg.fp8_gemm_scaled_noalloc(FAKE * 2, FAKE * 4, FAKE * 6, 0, 16, 16, 64, 0, 0, 0, 0)
+    assert st == fg.FP8G_ERR_INVALID_ARG
+
+
 def test_empty_extent_is_a_no_op_even_with_null_pointers():
     assert fg.fp8_gemm_scaled(0, 0, 0, 0, 0, 16, 16, 0) == fg.FP8G_OK
     assert fg.fp8_gemm_scaled(0, 0, 0, 0, 16, 0, 16, 0) == fg.FP8G_OK
