@@ -96,6 +96,8 @@ hipError_t launch_main5(const MainLaunch &l, hipStream_t stream);            // 
 hipError_t launch_main5_epi(const MainLaunch &l, hipStream_t stream);        // variant 10, bias / activation
 hipError_t launch_main4w(const MainLaunch &l, hipStream_t stream);           // variant 19
 hipError_t launch_main4w_epi(const MainLaunch &l, hipStream_t stream);       // variant 19, bias / activation
+hipError_t launch_main4wr(const MainLaunch &l, hipStream_t stream);          // variant 20
+hipError_t launch_main4wr_epi(const MainLaunch &l, hipStream_t stream);      // variant 20, bias / activation
 hipError_t launch_main_tiles(const MainLaunch &l, hipStream_t stream);       // variants 3, 17, 18
 hipError_t launch_main_tiles_epi(const MainLaunch &l, hipStream_t stream);   // the same, bias / activation
 hipError_t launch_skinny_epi(const SkinnyLaunch &l, hipStream_t stream);     // bias / activation

@@ -1697,6 +1697,364 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
   main_epilogue16<BM, BN, WM, WN, EPI>(acc, a, smem, s_lds, b_lds, m0, n0, wave, lane, tid);
 }
 
+// ------------------------- main path, one wave per SIMD, cache-line rows (odd K)
+//
+// Variant 19's tiles, waves and MFMA order for rows that do not start on the
+// 128-byte line grid (K % 128 != 0).  A 128-byte K window of such a row spans two
+// cache lines, and streaming it as it lies costs the global-to-LDS path about
+// twice the line traffic of an aligned row (measured on MI355X, 4096^2 x 4127:
+// 85-91 us against 62 us for the same steps on aligned rows).  Here every row is
+// fetched as whole aligned lines instead, one line per row per K step, and each
+// lane rebuilds its operand bytes from the two lines in registers.
+//
+// Row r of a tile starts a_r bytes into its first line (a_r = row address mod
+// 128).  Line j of the row is the 128 bytes at (row address - a_r) + 128 j; the
+// K window of step t (k in [128 t, 128 t + 128)) is bytes [a_r, a_r + 128) of
+// the line pair (t, t + 1).  So step t needs lines t and t + 1 of every row: a
+// line is read during two consecutive steps.  LDS holds ten 16 KiB units, each
+// one line of half the tile's rows of one operand (L = tile rows 0-63 and
+// 128-191, H = 64-127 and 192-255, as in variant 19); x lines cycle through three
+// units per half, w lines through two.  A step runs four quadrants of 16 MFMAs,
+// each followed by a barrier, and every unit is read in one quadrant only:
+//
+//     Q1  w L x x L   reads x H window (t)       DMA x L line t + 3
+//     Q2  w L x x H   reads w H window (t)       DMA x H line t + 3
+//     Q3  w H x x L   reads w L window (t + 1)   DMA w H line t + 2
+//     Q4  w H x x H   reads x L window (t + 1)   DMA w L line t + 3
+//
+// A line is published by the barrier before its first reading quadrant and
+// retired by the barrier after its second (1.25 steps later); its DMA goes out in
+// the quadrant after the barrier that retired the line it replaces, 1.75 steps
+// (x) or 0.75 steps (w) before it is published.
+//
+// Operand reads.  Lane l (row l % 16 of a 16-row block, K group g = l / 16)
+// needs bytes [a_r + 32 g, a_r + 32 g + 32) of the line pair: three aligned
+// 16-byte chunks c0 = a_r / 16 + 2 g, c0 + 1, c0 + 2 (chunk c lies in line t + c / 8).
+// The DMA stores chunk c of row u at position (c + s_u) mod 8 with the row's
+// rotation s_u = ((u / 2) mod 8 - a_r / 16) mod 8, so the lane's three chunks sit
+// at positions (u / 2 + 2 g + i) mod 8 whatever a_r is: sixteen consecutive rows
+// hit sixteen different 16-byte bank groups, as with variant 19's swizzle.  The
+// reads go out in one quadrant; the bytes are shifted into place (a_r mod 16
+// bytes: whole dwords by selects, the rest by byte alignment) in the next
+// quadrant, just before the block's first MFMA, so no MFMA waits on a read.
+// In the last step the bytes at or past K are cleared in both operands.
+//
+// Requirements (checked by the host): x and w 128-byte aligned, so no line
+// starts before an operand; M K and N K multiples of 16, so the last row of
+// either operand ends on a 16-byte boundary and a tile's buffer range never cuts
+// a chunk (bytes past the range read as zero; bytes of the next row that a line
+// carries past K are cleared by the realignment).
+template <int FMT = 0, bool EPI = false>
+__global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
+  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2, NWAVES = 4;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+  constexpr int UNIT = 128 * BK;              // 16 KiB: one line of 128 rows
+  constexpr int UDPW = UNIT / 1024 / NWAVES;  // LDS-DMA instructions per wave per unit (4)
+  static_assert(FM == 8 && FN == 8 && UDPW == 4, "the quadrant schedule assumes 8 x 8 blocks");
+  static_assert(2 * BM * BN + 2 * BN * 4 <= 10 * UNIT, "epilogue tile, scales and biases fit");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[10 * UNIT];
+
+  const int K = a.K;
+  const int nk = (K + BK - 1) / BK;  // K steps; lines 0 .. nk of every row are fetched
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+  // unit of line j: x L 0-2, x H 3-5, w L 6-7, w H 8-9 (uniform: scalar arithmetic)
+  auto mod3 = [&](int j) __attribute__((always_inline)) { return j - 3 * (int)(((uint32_t)j * 0xAAABu) >> 17); };
+  auto u_xl = [&](int j) __attribute__((always_inline)) { return (uint32_t)(mod3(j) * UNIT); };
+  auto u_xh = [&](int j) __attribute__((always_inline)) { return (uint32_t)((3 + mod3(j)) * UNIT); };
+  auto u_wl = [&](int j) __attribute__((always_inline)) { return (uint32_t)((6 + (j & 1)) * UNIT); };
+  auto u_wh = [&](int j) __attribute__((always_inline)) { return (uint32_t)((8 + (j & 1)) * UNIT); };
+  auto exists = [&](int j) __attribute__((always_inline)) { return j <= nk; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_m = wave % WM, wave_n = wave / WM;
+  int tm, tn;
+  tile_coords(a, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
+  // Each tile's rows as one buffer from the line holding its first byte to the
+  // end of its last valid row (a multiple of 16 bytes: see above).
+  const uint8_t *bx = a.x + (size_t)m0 * K, *bw = a.w + (size_t)n0 * K;
+  const uint32_t ax0 = (uint32_t)((uintptr_t)bx & 127u), aw0 = (uint32_t)((uintptr_t)bw & 127u);
+  const v4i rx = make_rsrc(bx - ax0, ax0 + (uint32_t)rows_x * (uint32_t)K);
+  const v4i rw = make_rsrc(bw - aw0, aw0 + (uint32_t)rows_w * (uint32_t)K);
+  const float my_scale = llvm_buffer_load_f32(make_rsrc(a.scale + n0, (uint32_t)(a.N - n0) * 4u), (uint32_t)tid * 4u, 0, 0);
+  float my_bias = 0.0f;
+  if (EPI && a.bias)
+    my_bias = llvm_buffer_load_f32(make_rsrc(a.bias + n0, (uint32_t)(a.N - n0) * 4u), (uint32_t)tid * 4u, 0, 0);
+
+  // Byte offset of tile row r's start from its buffer's base (a0 = offset of row 0).
+  auto row_off = [&](uint32_t a0, int r) __attribute__((always_inline)) { return a0 + (uint32_t)r * (uint32_t)K; };
+  // Tile row of unit row u (0..127) of an L (h = 0) or H (h = 1) unit.
+  auto tile_row = [&](int u, int h) __attribute__((always_inline)) { return u + (u >= 64 ? 64 : 0) + 64 * h; };
+
+  // DMA instruction t of a wave fills unit rows (4t + wave) * 8 .. + 7 of a
+  // line: lane l takes unit row u = (4t + wave) * 8 + l / 8 and LDS position
+  // p = l % 8, i.e. chunk (p - s_u) mod 8 of the row's line; the line's start
+  // (row offset rounded down to 128) sits in the VGPR offset, the line index
+  // times 128 in the SGPR offset.
+  uint32_t vdx[2][UDPW], vdw[2][UDPW];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int t = 0; t < UDPW; ++t) {
+      const int u = (t * NWAVES + wave) * 8 + (lane >> 3);
+      const int r = tile_row(u, h), tau = (u >> 1) & 7, p = lane & 7;
+      const uint32_t ox = row_off(ax0, r), ow = row_off(aw0, r);
+      const int cx = (p - (tau - (int)((ox & 127u) >> 4))) & 7, cw = (p - (tau - (int)((ow & 127u) >> 4))) & 7;
+      vdx[h][t] = (ox & ~127u) + 16u * (uint32_t)cx;
+      vdw[h][t] = (ow & ~127u) + 16u * (uint32_t)cw;
+    }
+  auto dma_unit = [&](const v4i &rs, uint32_t unit, const uint32_t (&vo)[UDPW], int j, int t)
+      __attribute__((always_inline)) {
+    dma16(rs, smem_base + unit + (uint32_t)(t * NWAVES + wave) * 1024u, vo[t], (uint32_t)j * BK);
+  };
+  // The four DMA groups of the schedule (4 instructions per wave each); the one
+  // for quadrant q of step s carries line s + 3 (x L, x H, w L) or s + 2 (w H).
+  auto issue = [&](int q, int s, int t) __attribute__((always_inline)) {
+    if (q == 1) dma_unit(rx, u_xl(s + 3), vdx[0], s + 3, t);
+    else if (q == 2) dma_unit(rx, u_xh(s + 3), vdx[1], s + 3, t);
+    else if (q == 3) dma_unit(rw, u_wh(s + 2), vdw[1], s + 2, t);
+    else dma_unit(rw, u_wl(s + 3), vdw[0], s + 3, t);
+  };
+  auto group_exists = [&](int q, int s) __attribute__((always_inline)) { return exists(q == 3 ? s + 2 : s + 3); };
+
+  // Operand blocks of this lane: block b of a wave tile is unit row (wave half)
+  // * 64 + (b % 4) * 16 + l16 of an L (b < 4) or H unit; ab/ax hold its row's
+  // a_r (w rows for A blocks, x rows for B blocks).
+  const int g = lane >> 4, l16 = lane & 15;
+  const int tau_r = (l16 >> 1) & 7;
+  const uint32_t pos0 = (uint32_t)(((tau_r + 2 * g) & 7) << 4), pos1 = (uint32_t)(((tau_r + 2 * g + 1) & 7) << 4),
+                 pos2 = (uint32_t)(((tau_r + 2 * g + 2) & 7) << 4);
+  const uint32_t ra = (uint32_t)(wave_n * 64 + l16) * BK, rb = (uint32_t)(wave_m * 64 + l16) * BK;
+  // Row offsets of the lane's rows: block b's row is tile row (wave half) * 64
+  // (+ 64 past the first 64 unit rows) + (b % 4) * 16 + l16 (+ 64 for H), so its
+  // offset is the lane's base plus a block constant times K.  Only the two
+  // bases stay in registers; each use recomputes a_r (an add and a mask), and
+  // the bases pass through an empty asm once per step so that nothing derived
+  // from them is hoisted out of the K loop (48 addresses would not fit).
+  uint32_t obw = row_off(aw0, tile_row(wave_n * 64 + l16, 0)), obx = row_off(ax0, tile_row(wave_m * 64 + l16, 0));
+  auto a_of = [&](uint32_t base, int b) __attribute__((always_inline)) {
+    return (int)((base + (uint32_t)((b & 3) * 16 + (b >> 2) * 64) * (uint32_t)K) & 127u);
+  };
+  // Reads of one block's window from the units of lines t (S0) and t + 1 (S1):
+  // chunks 0 and 1 into f, chunk 2 into x3.
+  auto read_win = [&](uint32_t S0, uint32_t S1, uint32_t row, int ar, int i, v8i &f, v4i &x3)
+      __attribute__((always_inline)) {
+    const int c0 = (ar >> 4) + 2 * g;
+    const uint32_t pos = i == 0 ? pos0 : i == 1 ? pos1 : pos2;
+    const uint32_t at = (c0 + i >= 8 ? S1 : S0) + row + pos;
+    const uint4 v = *(const uint4 *)(smem + at);
+    if (i < 2) {
+      f[4 * i + 0] = (int)v.x; f[4 * i + 1] = (int)v.y; f[4 * i + 2] = (int)v.z; f[4 * i + 3] = (int)v.w;
+    } else {
+      x3 = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    }
+  };
+  // Shift the window into place: bytes [ar % 16, ar % 16 + 32) of the 48 read,
+  // in three stages that may run apart (each one MFMA slot): whole dwords move
+  // by 8 bytes, then by 4 bytes (V_PERM_B32 with a per-lane selector picking
+  // its high or its low source dword), then the last 0-3 bytes move by
+  // V_ALIGNBYTE_B32.  The state stays in f and x3 between stages.  With `tail`
+  // (the guarded last steps only) the last stage also clears the bytes at or
+  // past K when t is the last step.
+  constexpr uint32_t kHi = 0x07060504u, kLo = 0x03020100u;  // perm selectors: high or low dword
+  auto rstage = [&](v8i &f, v4i &x3, int ar, int t, int stage, auto tail) __attribute__((always_inline)) {
+    const uint32_t beta = (uint32_t)ar & 15u;
+    if (stage == 0) {
+      const uint32_t s8 = (beta & 8u) ? kHi : kLo;
+      f[0] = (int)__builtin_amdgcn_perm(f[2], f[0], s8); f[1] = (int)__builtin_amdgcn_perm(f[3], f[1], s8);
+      f[2] = (int)__builtin_amdgcn_perm(f[4], f[2], s8); f[3] = (int)__builtin_amdgcn_perm(f[5], f[3], s8);
+      f[4] = (int)__builtin_amdgcn_perm(f[6], f[4], s8); f[5] = (int)__builtin_amdgcn_perm(f[7], f[5], s8);
+      f[6] = (int)__builtin_amdgcn_perm(x3.x, f[6], s8); f[7] = (int)__builtin_amdgcn_perm(x3.y, f[7], s8);
+      x3.x = (int)__builtin_amdgcn_perm(x3.z, x3.x, s8); x3.y = (int)__builtin_amdgcn_perm(x3.w, x3.y, s8);
+    } else if (stage == 1) {
+      const uint32_t s4 = (beta & 4u) ? kHi : kLo;
+      f[0] = (int)__builtin_amdgcn_perm(f[1], f[0], s4); f[1] = (int)__builtin_amdgcn_perm(f[2], f[1], s4);
+      f[2] = (int)__builtin_amdgcn_perm(f[3], f[2], s4); f[3] = (int)__builtin_amdgcn_perm(f[4], f[3], s4);
+      f[4] = (int)__builtin_amdgcn_perm(f[5], f[4], s4); f[5] = (int)__builtin_amdgcn_perm(f[6], f[5], s4);
+      f[6] = (int)__builtin_amdgcn_perm(f[7], f[6], s4); f[7] = (int)__builtin_amdgcn_perm(x3.x, f[7], s4);
+      x3.x = (int)__builtin_amdgcn_perm(x3.y, x3.x, s4);
+    } else if (stage == 2) {
+      const uint32_t sh = beta & 3u;
+      f[0] = (int)__builtin_amdgcn_alignbyte(f[1], f[0], sh); f[1] = (int)__builtin_amdgcn_alignbyte(f[2], f[1], sh);
+      f[2] = (int)__builtin_amdgcn_alignbyte(f[3], f[2], sh); f[3] = (int)__builtin_amdgcn_alignbyte(f[4], f[3], sh);
+      f[4] = (int)__builtin_amdgcn_alignbyte(f[5], f[4], sh); f[5] = (int)__builtin_amdgcn_alignbyte(f[6], f[5], sh);
+      f[6] = (int)__builtin_amdgcn_alignbyte(f[7], f[6], sh); f[7] = (int)__builtin_amdgcn_alignbyte(x3.x, f[7], sh);
+      if (decltype(tail)::value && t == nk - 1) {
+        const int valid = K - t * BK - 32 * g;  // bytes of this lane's 32 that lie before K
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int v = valid - 4 * e;
+          const uint32_t m = v >= 4 ? 0xFFFFFFFFu : v <= 0 ? 0u : (1u << (8 * v)) - 1u;
+          f[e] = (int)((uint32_t)f[e] & m);
+        }
+      }
+    }
+  };
+  auto realign = [&](v8i &f, v4i &x3, int ar, int t, auto tail) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < 3; ++st) rstage(f, x3, ar, t, st, tail);
+  };
+
+  v4f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8i A[FN], B[FM];
+  v4i A3[FN], B3[FM];  // third chunk of each block's window until its realignment
+
+  // vmcnt with n DMA groups allowed to stay in flight.
+  auto wait_groups = [&](int n) __attribute__((always_inline)) {
+    switch (n) {
+      case 0: vm_wait<0>(); break;
+      case 1: vm_wait<UDPW>(); break;
+      case 2: vm_wait<2 * UDPW>(); break;
+      case 3: vm_wait<3 * UDPW>(); break;
+      case 4: vm_wait<4 * UDPW>(); break;
+      case 5: vm_wait<5 * UDPW>(); break;
+      default: vm_wait<6 * UDPW>(); break;
+    }
+  };
+
+  // Prologue: lines 0 and 1 of every unit, and line 0 of w H; then the first
+  // windows of A[0..3] and B[0..3]; then the groups the schedule places in the
+  // (virtual) step -1: x L 2, x H 2, w H 1, w L 2 (w L 2 into the unit of w L 0,
+  // free once the windows are read).
+#pragma unroll
+  for (int t = 0; t < UDPW; ++t) {
+    dma_unit(rx, u_xl(0), vdx[0], 0, t);
+    dma_unit(rw, u_wl(0), vdw[0], 0, t);
+  }
+#pragma unroll
+  for (int t = 0; t < UDPW; ++t) {
+    dma_unit(rx, u_xl(1), vdx[0], 1, t);
+    dma_unit(rw, u_wl(1), vdw[0], 1, t);
+  }
+#pragma unroll
+  for (int t = 0; t < UDPW; ++t) {
+    dma_unit(rx, u_xh(0), vdx[1], 0, t);
+    dma_unit(rx, u_xh(1), vdx[1], 1, t);
+    dma_unit(rw, u_wh(0), vdw[1], 0, t);
+  }
+  vm_wait<0>();
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      read_win(u_wl(0), u_wl(1), ra + b * 16 * BK, a_of(obw, b), i, A[b], A3[b]);
+      read_win(u_xl(0), u_xl(1), rb + b * 16 * BK, a_of(obx, b), i, B[b], B3[b]);
+    }
+  __syncthreads();  // the windows are read: w L 0 and x L 0 are retired
+#pragma unroll
+  for (int q = 1; q <= 4; ++q)
+    if (group_exists(q, -1)) {
+#pragma unroll
+      for (int t = 0; t < UDPW; ++t) issue(q, -1, t);
+    }
+  // B[1..3] are realigned in step 0's first quadrant, as in every step.
+#pragma unroll
+  for (int b = 0; b < 4; ++b) realign(A[b], A3[b], a_of(obw, b), 0, std::true_type{});
+  realign(B[0], B3[0], a_of(obx, 0), 0, std::true_type{});
+
+  // Step s.  STEADY: every DMA group and read of the schedule exists (s + 3 <=
+  // nk), so the body has no branches; the last steps take the guarded body.
+  // Reads go out with MFMAs 0-11 of their quadrant (three per block), DMAs with
+  // MFMAs 1, 5, 9, 13.  A block's realignment runs in its three stages with the
+  // three MFMAs that start four MFMAs before its first use: its reads went out
+  // at least a quadrant earlier, or (the first block read in a quadrant) ten
+  // MFMAs earlier.
+  auto step = [&](const int s, auto steady) __attribute__((always_inline)) {
+    constexpr bool STEADY = decltype(steady)::value;
+    using TAILC = std::integral_constant<bool, !STEADY>;
+    const bool next = STEADY || s + 1 < nk;  // the windows of step s + 1 exist
+    asm volatile("" : "+v"(obw), "+v"(obx));
+    // ---- Q1: w L x x L; read x H (s) into B[4..7]; realign B[1..4]
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int mb = q >> 2, nb = q & 3;
+      acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
+      if ((q & 3) < 3) rstage(B[1 + (q >> 2)], B3[1 + (q >> 2)], a_of(obx, 1 + (q >> 2)), s, q & 3, TAILC{});
+      if (q < 12) read_win(u_xh(s), u_xh(s + 1), rb + (q / 3) * 16 * BK, a_of(obx, 4 + q / 3), q % 3, B[4 + q / 3], B3[4 + q / 3]);
+      if ((q & 3) == 1 && (STEADY || group_exists(1, s))) issue(1, s, q >> 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // B1: publishes w H line s + 1; groups issued after it: w L s + 2, x L s + 3
+    if (STEADY) vm_wait<2 * UDPW>();
+    else wait_groups((int)group_exists(4, s - 1) + (int)group_exists(1, s));
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- Q2: w L x x H; read w H (s) into A[4..7]; realign B[5..7], A[4]
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int mb = 4 + (q >> 2), nb = q & 3;
+      acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
+      if (q < 12 && (q & 3) < 3) rstage(B[5 + (q >> 2)], B3[5 + (q >> 2)], a_of(obx, 5 + (q >> 2)), s, q & 3, TAILC{});
+      if (q >= 12 && (q & 3) < 3) rstage(A[4], A3[4], a_of(obw, 4), s, q & 3, TAILC{});
+      if (q < 12) read_win(u_wh(s), u_wh(s + 1), ra + (q / 3) * 16 * BK, a_of(obw, 4 + q / 3), q % 3, A[4 + q / 3], A3[4 + q / 3]);
+      if ((q & 3) == 1 && (STEADY || group_exists(2, s))) issue(2, s, q >> 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // B2: publishes w L line s + 2; after it: x L s + 3, x H s + 3
+    if (STEADY) vm_wait<2 * UDPW>();
+    else wait_groups((int)group_exists(1, s) + (int)group_exists(2, s));
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- Q3: w H x x L; read w L (s + 1) into A[0..3]; realign A[5..7], A[0]
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int nb = 4 + (q >> 2), mb = q & 3;
+      acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
+      if (q < 12 && (q & 3) < 3) rstage(A[5 + (q >> 2)], A3[5 + (q >> 2)], a_of(obw, 5 + (q >> 2)), s, q & 3, TAILC{});
+      if (next && q >= 12 && (q & 3) < 3) rstage(A[0], A3[0], a_of(obw, 0), s + 1, q & 3, TAILC{});
+      if (next && q < 12) read_win(u_wl(s + 1), u_wl(s + 2), ra + (q / 3) * 16 * BK, a_of(obw, q / 3), q % 3, A[q / 3], A3[q / 3]);
+      if ((q & 3) == 1 && (STEADY || group_exists(3, s))) issue(3, s, q >> 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // B3: publishes x L line s + 2; after it: x H s + 2, w H s + 1, w L s + 2,
+    // x L s + 3, x H s + 3, w H s + 2
+    if (STEADY) vm_wait<6 * UDPW>();
+    else
+      wait_groups((int)group_exists(2, s - 1) + (int)group_exists(3, s - 1) + (int)group_exists(4, s - 1) +
+                  (int)group_exists(1, s) + (int)group_exists(2, s) + (int)group_exists(3, s));
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- Q4: w H x x H; read x L (s + 1) into B[0..3]; realign A[1..3], B[0]
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int nb = 4 + (q >> 2), mb = 4 + (q & 3);
+      acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
+      if (next && q < 12 && (q & 3) < 3) rstage(A[1 + (q >> 2)], A3[1 + (q >> 2)], a_of(obw, 1 + (q >> 2)), s + 1, q & 3, TAILC{});
+      if (next && q >= 12 && (q & 3) < 3) rstage(B[0], B3[0], a_of(obx, 0), s + 1, q & 3, TAILC{});
+      if (next && q < 12) read_win(u_xl(s + 1), u_xl(s + 2), rb + (q / 3) * 16 * BK, a_of(obx, q / 3), q % 3, B[q / 3], B3[q / 3]);
+      if ((q & 3) == 1 && (STEADY || group_exists(4, s))) issue(4, s, q >> 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // B4: publishes x H line s + 2; after it: w H s + 1, w L s + 2, and the four
+    // groups of this step
+    if (STEADY) vm_wait<6 * UDPW>();
+    else
+      wait_groups((int)group_exists(3, s - 1) + (int)group_exists(4, s - 1) + (int)group_exists(1, s) +
+                  (int)group_exists(2, s) + (int)group_exists(3, s) + (int)group_exists(4, s));
+    __syncthreads();
+  };
+  int s = 0;
+  for (; s + 3 <= nk; ++s) step(s, std::true_type{});
+  for (; s < nk; ++s) step(s, std::false_type{});
+
+  // Every DMA has landed and every wave is done with the units: scales (and
+  // biases) go into LDS past the bf16 tile.
+  vm_wait<0>();
+  float *s_lds = (float *)(smem + 2 * BM * BN), *b_lds = s_lds + BN;
+  __syncthreads();
+  s_lds[tid] = my_scale;
+  if constexpr (EPI) b_lds[tid] = my_bias;
+  main_epilogue16<BM, BN, WM, WN, EPI>(acc, a, smem, s_lds, b_lds, m0, n0, wave, lane, tid);
+}
+
 // ------------------------------------------------------- launch templates
 // Instantiated by the fp8g_launch_*.hip units.  EPI = the call has a bias or
 // an activation (kernels built without it compile only the plain epilogue).
@@ -1767,6 +2125,16 @@ static hipError_t launch_main4w_t(const MainLaunch &l, hipStream_t stream) {
   return with_format(l.fmt, [&](auto fmt) {
     constexpr int F = decltype(fmt)::value;
     return dispatch(fp8g_main4w_kernel<F, EPI>, grid, block, stream, l.ev, a);
+  });
+}
+// The cache-line-row kernel (variant 20; the host checks its requirements).
+template <bool EPI>
+static hipError_t launch_main4wr_t(const MainLaunch &l, hipStream_t stream) {
+  const MainArgs a = main_args(l);
+  const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(256);
+  return with_format(l.fmt, [&](auto fmt) {
+    constexpr int F = decltype(fmt)::value;
+    return dispatch(fp8g_main4wr_kernel<F, EPI>, grid, block, stream, l.ev, a);
   });
 }
 template <bool EPI>

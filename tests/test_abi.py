@@ -166,8 +166,15 @@ def test_plan_main_kernel_choice():
     (variant 19); with a K tail on the eight-wave kernel (variant 10)."""
     assert fg.fp8_gemm_plan(8192, 8192, 8192)["variant"] == 19
     assert fg.fp8_gemm_plan(4096, 4096, 4096)["variant"] == 19      # 256 tiles
-    odd = fg.fp8_gemm_plan(4096, 4096, 4127)
+    odd = fg.fp8_gemm_plan(4096, 4096, 4127)                           # rows read in place
     assert odd["variant"] == 10 and odd["k_tail"] == 1
+    # the whole-line variant (opt-in) needs M K and N K multiples of 16
+    assert fg.fp8_gemm_plan_ex(4096, 4096, 4127, fg.PATH_MAIN, 20, 0)["variant"] == 20
+    assert fg.fp8_gemm_plan_ex(4096, 4104, 4128, fg.PATH_MAIN, 20, 0)["variant"] == 20
+    with pytest.raises(fg.Fp8gError):
+        fg.fp8_gemm_plan_ex(4097, 4096, 4127, fg.PATH_MAIN, 20, 0)
+    with pytest.raises(fg.Fp8gError):
+        fg.fp8_gemm_plan_ex(4096, 4104, 4127, fg.PATH_MAIN, 20, 0)
     assert fg.fp8_gemm_plan(3072, 3072, 3072)["variant"] == 19      # 144 tiles
     forced = fg.fp8_gemm_plan_ex(300, 300, 384, fg.PATH_MAIN, 19, 0)
     assert forced["variant"] == 19 and forced["grid"] == 4 and forced["tile_k"] == 128

@@ -62,6 +62,63 @@ def test_main_one_wave_per_simd_matches_eight_wave():
         compare(a, oracle.gemm_scaled(x, w, s), f"{M}x{N}x{K} v19")
 
 
+# ------------- main path, rows fetched as whole cache lines (variant 20, odd K) --
+# K from one byte (a single step) to several steps with every kind of tail; K
+# % 16 == 0 and K % 128 == 0 (rows realigned by whole chunks, or not at all);
+# M, N multiples of 16 (the variant needs M K and N K multiples of 16) with
+# rows past M and N in the edge tiles.
+V20_SHAPES = [(256, 256, 4127), (272, 400, 4127), (512, 768, 1000), (256, 512, 1), (304, 256, 17),
+              (256, 256, 129), (528, 272, 257), (256, 256, 383), (256, 256, 4112), (256, 256, 4160),
+              (256, 256, 4096), (48, 560, 3001), (768, 256, 8191), (272, 288, 640)]
+
+
+@pytest.mark.parametrize("shape", V20_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_main_cache_line_rows(shape):
+    """Variant 20 against the oracle, every element, and bit for bit against
+    variant 10 (both add the same 128-byte K steps in the same order)."""
+    M, N, K = shape
+    x, w, s = synth.fp8_inputs(M, N, K, seed=21)
+    say(f"v20 {shape}")
+    a = run(x, w, s, path=fg.PATH_MAIN, variant=20)
+    compare(a, oracle.gemm_scaled(x, w, s), f"{shape} v20")
+    b = run(x, w, s, path=fg.PATH_MAIN, variant=10)
+    assert np.array_equal(a, b), "variant 20 differs from variant 10"
+
+
+def test_odd_k_operands_inside_larger_buffers():
+    """K = 4127 (every row start offset mod 128 over 128 rows) with the operands
+    starting 0, 16 and 80 rows into larger buffers (128-byte aligned, then 112
+    and 48 bytes into a line), on the default plan and on the whole-line
+    variant 20, which falls back to variant 10 for operands that are not
+    128-byte aligned when it was not forced.  Every element, every time."""
+    import torch
+    M, N, K = 512, 528, 4127
+    x, w, s = synth.fp8_inputs(M, N, K, seed=22)
+    ref = oracle.gemm_scaled(x, w, s)
+    for skip in (0, 16, 80):  # whole rows before the operands: 128-aligned starts only when skip*K % 128 == 0
+        xb = torch.zeros((skip + M) * K, dtype=torch.uint8, device="cuda")
+        wb = torch.zeros((skip + N) * K, dtype=torch.uint8, device="cuda")
+        xb[skip * K:].copy_(torch.from_numpy(x.reshape(-1)))
+        wb[skip * K:].copy_(torch.from_numpy(w.reshape(-1)))
+        sd = torch.from_numpy(s).cuda()
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        say(f"v20 offsets skip={skip}")
+        st = fg.fp8_gemm_scaled(xb.data_ptr() + skip * K, wb.data_ptr() + skip * K, sd.data_ptr(), y.data_ptr(),
+                                M, N, K, torch.cuda.current_stream().cuda_stream)
+        assert st == fg.FP8G_OK, fg.fp8_gemm_last_error()
+        torch.cuda.synchronize()
+        compare(y.view(torch.int16).cpu().numpy().view(np.uint16), ref, f"skip={skip}")
+        aligned = skip * K % 128 == 0
+        st = fg.fp8_gemm_scaled_ex(xb.data_ptr() + skip * K, wb.data_ptr() + skip * K, sd.data_ptr(), y.data_ptr(),
+                                   M, N, K, fg.PATH_MAIN, 20, 0, torch.cuda.current_stream().cuda_stream)
+        if aligned:
+            assert st == fg.FP8G_OK, fg.fp8_gemm_last_error()
+            torch.cuda.synchronize()
+            compare(y.view(torch.int16).cpu().numpy().view(np.uint16), ref, f"skip={skip} v20")
+        else:  # forced whole-line rows need 128-byte-aligned operands
+            assert st == fg.FP8G_ERR_INVALID_ARG and "128-byte" in fg.fp8_gemm_last_error()
+
+
 # ------------------------------------------- main path, stream-K (variant 16) --
 # Forced stream-K workgroup counts on small grids: ranges that end inside a
 # tile, ranges that cover several tiles, tiles with one to many contributors,
