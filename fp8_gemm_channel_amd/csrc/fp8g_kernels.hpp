@@ -46,6 +46,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "fp8g_internal.h"
 
@@ -341,6 +342,7 @@ __device__ __forceinline__ void tile_coords(const MainArgs &a, int &tm, int &tn)
 template <int BM, int BN, int NTHREADS>
 __device__ __forceinline__ void store_tile_rows(const MainArgs &a, const uint8_t *smem, int m0, int n0, int tid) {
   constexpr int CPR = BN / 8, PITCH = 2 * BN, TOTAL = BM * CPR;
+  auto sw = [](int r) __attribute__((always_inline)) { return r & (CPR - 1); };
   if constexpr (TOTAL % NTHREADS == 0 && NTHREADS % CPR == 0) {
     constexpr int ITERS = TOTAL / NTHREADS, B = ITERS < 8 ? ITERS : 8;
     static_assert(ITERS % B == 0, "whole batches");
@@ -356,7 +358,7 @@ __device__ __forceinline__ void store_tile_rows(const MainArgs &a, const uint8_t
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           const int r = r0 + (j0 + b) * RSTEP;
-          v[b] = *(const v4i *)(smem + r * PITCH + ((c ^ (r & (CPR - 1))) << 4));
+          v[b] = *(const v4i *)(smem + r * PITCH + ((c ^ sw(r)) << 4));
         }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
@@ -371,7 +373,7 @@ __device__ __forceinline__ void store_tile_rows(const MainArgs &a, const uint8_t
     const int r = idx / CPR, c = idx % CPR;
     const int m = m0 + r, n = n0 + 8 * c;
     if (m >= a.M || n >= a.N) continue;
-    const uint4 v = *(const uint4 *)(smem + r * PITCH + ((c ^ (r & (CPR - 1))) << 4));
+    const uint4 v = *(const uint4 *)(smem + r * PITCH + ((c ^ sw(r)) << 4));
     uint16_t *dst = a.y + (size_t)m * a.N + n;
     if (a.ystore == 16) {  // N % 8 == 0 and y 16-byte aligned: the chunk is whole
       __builtin_nontemporal_store(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, (v4i *)dst);
@@ -1473,6 +1475,175 @@ __device__ __forceinline__ void main_epilogue16(const v4f (&acc)[BN / WN / 16][B
 #undef FP8G_EPI
 }
 
+// Epilogue of variant 20, whose operand blocks carry tile rows in a per-call
+// order (fp8g_main4wr_kernel).  Lane row i of a 16-row block carries the tile
+// row perm(b, h, i); rows 2j and 2j + 1 are 128 apart.  So lane l (l16 = l % 16,
+// g = l / 16) holds, in accumulator block (nb, mb), row mrow[mb] (its own l16 in
+// x block mb) and, for elements e = 0, 1, 2, 3, columns pa[nb], pa[nb] + 128,
+// pb[nb], pb[nb] + 128 (lane rows 4 g + e of w block nb): scattered rows and
+// columns, but in pairs 128 apart.
+//
+// The bf16 tile is staged as column pairs: dword p (0..127) of row r holds
+// columns p (low half) and p + 128 (high half), so each element pair is one
+// 4-byte write.  Row pitch 512 bytes; pair chunk c = p / 4 of row r at position c
+// ^ pswz(r), pswz(r) = ((r / 16) ^ r) mod 16; dword j of a chunk at j ^ ((c / 8)
+// mod 4).  One write instruction stores one pair p_g per lane group g (the four
+// agree mod 32 and differ in p / 32: four dword positions) for sixteen rows
+// (which agree mod 16 and differ in r / 16: sixteen chunk positions), so the 64
+// lanes write 64 different banks.
+__device__ __forceinline__ int pswz(int r) { return ((r >> 4) ^ r) & 15; }
+
+// Writes the 256 x 256 bf16 tile staged by main_epilogue_perm_t to y (256
+// threads).  Pass q (0..15) takes column group G = 4 (q % 4) + t % 4 of row 64 (q
+// / 4) + t / 4 (thread t): pair chunks 2G and 2G + 1, i.e. columns 8 G .. 8 G + 7
+// (low halves) and 128 + 8 G .. (high halves), one 16-byte store each.  Within a
+// pass the chunks' dword order is fixed ((2G / 8) mod 4 = q mod 4), four lanes
+// store 64 contiguous bytes of a row, and the sixteen rows a wave reads have
+// different pswz (no bank conflicts).
+__device__ __forceinline__ void store_tile_pairs(const MainArgs &a, const uint8_t *smem, int m0, int n0, int tid) {
+  constexpr int PITCH = 512;
+  // columns 8 G .. + 7 (lo) and 128 + 8 G .. + 7 (hi) of row r for pass q
+  auto fetch = [&](int q, int r, int G, v4i &lo, v4i &hi) __attribute__((always_inline)) {
+    v4i d[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 2 * G + h;
+      const v4i v = *(const v4i *)(smem + r * PITCH + ((c ^ pswz(r)) << 4));
+      switch (q & 3) {  // pair 4 c + j is stored at dword j ^ (q % 4)
+        case 0: d[h] = v; break;
+        case 1: d[h] = v4i{v[1], v[0], v[3], v[2]}; break;
+        case 2: d[h] = v4i{v[2], v[3], v[0], v[1]}; break;
+        default: d[h] = v4i{v[3], v[2], v[1], v[0]}; break;
+      }
+    }
+    const uint32_t p[8] = {(uint32_t)d[0][0], (uint32_t)d[0][1], (uint32_t)d[0][2], (uint32_t)d[0][3],
+                           (uint32_t)d[1][0], (uint32_t)d[1][1], (uint32_t)d[1][2], (uint32_t)d[1][3]};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lo[k] = (int)__builtin_amdgcn_perm(p[2 * k + 1], p[2 * k], 0x05040100u);  // low halves
+      hi[k] = (int)__builtin_amdgcn_perm(p[2 * k + 1], p[2 * k], 0x07060302u);  // high halves
+    }
+  };
+  if (a.ystore == 16 && m0 + 256 <= a.M && n0 + 256 <= a.N) {
+#pragma unroll
+    for (int q0 = 0; q0 < 16; q0 += 4) {
+      v4i lo[4], hi[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int q = q0 + b;
+        fetch(q, 64 * (q >> 2) + (tid >> 2), 4 * (q & 3) + (tid & 3), lo[b], hi[b]);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int q = q0 + b, r = 64 * (q >> 2) + (tid >> 2), G = 4 * (q & 3) + (tid & 3);
+        uint16_t *row = a.y + (size_t)(m0 + r) * a.N + n0;
+        __builtin_nontemporal_store(lo[b], (v4i *)(row + 8 * G));
+        __builtin_nontemporal_store(hi[b], (v4i *)(row + 128 + 8 * G));
+      }
+    }
+    return;
+  }
+#pragma unroll 4
+  for (int q = 0; q < 16; ++q) {
+    const int r = 64 * (q >> 2) + (tid >> 2), G = 4 * (q & 3) + (tid & 3);
+    const int m = m0 + r;
+    if (m >= a.M || n0 + 8 * G >= a.N) continue;
+    v4i lo, hi;
+    fetch(q, r, G, lo, hi);
+    uint16_t *row = a.y + (size_t)m * a.N + n0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n = n0 + 128 * h + 8 * G;
+      if (n >= a.N) continue;
+      const v4i v = h ? hi : lo;
+      uint16_t *dst = row + 128 * h + 8 * G;
+      if (a.ystore == 16) {  // N % 8 == 0 and y 16-byte aligned: the chunk is whole
+        __builtin_nontemporal_store(v, (v4i *)dst);
+      } else if (a.ystore == 8) {  // N % 4 == 0 and y 8-byte aligned
+        *(uint2 *)dst = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+        if (n + 4 < a.N) *(uint2 *)(dst + 4) = make_uint2((uint32_t)v[2], (uint32_t)v[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < a.N) dst[e] = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
+template <int ACT, bool BIAS>
+__device__ __forceinline__ void main_epilogue_perm_t(const v4f (&acc)[8][8], const MainArgs &a, uint8_t *smem,
+                                                     const float *s_lds, const float *b_lds, int m0, int n0,
+                                                     const int (&mrow)[8], const int (&pa)[8], const int (&pb)[8],
+                                                     int tid) {
+  constexpr int PITCH = 512;
+  __syncthreads();  // s_lds (and b_lds) are published
+  uint32_t rbase[8], rsw[8];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    rbase[mb] = (uint32_t)mrow[mb] * PITCH;
+    rsw[mb] = (uint32_t)pswz(mrow[mb]) << 4;
+  }
+  auto val = [&](float v, float scl, float bs) __attribute__((always_inline)) {
+    float z = v * scl;
+    if constexpr (BIAS) z += bs;
+    return activation<ACT>(z);
+  };
+  // byte offset of pair p within its row, before the row's chunk swizzle
+  auto at = [](int p) __attribute__((always_inline)) {
+    return ((uint32_t)(p >> 2) << 4) | ((uint32_t)((p & 3) ^ ((p >> 5) & 3)) << 2);
+  };
+  // Every scale (and bias) this lane needs is read before the first write: LDS
+  // operations complete in order, so a read behind writes waits for all of them.
+  float sc[8][4], bi[8][4];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const int col[4] = {pa[nb], pa[nb] + 128, pb[nb], pb[nb] + 128};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sc[nb][e] = s_lds[col[e]];
+      bi[nb][e] = BIAS ? b_lds[col[e]] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const uint32_t ca = at(pa[nb]), cb = at(pb[nb]);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const v4f &v = acc[nb][mb];
+      *(uint32_t *)(smem + (rbase[mb] | (ca ^ rsw[mb]))) =
+          bf16x2_rne(val(v[0], sc[nb][0], bi[nb][0]), val(v[1], sc[nb][1], bi[nb][1]));
+      *(uint32_t *)(smem + (rbase[mb] | (cb ^ rsw[mb]))) =
+          bf16x2_rne(val(v[2], sc[nb][2], bi[nb][2]), val(v[3], sc[nb][3], bi[nb][3]));
+    }
+  }
+  __syncthreads();
+  store_tile_pairs(a, smem, m0, n0, tid);
+}
+template <bool EPI>
+__device__ __forceinline__ void main_epilogue_perm(const v4f (&acc)[8][8], const MainArgs &a, uint8_t *smem,
+                                                   const float *s_lds, const float *b_lds, int m0, int n0,
+                                                   const int (&mrow)[8], const int (&pa)[8], const int (&pb)[8],
+                                                   int tid) {
+  if constexpr (!EPI) {
+    main_epilogue_perm_t<kActNone, false>(acc, a, smem, s_lds, b_lds, m0, n0, mrow, pa, pb, tid);
+    return;
+  }
+  const int sel = a.act * 2 + (a.bias != nullptr ? 1 : 0);
+#define FP8G_EPI(ACT, BIAS) main_epilogue_perm_t<ACT, BIAS>(acc, a, smem, s_lds, b_lds, m0, n0, mrow, pa, pb, tid)
+  switch (sel) {
+    case 1: FP8G_EPI(kActNone, true); break;
+    case 2: FP8G_EPI(kActRelu, false); break;
+    case 3: FP8G_EPI(kActRelu, true); break;
+    case 4: FP8G_EPI(kActSilu, false); break;
+    case 5: FP8G_EPI(kActSilu, true); break;
+    case 6: FP8G_EPI(kActGeluTanh, false); break;
+    case 7: FP8G_EPI(kActGeluTanh, true); break;
+    default: FP8G_EPI(kActNone, false); break;
+  }
+#undef FP8G_EPI
+}
+
 // ------------------------------------------- main path, one wave per SIMD
 //
 // 256 x 256 tiles and 128-byte K steps with four waves, each owning a 128 (m) x
@@ -1699,23 +1870,38 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
 
 // ------------------------- main path, one wave per SIMD, cache-line rows (odd K)
 //
-// Variant 19's tiles, waves and MFMA order for rows that do not start on the
-// 128-byte line grid (K % 128 != 0).  A 128-byte K window of such a row spans two
-// cache lines, and streaming it as it lies costs the global-to-LDS path about
-// twice the line traffic of an aligned row (measured on MI355X, 4096^2 x 4127:
-// 85-91 us against 62 us for the same steps on aligned rows).  Here every row is
-// fetched as whole aligned lines instead, one line per row per K step, and each
-// lane rebuilds its operand bytes from the two lines in registers.
+// Variant 19's tiles, waves and MFMA order for odd K, where rows do not start on
+// the 128-byte line grid.  A 128-byte K window of such a row spans two cache
+// lines, and streaming it as it lies costs the global-to-LDS path about twice
+// the line traffic of an aligned row (measured on MI355X, 4096^2 x 4127: 85-91
+// us against 62 us for the same steps on aligned rows).  Here every row is
+// fetched as whole aligned lines, one line per row per K step, and each lane
+// rebuilds its operand bytes from two lines in registers.
 //
-// Row r of a tile starts a_r bytes into its first line (a_r = row address mod
-// 128).  Line j of the row is the 128 bytes at (row address - a_r) + 128 j; the
-// K window of step t (k in [128 t, 128 t + 128)) is bytes [a_r, a_r + 128) of
-// the line pair (t, t + 1).  So step t needs lines t and t + 1 of every row: a
-// line is read during two consecutive steps.  LDS holds ten 16 KiB units, each
-// one line of half the tile's rows of one operand (L = tile rows 0-63 and
-// 128-191, H = 64-127 and 192-255, as in variant 19); x lines cycle through three
-// units per half, w lines through two.  A step runs four quadrants of 16 MFMAs,
-// each followed by a barrier, and every unit is read in one quadrant only:
+// Row r of a tile starts o_r = a0 + r K bytes past the line holding the tile's
+// first byte (a0 = that byte's address mod 128); write o_r mod 128 = 16 c_r +
+// beta_r (chunk c_r, byte beta_r of its line).  The K window of step t is then
+// the nine 16-byte chunks c_r .. c_r + 8 of the row's lines t and t + 1, shifted
+// down by beta_r bytes.
+//
+// Row order.  For odd K, r -> o_r mod 128 is a bijection of r mod 128, so tile
+// rows can be dealt to MFMA block lanes by (c, beta): lane row i (0..15) of
+// block b (0..7) of wave half h carries the row with c = i / 2 and beta = 2 b +
+// h (lane rows 2 j and 2 j + 1 take the two rows of that class, 128 apart):
+//
+//     perm(b, h, i) = ((16 (i / 2) + 2 b + h - a0) K^-1 mod 128) + 128 (i mod 2)
+//
+// A block's shift is then beta / 4 = b / 2 whole dwords, known at compile time,
+// plus beta mod 4 = 2 (b mod 2) + h bytes, a wave-uniform value: eight
+// V_ALIGNBYTE_B32 per 32-byte window and no branch.  Where a lane finds its
+// chunks in LDS does not depend on the call either.  The epilogue puts the rows
+// back in order (main_epilogue_perm).
+//
+// LDS holds ten 16 KiB units, each one line of half the tile's rows of one
+// operand (L = blocks 0-3 of both wave halves, H = blocks 4-7; unit row 64 h + 16
+// (b mod 4) + i); x lines cycle through three units per half, w lines through
+// two.  A step runs four quadrants of 16 MFMAs, each followed by a barrier, and
+// every unit is read in one quadrant only:
 //
 //     Q1  w L x x L   reads x H window (t)       DMA x L line t + 3
 //     Q2  w L x x H   reads w H window (t)       DMA x H line t + 3
@@ -1727,23 +1913,29 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
 // the quadrant after the barrier that retired the line it replaces, 1.75 steps
 // (x) or 0.75 steps (w) before it is published.
 //
-// Operand reads.  Lane l (row l % 16 of a 16-row block, K group g = l / 16)
-// needs bytes [a_r + 32 g, a_r + 32 g + 32) of the line pair: three aligned
-// 16-byte chunks c0 = a_r / 16 + 2 g, c0 + 1, c0 + 2 (chunk c lies in line t + c / 8).
-// The DMA stores chunk c of row u at position (c + s_u) mod 8 with the row's
-// rotation s_u = ((u / 2) mod 8 - a_r / 16) mod 8, so the lane's three chunks sit
-// at positions (u / 2 + 2 g + i) mod 8 whatever a_r is: sixteen consecutive rows
-// hit sixteen different 16-byte bank groups, as with variant 19's swizzle.  The
-// reads go out in one quadrant; the bytes are shifted into place (a_r mod 16
-// bytes: whole dwords by selects, the rest by byte alignment) in the next
-// quadrant, just before the block's first MFMA, so no MFMA waits on a read.
-// In the last step the bytes at or past K are cleared in both operands.
+// In a unit, row i's window chunk v (line chunk (c + v) mod 8) sits at position
+// v ^ swz16(i).  Lane l (i = l mod 16, K group g = l / 16) reads window chunks
+// 2 g, 2 g + 1 and 2 g + 2, the last ones from the unit of line t + 1 once c + v
+// reaches 8: positions and unit choice depend on the lane alone.  The reads go
+// out in one quadrant and the shift is applied in the next, just before the
+// block's first MFMA; in the last step the bytes at or past K are cleared in
+// both operands.
 //
-// Requirements (checked by the host): x and w 128-byte aligned, so no line
-// starts before an operand; M K and N K multiples of 16, so the last row of
-// either operand ends on a 16-byte boundary and a tile's buffer range never cuts
-// a chunk (bytes past the range read as zero; bytes of the next row that a line
-// carries past K are cleared by the realignment).
+// Requirements (checked by the host): K odd; x and w 128-byte aligned, so no
+// line starts before an operand; M K and N K multiples of 16, so the last row
+// of either operand ends on a 16-byte boundary and a tile's buffer range never
+// cuts a chunk (bytes past the range read as zero; bytes of the next row that a
+// line carries past K are cleared).
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(std::integral_constant<int, 0>{}) .. f(std::integral_constant<int, N - 1>{}).
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int FMT = 0, bool EPI = false>
 __global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
   constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2, NWAVES = 4;
@@ -1783,27 +1975,33 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
   if (EPI && a.bias)
     my_bias = llvm_buffer_load_f32(make_rsrc(a.bias + n0, (uint32_t)(a.N - n0) * 4u), (uint32_t)tid * 4u, 0, 0);
 
-  // Byte offset of tile row r's start from its buffer's base (a0 = offset of row 0).
-  auto row_off = [&](uint32_t a0, int r) __attribute__((always_inline)) { return a0 + (uint32_t)r * (uint32_t)K; };
-  // Tile row of unit row u (0..127) of an L (h = 0) or H (h = 1) unit.
-  auto tile_row = [&](int u, int h) __attribute__((always_inline)) { return u + (u >= 64 ? 64 : 0) + 64 * h; };
+  // K^-1 mod 128 (K odd): K K = 1 mod 8, and each Newton step x (2 - K x)
+  // doubles the number of correct low bits (3 -> 6 -> 12).
+  uint32_t kinv = (uint32_t)K;
+  kinv *= 2u - (uint32_t)K * kinv;
+  kinv *= 2u - (uint32_t)K * kinv;
+  // Tile row carried by lane row i of block b of wave half h (a0: ax0 or aw0).
+  auto perm = [&](uint32_t a0, int b, int h, int i) __attribute__((always_inline)) {
+    return (int)((((uint32_t)(16 * (i >> 1) + 2 * b + h) - a0) * kinv) & 127u) + 128 * (i & 1);
+  };
 
   // DMA instruction t of a wave fills unit rows (4t + wave) * 8 .. + 7 of a
-  // line: lane l takes unit row u = (4t + wave) * 8 + l / 8 and LDS position
-  // p = l % 8, i.e. chunk (p - s_u) mod 8 of the row's line; the line's start
-  // (row offset rounded down to 128) sits in the VGPR offset, the line index
-  // times 128 in the SGPR offset.
+  // line: lane l takes unit row u = (4t + wave) * 8 + l / 8 and position p = l %
+  // 8, i.e. window chunk p ^ swz16(u % 16) = line chunk (c + that) mod 8.  The
+  // line's start sits in the VGPR offset, the line index times 128 in the SGPR
+  // offset.
   uint32_t vdx[2][UDPW], vdw[2][UDPW];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int hu = 0; hu < 2; ++hu)
 #pragma unroll
     for (int t = 0; t < UDPW; ++t) {
       const int u = (t * NWAVES + wave) * 8 + (lane >> 3);
-      const int r = tile_row(u, h), tau = (u >> 1) & 7, p = lane & 7;
-      const uint32_t ox = row_off(ax0, r), ow = row_off(aw0, r);
-      const int cx = (p - (tau - (int)((ox & 127u) >> 4))) & 7, cw = (p - (tau - (int)((ow & 127u) >> 4))) & 7;
-      vdx[h][t] = (ox & ~127u) + 16u * (uint32_t)cx;
-      vdw[h][t] = (ow & ~127u) + 16u * (uint32_t)cw;
+      const int h = u >> 6, b = ((u >> 4) & 3) + 4 * hu, i = u & 15;
+      const uint32_t v = (uint32_t)((lane & 7) ^ swz16(i));
+      const uint32_t ox = ax0 + (uint32_t)perm(ax0, b, h, i) * (uint32_t)K;
+      const uint32_t ow = aw0 + (uint32_t)perm(aw0, b, h, i) * (uint32_t)K;
+      vdx[hu][t] = (ox & ~127u) + 16u * ((((ox >> 4) & 7u) + v) & 7u);
+      vdw[hu][t] = (ow & ~127u) + 16u * ((((ow >> 4) & 7u) + v) & 7u);
     }
   auto dma_unit = [&](const v4i &rs, uint32_t unit, const uint32_t (&vo)[UDPW], int j, int t)
       __attribute__((always_inline)) {
@@ -1819,83 +2017,59 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
   };
   auto group_exists = [&](int q, int s) __attribute__((always_inline)) { return exists(q == 3 ? s + 2 : s + 3); };
 
-  // Operand blocks of this lane: block b of a wave tile is unit row (wave half)
-  // * 64 + (b % 4) * 16 + l16 of an L (b < 4) or H unit; ab/ax hold its row's
-  // a_r (w rows for A blocks, x rows for B blocks).
+  // Operand reads.  Read k (0..2) of lane l is window chunk v = 2 g + k of unit
+  // row 64 h + 16 (b mod 4) + l16: LDS offset lp[k] + 2048 (b mod 4) from the
+  // unit of line t, or of line t + 1 where sel[k] is set.
   const int g = lane >> 4, l16 = lane & 15;
-  const int tau_r = (l16 >> 1) & 7;
-  const uint32_t pos0 = (uint32_t)(((tau_r + 2 * g) & 7) << 4), pos1 = (uint32_t)(((tau_r + 2 * g + 1) & 7) << 4),
-                 pos2 = (uint32_t)(((tau_r + 2 * g + 2) & 7) << 4);
-  const uint32_t ra = (uint32_t)(wave_n * 64 + l16) * BK, rb = (uint32_t)(wave_m * 64 + l16) * BK;
-  // Row offsets of the lane's rows: block b's row is tile row (wave half) * 64
-  // (+ 64 past the first 64 unit rows) + (b % 4) * 16 + l16 (+ 64 for H), so its
-  // offset is the lane's base plus a block constant times K.  Only the two
-  // bases stay in registers; each use recomputes a_r (an add and a mask), and
-  // the bases pass through an empty asm once per step so that nothing derived
-  // from them is hoisted out of the K loop (48 addresses would not fit).
-  uint32_t obw = row_off(aw0, tile_row(wave_n * 64 + l16, 0)), obx = row_off(ax0, tile_row(wave_m * 64 + l16, 0));
-  auto a_of = [&](uint32_t base, int b) __attribute__((always_inline)) {
-    return (int)((base + (uint32_t)((b & 3) * 16 + (b >> 2) * 64) * (uint32_t)K) & 127u);
-  };
-  // Reads of one block's window from the units of lines t (S0) and t + 1 (S1):
-  // chunks 0 and 1 into f, chunk 2 into x3.
-  auto read_win = [&](uint32_t S0, uint32_t S1, uint32_t row, int ar, int i, v8i &f, v4i &x3)
+  uint32_t lpx[3], lpw[3], sel[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int v = 2 * g + k;
+    const uint32_t pos = (uint32_t)l16 * BK + (uint32_t)(((v & 7) ^ swz16(l16)) << 4);
+    lpx[k] = (uint32_t)wave_m * 64u * BK + pos;
+    lpw[k] = (uint32_t)wave_n * 64u * BK + pos;
+    sel[k] = (l16 >> 1) + v >= 8 ? ~0u : 0u;
+  }
+  // The three addresses of a window read from units S0 (line t) and S1 (line t + 1).
+  auto win = [&](uint32_t S0, uint32_t S1, const uint32_t (&lp)[3], uint32_t (&at)[3])
       __attribute__((always_inline)) {
-    const int c0 = (ar >> 4) + 2 * g;
-    const uint32_t pos = i == 0 ? pos0 : i == 1 ? pos1 : pos2;
-    const uint32_t at = (c0 + i >= 8 ? S1 : S0) + row + pos;
-    const uint4 v = *(const uint4 *)(smem + at);
-    if (i < 2) {
-      f[4 * i + 0] = (int)v.x; f[4 * i + 1] = (int)v.y; f[4 * i + 2] = (int)v.z; f[4 * i + 3] = (int)v.w;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) at[k] = lp[k] + S0 + (sel[k] & (S1 - S0));
+  };
+  // Read k of block b mod 4 = bl: chunks 0 and 1 into f, chunk 2 into x3.
+  auto read_blk = [&](const uint32_t (&at)[3], int bl, int k, v8i &f, v4i &x3) __attribute__((always_inline)) {
+    const uint4 v = *(const uint4 *)(smem + at[k] + (uint32_t)bl * 16u * BK);
+    if (k < 2) {
+      f[4 * k + 0] = (int)v.x; f[4 * k + 1] = (int)v.y; f[4 * k + 2] = (int)v.z; f[4 * k + 3] = (int)v.w;
     } else {
       x3 = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
     }
   };
-  // Shift the window into place: bytes [ar % 16, ar % 16 + 32) of the 48 read,
-  // in three stages that may run apart (each one MFMA slot): whole dwords move
-  // by 8 bytes, then by 4 bytes (V_PERM_B32 with a per-lane selector picking
-  // its high or its low source dword), then the last 0-3 bytes move by
-  // V_ALIGNBYTE_B32.  The state stays in f and x3 between stages.  With `tail`
-  // (the guarded last steps only) the last stage also clears the bytes at or
-  // past K when t is the last step.
-  constexpr uint32_t kHi = 0x07060504u, kLo = 0x03020100u;  // perm selectors: high or low dword
-  auto rstage = [&](v8i &f, v4i &x3, int ar, int t, int stage, auto tail) __attribute__((always_inline)) {
-    const uint32_t beta = (uint32_t)ar & 15u;
-    if (stage == 0) {
-      const uint32_t s8 = (beta & 8u) ? kHi : kLo;
-      f[0] = (int)__builtin_amdgcn_perm(f[2], f[0], s8); f[1] = (int)__builtin_amdgcn_perm(f[3], f[1], s8);
-      f[2] = (int)__builtin_amdgcn_perm(f[4], f[2], s8); f[3] = (int)__builtin_amdgcn_perm(f[5], f[3], s8);
-      f[4] = (int)__builtin_amdgcn_perm(f[6], f[4], s8); f[5] = (int)__builtin_amdgcn_perm(f[7], f[5], s8);
-      f[6] = (int)__builtin_amdgcn_perm(x3.x, f[6], s8); f[7] = (int)__builtin_amdgcn_perm(x3.y, f[7], s8);
-      x3.x = (int)__builtin_amdgcn_perm(x3.z, x3.x, s8); x3.y = (int)__builtin_amdgcn_perm(x3.w, x3.y, s8);
-    } else if (stage == 1) {
-      const uint32_t s4 = (beta & 4u) ? kHi : kLo;
-      f[0] = (int)__builtin_amdgcn_perm(f[1], f[0], s4); f[1] = (int)__builtin_amdgcn_perm(f[2], f[1], s4);
-      f[2] = (int)__builtin_amdgcn_perm(f[3], f[2], s4); f[3] = (int)__builtin_amdgcn_perm(f[4], f[3], s4);
-      f[4] = (int)__builtin_amdgcn_perm(f[5], f[4], s4); f[5] = (int)__builtin_amdgcn_perm(f[6], f[5], s4);
-      f[6] = (int)__builtin_amdgcn_perm(f[7], f[6], s4); f[7] = (int)__builtin_amdgcn_perm(x3.x, f[7], s4);
-      x3.x = (int)__builtin_amdgcn_perm(x3.y, x3.x, s4);
-    } else if (stage == 2) {
-      const uint32_t sh = beta & 3u;
-      f[0] = (int)__builtin_amdgcn_alignbyte(f[1], f[0], sh); f[1] = (int)__builtin_amdgcn_alignbyte(f[2], f[1], sh);
-      f[2] = (int)__builtin_amdgcn_alignbyte(f[3], f[2], sh); f[3] = (int)__builtin_amdgcn_alignbyte(f[4], f[3], sh);
-      f[4] = (int)__builtin_amdgcn_alignbyte(f[5], f[4], sh); f[5] = (int)__builtin_amdgcn_alignbyte(f[6], f[5], sh);
-      f[6] = (int)__builtin_amdgcn_alignbyte(f[7], f[6], sh); f[7] = (int)__builtin_amdgcn_alignbyte(x3.x, f[7], sh);
-      if (decltype(tail)::value && t == nk - 1) {
-        const int valid = K - t * BK - 32 * g;  // bytes of this lane's 32 that lie before K
+  // Shift block b's window into place: bytes [beta, beta + 32) of the 48 read,
+  // beta = 2 b + h, i.e. registers from b / 2 on and sh[b % 2] = beta mod 4
+  // bytes.  With `tail` (the guarded last steps only) bytes at or past K are
+  // then cleared when t is the last step.
+  const uint32_t shx[2] = {(uint32_t)wave_m, 2u + (uint32_t)wave_m};
+  const uint32_t shw[2] = {(uint32_t)wave_n, 2u + (uint32_t)wave_n};
+  auto realign = [&](v8i &f, const v4i &x3, auto bc, const uint32_t (&sh)[2], int t, auto tail)
+      __attribute__((always_inline)) {
+    constexpr int b = decltype(bc)::value, D = b >> 1;
+    const uint32_t r[12] = {(uint32_t)f[0], (uint32_t)f[1], (uint32_t)f[2], (uint32_t)f[3], (uint32_t)f[4],
+                            (uint32_t)f[5], (uint32_t)f[6], (uint32_t)f[7], (uint32_t)x3.x, (uint32_t)x3.y,
+                            (uint32_t)x3.z, (uint32_t)x3.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int v = valid - 4 * e;
-          const uint32_t m = v >= 4 ? 0xFFFFFFFFu : v <= 0 ? 0u : (1u << (8 * v)) - 1u;
-          f[e] = (int)((uint32_t)f[e] & m);
-        }
+    for (int e = 0; e < 8; ++e) f[e] = (int)__builtin_amdgcn_alignbyte(r[e + D + 1], r[e + D], sh[b & 1]);
+    if (decltype(tail)::value && t == nk - 1) {
+      const int valid = K - t * BK - 32 * g;  // bytes of this lane's 32 that lie before K
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int vb = valid - 4 * e;
+        const uint32_t m = vb >= 4 ? 0xFFFFFFFFu : vb <= 0 ? 0u : (1u << (8 * vb)) - 1u;
+        f[e] = (int)((uint32_t)f[e] & m);
       }
     }
   };
-  auto realign = [&](v8i &f, v4i &x3, int ar, int t, auto tail) __attribute__((always_inline)) {
-#pragma unroll
-    for (int st = 0; st < 3; ++st) rstage(f, x3, ar, t, st, tail);
-  };
+  using I0 = std::integral_constant<int, 0>;
 
   v4f acc[FN][FM];
 #pragma unroll
@@ -1940,13 +2114,18 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
   }
   vm_wait<0>();
   __syncthreads();
+  {
+    uint32_t aw[3], ax[3];
+    win(u_wl(0), u_wl(1), lpw, aw);
+    win(u_xl(0), u_xl(1), lpx, ax);
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      read_win(u_wl(0), u_wl(1), ra + b * 16 * BK, a_of(obw, b), i, A[b], A3[b]);
-      read_win(u_xl(0), u_xl(1), rb + b * 16 * BK, a_of(obx, b), i, B[b], B3[b]);
-    }
+      for (int k = 0; k < 3; ++k) {
+        read_blk(aw, b, k, A[b], A3[b]);
+        read_blk(ax, b, k, B[b], B3[b]);
+      }
+  }
   __syncthreads();  // the windows are read: w L 0 and x L 0 are retired
 #pragma unroll
   for (int q = 1; q <= 4; ++q)
@@ -1955,65 +2134,72 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
       for (int t = 0; t < UDPW; ++t) issue(q, -1, t);
     }
   // B[1..3] are realigned in step 0's first quadrant, as in every step.
-#pragma unroll
-  for (int b = 0; b < 4; ++b) realign(A[b], A3[b], a_of(obw, b), 0, std::true_type{});
-  realign(B[0], B3[0], a_of(obx, 0), 0, std::true_type{});
+  static_for<4>([&](auto bc) __attribute__((always_inline)) {
+    realign(A[decltype(bc)::value], A3[decltype(bc)::value], bc, shw, 0, std::true_type{});
+  });
+  realign(B[0], B3[0], I0{}, shx, 0, std::true_type{});
 
   // Step s.  STEADY: every DMA group and read of the schedule exists (s + 3 <=
   // nk), so the body has no branches; the last steps take the guarded body.
   // Reads go out with MFMAs 0-11 of their quadrant (three per block), DMAs with
-  // MFMAs 1, 5, 9, 13.  A block's realignment runs in its three stages with the
-  // three MFMAs that start four MFMAs before its first use: its reads went out
-  // at least a quadrant earlier, or (the first block read in a quadrant) ten
-  // MFMAs earlier.
+  // MFMAs 1, 5, 9, 13.  A block is realigned four MFMAs before its first use:
+  // its reads went out at least a quadrant earlier, or (the first block read in
+  // a quadrant) twelve MFMAs earlier.
   auto step = [&](const int s, auto steady) __attribute__((always_inline)) {
     constexpr bool STEADY = decltype(steady)::value;
     using TAILC = std::integral_constant<bool, !STEADY>;
     const bool next = STEADY || s + 1 < nk;  // the windows of step s + 1 exist
-    asm volatile("" : "+v"(obw), "+v"(obx));
+    uint32_t at[3];
     // ---- Q1: w L x x L; read x H (s) into B[4..7]; realign B[1..4]
+    win(u_xh(s), u_xh(s + 1), lpx, at);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int mb = q >> 2, nb = q & 3;
+    static_for<16>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value, mb = q >> 2, nb = q & 3;
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
-      if ((q & 3) < 3) rstage(B[1 + (q >> 2)], B3[1 + (q >> 2)], a_of(obx, 1 + (q >> 2)), s, q & 3, TAILC{});
-      if (q < 12) read_win(u_xh(s), u_xh(s + 1), rb + (q / 3) * 16 * BK, a_of(obx, 4 + q / 3), q % 3, B[4 + q / 3], B3[4 + q / 3]);
+      if constexpr ((q & 3) == 0)
+        realign(B[1 + mb], B3[1 + mb], std::integral_constant<int, 1 + mb>{}, shx, s, TAILC{});
+      if constexpr (q < 12) read_blk(at, q / 3, q % 3, B[4 + q / 3], B3[4 + q / 3]);
       if ((q & 3) == 1 && (STEADY || group_exists(1, s))) issue(1, s, q >> 2);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      __builtin_amdgcn_sched_barrier(0);  // keep the spread as written
+    });
     // B1: publishes w H line s + 1; groups issued after it: w L s + 2, x L s + 3
     if (STEADY) vm_wait<2 * UDPW>();
     else wait_groups((int)group_exists(4, s - 1) + (int)group_exists(1, s));
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
     // ---- Q2: w L x x H; read w H (s) into A[4..7]; realign B[5..7], A[4]
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int mb = 4 + (q >> 2), nb = q & 3;
+    win(u_wh(s), u_wh(s + 1), lpw, at);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<16>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value, mb = 4 + (q >> 2), nb = q & 3;
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
-      if (q < 12 && (q & 3) < 3) rstage(B[5 + (q >> 2)], B3[5 + (q >> 2)], a_of(obx, 5 + (q >> 2)), s, q & 3, TAILC{});
-      if (q >= 12 && (q & 3) < 3) rstage(A[4], A3[4], a_of(obw, 4), s, q & 3, TAILC{});
-      if (q < 12) read_win(u_wh(s), u_wh(s + 1), ra + (q / 3) * 16 * BK, a_of(obw, 4 + q / 3), q % 3, A[4 + q / 3], A3[4 + q / 3]);
+      if constexpr (q < 12 && (q & 3) == 0)
+        realign(B[mb + 1], B3[mb + 1], std::integral_constant<int, mb + 1>{}, shx, s, TAILC{});
+      if constexpr (q == 12) realign(A[4], A3[4], std::integral_constant<int, 4>{}, shw, s, TAILC{});
+      if constexpr (q < 12) read_blk(at, q / 3, q % 3, A[4 + q / 3], A3[4 + q / 3]);
       if ((q & 3) == 1 && (STEADY || group_exists(2, s))) issue(2, s, q >> 2);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     // B2: publishes w L line s + 2; after it: x L s + 3, x H s + 3
     if (STEADY) vm_wait<2 * UDPW>();
     else wait_groups((int)group_exists(1, s) + (int)group_exists(2, s));
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
     // ---- Q3: w H x x L; read w L (s + 1) into A[0..3]; realign A[5..7], A[0]
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int nb = 4 + (q >> 2), mb = q & 3;
+    win(u_wl(s + 1), u_wl(s + 2), lpw, at);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<16>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value, nb = 4 + (q >> 2), mb = q & 3;
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
-      if (q < 12 && (q & 3) < 3) rstage(A[5 + (q >> 2)], A3[5 + (q >> 2)], a_of(obw, 5 + (q >> 2)), s, q & 3, TAILC{});
-      if (next && q >= 12 && (q & 3) < 3) rstage(A[0], A3[0], a_of(obw, 0), s + 1, q & 3, TAILC{});
-      if (next && q < 12) read_win(u_wl(s + 1), u_wl(s + 2), ra + (q / 3) * 16 * BK, a_of(obw, q / 3), q % 3, A[q / 3], A3[q / 3]);
+      if constexpr (q < 12 && (q & 3) == 0)
+        realign(A[nb + 1], A3[nb + 1], std::integral_constant<int, nb + 1>{}, shw, s, TAILC{});
+      if constexpr (q == 12) {
+        if (next) realign(A[0], A3[0], I0{}, shw, s + 1, TAILC{});
+      }
+      if constexpr (q < 12) {
+        if (next) read_blk(at, q / 3, q % 3, A[q / 3], A3[q / 3]);
+      }
       if ((q & 3) == 1 && (STEADY || group_exists(3, s))) issue(3, s, q >> 2);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     // B3: publishes x L line s + 2; after it: x H s + 2, w H s + 1, w L s + 2,
     // x L s + 3, x H s + 3, w H s + 2
     if (STEADY) vm_wait<6 * UDPW>();
@@ -2021,18 +2207,24 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
       wait_groups((int)group_exists(2, s - 1) + (int)group_exists(3, s - 1) + (int)group_exists(4, s - 1) +
                   (int)group_exists(1, s) + (int)group_exists(2, s) + (int)group_exists(3, s));
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
     // ---- Q4: w H x x H; read x L (s + 1) into B[0..3]; realign A[1..3], B[0]
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int nb = 4 + (q >> 2), mb = 4 + (q & 3);
+    win(u_xl(s + 1), u_xl(s + 2), lpx, at);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<16>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value, nb = 4 + (q >> 2), mb = 4 + (q & 3);
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
-      if (next && q < 12 && (q & 3) < 3) rstage(A[1 + (q >> 2)], A3[1 + (q >> 2)], a_of(obw, 1 + (q >> 2)), s + 1, q & 3, TAILC{});
-      if (next && q >= 12 && (q & 3) < 3) rstage(B[0], B3[0], a_of(obx, 0), s + 1, q & 3, TAILC{});
-      if (next && q < 12) read_win(u_xl(s + 1), u_xl(s + 2), rb + (q / 3) * 16 * BK, a_of(obx, q / 3), q % 3, B[q / 3], B3[q / 3]);
+      if constexpr (q < 12 && (q & 3) == 0) {
+        if (next) realign(A[1 + (q >> 2)], A3[1 + (q >> 2)], std::integral_constant<int, 1 + (q >> 2)>{}, shw, s + 1, TAILC{});
+      }
+      if constexpr (q == 12) {
+        if (next) realign(B[0], B3[0], I0{}, shx, s + 1, TAILC{});
+      }
+      if constexpr (q < 12) {
+        if (next) read_blk(at, q / 3, q % 3, B[q / 3], B3[q / 3]);
+      }
       if ((q & 3) == 1 && (STEADY || group_exists(4, s))) issue(4, s, q >> 2);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     // B4: publishes x H line s + 2; after it: w H s + 1, w L s + 2, and the four
     // groups of this step
     if (STEADY) vm_wait<6 * UDPW>();
@@ -2052,7 +2244,17 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
   __syncthreads();
   s_lds[tid] = my_scale;
   if constexpr (EPI) b_lds[tid] = my_bias;
-  main_epilogue16<BM, BN, WM, WN, EPI>(acc, a, smem, s_lds, b_lds, m0, n0, wave, lane, tid);
+  // rows of this lane (l16 of each x block) and its column pairs (lane rows 4 g
+  // and 4 g + 2 of each w block; 4 g + 1 and 4 g + 3 are those plus 128)
+  int mrow[FM], pa[FN], pb[FN];
+#pragma unroll
+  for (int mb = 0; mb < FM; ++mb) mrow[mb] = perm(ax0, mb, wave_m, l16);
+#pragma unroll
+  for (int nb = 0; nb < FN; ++nb) {
+    pa[nb] = perm(aw0, nb, wave_n, 4 * g);
+    pb[nb] = perm(aw0, nb, wave_n, 4 * g + 2);
+  }
+  main_epilogue_perm<EPI>(acc, a, smem, s_lds, b_lds, m0, n0, mrow, pa, pb, tid);
 }
 
 // ------------------------------------------------------- launch templates

@@ -163,18 +163,20 @@ def test_plan_odd_k_reads_rows_in_place():
 
 def test_plan_main_kernel_choice():
     """256 x 256 tiles without a K tail run on the one-wave-per-SIMD kernel
-    (variant 19); with a K tail on the eight-wave kernel (variant 10)."""
+    (variant 19); odd K on its whole-line form (variant 20) where M K and N K
+    are multiples of 16; other K tails on the eight-wave kernel (variant 10)."""
     assert fg.fp8_gemm_plan(8192, 8192, 8192)["variant"] == 19
     assert fg.fp8_gemm_plan(4096, 4096, 4096)["variant"] == 19      # 256 tiles
     odd = fg.fp8_gemm_plan(4096, 4096, 4127)                           # rows read in place
-    assert odd["variant"] == 10 and odd["k_tail"] == 1
-    # the whole-line variant (opt-in) needs M K and N K multiples of 16
+    assert odd["variant"] == 20 and odd["k_tail"] == 1 and odd["workspace_bytes"] == 0
+    assert fg.fp8_gemm_plan(4104, 4096, 4127)["variant"] == 10         # M K not a multiple of 16
+    assert fg.fp8_gemm_plan(4096, 4096, 4128)["variant"] == 10         # even K
+    # the whole-line variant (opt-in) needs odd K and M K, N K multiples of 16
     assert fg.fp8_gemm_plan_ex(4096, 4096, 4127, fg.PATH_MAIN, 20, 0)["variant"] == 20
-    assert fg.fp8_gemm_plan_ex(4096, 4104, 4128, fg.PATH_MAIN, 20, 0)["variant"] == 20
-    with pytest.raises(fg.Fp8gError):
-        fg.fp8_gemm_plan_ex(4097, 4096, 4127, fg.PATH_MAIN, 20, 0)
-    with pytest.raises(fg.Fp8gError):
-        fg.fp8_gemm_plan_ex(4096, 4104, 4127, fg.PATH_MAIN, 20, 0)
+    assert fg.fp8_gemm_plan_ex(48, 560, 3001, fg.PATH_MAIN, 20, 0)["variant"] == 20
+    for shape in [(4097, 4096, 4127), (4096, 4104, 4127), (4096, 4104, 4128), (256, 256, 1000), (256, 256, 4096)]:
+        with pytest.raises(fg.Fp8gError):
+            fg.fp8_gemm_plan_ex(*shape, fg.PATH_MAIN, 20, 0)
     assert fg.fp8_gemm_plan(3072, 3072, 3072)["variant"] == 19      # 144 tiles
     forced = fg.fp8_gemm_plan_ex(300, 300, 384, fg.PATH_MAIN, 19, 0)
     assert forced["variant"] == 19 and forced["grid"] == 4 and forced["tile_k"] == 128

@@ -74,7 +74,7 @@ def test_main_variants_all_formats(variant, fmts):
 @pytest.mark.parametrize("fmts", FORMATS, ids=lambda f: f"x{f[0]}w{f[1]}")
 def test_main_cache_line_rows_all_formats(fmts):
     _case(272, 528, 257, fg.ACT_GELU_TANH, *fmts, path=fg.PATH_MAIN, variant=20)
-    _case(256, 80, 1000, fg.ACT_SILU, *fmts, path=fg.PATH_MAIN, variant=20)
+    _case(256, 80, 1001, fg.ACT_SILU, *fmts, path=fg.PATH_MAIN, variant=20)
     _case(256, 256, 4127, fg.ACT_RELU, *fmts, path=fg.PATH_MAIN, variant=20)
 
 
