@@ -68,7 +68,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "fp8_gemm_channel_amd", "csrc", f)
                   for f in ("fp8g_kernels.hpp", "fp8g_launch_main4w.hip")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_main4w_kernel_square-8192_traffic.md")
 TRACE_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_5shape_bench_kernel_trace.md")
-MAIN_KERNEL_NAMES = {10: "fp8g_main5_kernel", 16: "fp8g_main5_kernel", 19: "fp8g_main4w_kernel"}
+MAIN_KERNEL_NAMES = {10: "fp8g_main5_kernel", 16: "fp8g_main5_kernel", 19: "fp8g_main4w_kernel",
+                     20: "fp8g_main4wr_kernel"}
 
 
 def kernel_source_hash() -> str:
@@ -204,6 +205,10 @@ def main() -> int:
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (3 times); used to "
                          "calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE against a kernel of known traffic")
+    ap.add_argument("--read-bytes", type=int, default=0,
+                    help="only sum a float32 buffer of this many bytes (cold, 5 times): one launch that "
+                         "reads that much from HBM and writes almost nothing, the reference rate for a "
+                         "memory-bound shape of the same size")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -228,6 +233,23 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 3}), flush=True)
+        return 0
+
+    if args.read_bytes:
+        src = torch.ones(args.read_bytes // 4, dtype=torch.float32, device=dev)  # sums stay exact below 2^24
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t = []
+        for i in range(5):
+            flush.fill_(i)
+            e0.record(stream)
+            total = src.sum()
+            e1.record(stream)
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e3)
+        assert float(total) == float(args.read_bytes // 4)
+        print(json.dumps({"read_bytes": args.read_bytes, "launches": 5, "marker_median_us": float(np.median(t))}),
+              flush=True)
         return 0
 
     workloads = [w for w in synth.WORKLOADS if not args.only or w.name in args.only.split(",")]

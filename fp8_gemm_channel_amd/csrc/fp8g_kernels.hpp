@@ -2059,6 +2059,13 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
                             (uint32_t)x3.z, (uint32_t)x3.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = (int)__builtin_amdgcn_alignbyte(r[e + D + 1], r[e + D], sh[b & 1]);
+    // The dwords the shift does not use are consumed here, so the compiler keeps
+    // every read at 16 bytes: narrower reads are serviced for more lanes at once,
+    // and the four K groups of a block then collide on the same banks (measured:
+    // 20x the bank-conflict cycles of whole-chunk reads).
+#pragma unroll
+    for (int i = 0; i < 12; ++i)
+      if (i < D || i > D + 8) asm volatile("" : : "v"(r[i]));
     if (decltype(tail)::value && t == nk - 1) {
       const int valid = K - t * BK - 32 * g;  // bytes of this lane's 32 that lie before K
 #pragma unroll
