@@ -6,13 +6,17 @@ Tolerance (per element, both sides widened to double):
 For stress inputs whose dot products cancel heavily (outside the five seeded
 benchmark shapes) a tolerance relative to |y| cannot be met by any fp32
 accumulation, in any order, so those tests add the conditioning term
-    COND_GAMMA * scale[n] * sum_k |x[m,k] * w[n,k]|
-with COND_GAMMA = 2^-12.  Two roundings make up the bound: the gfx950 fp8
-MFMA does not add the products of one instruction in exact fp32 (measured:
-errors up to about 2^-15 .. 2^-13 of the largest product in the instruction's
-K block, which is at most that block's sum |x w|), and fp32 accumulation across
-blocks adds about 2^-24 * sqrt(K/64) relative.  N(0,1) inputs show about 2^-20
-of sum |x w|; uniformly random codes (2^-9 .. 448) about 2^-15.
+    gamma * scale[n] * sum_k |x[m,k] * w[n,k]|.
+Two roundings make up the error: the gfx950 fp8 MFMA does not add the products
+of one instruction in exact fp32 (measured: errors up to about 2^-15 .. 2^-13
+of the largest product in the instruction's K block, which is at most that
+block's sum |x w|), and fp32 accumulation across blocks adds about
+2^-24 * sqrt(K/64) relative.  Measured on MI355X, the error beyond the base
+bound as a fraction of scale[n] * sum_k |x w|: inputs drawn N(0, sigma^2), then
+quantised, up to 2^-18.8 (sigma = 100, K = 129; 2^-20 .. 2^-21 at K = 4096 and
+4127), so those tests take gamma = COND_GAMMA_GAUSS = 2^-16; uniformly random
+codes (2^-9 .. 448), whose large products sit beside tiny ones in one MFMA
+block, up to 2^-15.0, so they take gamma = COND_GAMMA_CODES = 2^-12.
 """
 from __future__ import annotations
 
@@ -26,7 +30,8 @@ import oracle
 
 ATOL = 1e-2
 RTOL = 1e-2
-COND_GAMMA = 2.0 ** -12
+COND_GAMMA_GAUSS = 2.0 ** -16  # 7x the measured worst case of N(0, sigma^2) draws
+COND_GAMMA_CODES = 2.0 ** -12  # 8x the measured worst case of uniformly random codes
 
 
 def conditioning(x: np.ndarray, w: np.ndarray, scale: np.ndarray) -> np.ndarray:
@@ -60,9 +65,10 @@ def run(x: np.ndarray, w: np.ndarray, scale: np.ndarray, *, path=0, variant=0, s
     return out.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def compare(got: np.ndarray, ref: np.ndarray, what: str = "", cond: np.ndarray | None = None) -> dict:
+def compare(got: np.ndarray, ref: np.ndarray, what: str = "", cond: np.ndarray | None = None,
+            gamma: float = COND_GAMMA_GAUSS) -> dict:
     """Assert the tolerance on every element; return diagnostics.  `cond`
-    (same shape) adds COND_GAMMA * cond to the bound (stress inputs only)."""
+    (same shape) adds gamma * cond to the bound (stress inputs only)."""
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
     g = oracle.bf16_bits_to_double(got)
     r = oracle.bf16_bits_to_double(ref)
@@ -72,7 +78,7 @@ def compare(got: np.ndarray, ref: np.ndarray, what: str = "", cond: np.ndarray |
     err = np.abs(g[ok] - r[ok])
     bound = ATOL + RTOL * np.abs(r[ok])
     if cond is not None:
-        bound = bound + COND_GAMMA * cond[ok]
+        bound = bound + gamma * cond[ok]
     bad = err > bound
     if bad.any():
         idx = np.argmax(err - bound)
@@ -84,4 +90,15 @@ def compare(got: np.ndarray, ref: np.ndarray, what: str = "", cond: np.ndarray |
     exact = float(np.mean(gi == ri)) if gi.size else 1.0
     same_sign = (gi >> 15) == (ri >> 15)
     ulp = int(np.max(np.abs(gi - ri)[same_sign])) if same_sign.any() else 0
-    return {"exact": exact, "max_ulp": ulp, "max_err": float(err.max()) if err.size else 0.0}
+    out = {"exact": exact, "max_ulp": ulp, "max_err": float(err.max()) if err.size else 0.0}
+    if cond is not None and err.size:
+        # the error beyond the base bound as a fraction of the conditioning term
+        # (log2): what gamma has to cover, for the record
+        c = cond[ok]
+        excess = err - (ATOL + RTOL * np.abs(r[ok]))
+        sel = (excess > 0) & (c > 0)
+        ratio = float(np.max(excess[sel] / c[sel])) if sel.any() else 0.0
+        out["log2_excess_over_cond"] = float(np.log2(ratio)) if ratio > 0 else float("-inf")
+        say(f"{what}: error beyond the base bound / (scale sum|x w|) = 2^{out['log2_excess_over_cond']:.1f} "
+            f"({int(sel.sum())} elements beyond the base bound)")
+    return out

@@ -15,7 +15,7 @@ import torch
 import fp8_gemm_channel_amd as fg
 import oracle
 import synth
-from tests.gpu_util import compare, conditioning, run, say, to_dev
+from tests.gpu_util import COND_GAMMA_CODES, compare, conditioning, run, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -81,7 +81,7 @@ def test_all_codes_random_including_nan():
     s = np.full(N, 0.01, np.float32)
     say("nan propagation")
     cond = conditioning(x, w, s)
-    compare(run(x, w, s), oracle.gemm_scaled(x, w, s), "nan", cond=np.nan_to_num(cond))
+    compare(run(x, w, s), oracle.gemm_scaled(x, w, s), "nan", cond=np.nan_to_num(cond), gamma=COND_GAMMA_CODES)
 
 
 def _call_live(xd, wd, sd, out):
