@@ -1486,38 +1486,28 @@ __device__ __forceinline__ void main_epilogue16(const v4f (&acc)[BN / WN / 16][B
 // The bf16 tile is staged as column pairs: dword p (0..127) of row r holds
 // columns p (low half) and p + 128 (high half), so each element pair is one
 // 4-byte write.  Row pitch 512 bytes; pair chunk c = p / 4 of row r at position c
-// ^ pswz(r), pswz(r) = ((r / 16) ^ r) mod 16; dword j of a chunk at j ^ ((c / 8)
-// mod 4).  One write instruction stores one pair p_g per lane group g (the four
-// agree mod 32 and differ in p / 32: four dword positions) for sixteen rows
-// (which agree mod 16 and differ in r / 16: sixteen chunk positions), so the 64
-// lanes write 64 different banks.
+// ^ pswz(r), pswz(r) = ((r / 16) ^ r) mod 16.  One write instruction stores one
+// pair p_g per lane group g for sixteen rows that agree mod 16 and differ in r /
+// 16 (sixteen chunk positions); the four p_g agree mod 32, so two of the groups
+// share a bank (2-way conflicts, in exchange for whole-line stores below).
 __device__ __forceinline__ int pswz(int r) { return ((r >> 4) ^ r) & 15; }
 
 // Writes the 256 x 256 bf16 tile staged by main_epilogue_perm_t to y (256
-// threads).  Pass q (0..15) takes column group G = 4 (q % 4) + t % 4 of row 64 (q
-// / 4) + t / 4 (thread t): pair chunks 2G and 2G + 1, i.e. columns 8 G .. 8 G + 7
-// (low halves) and 128 + 8 G .. (high halves), one 16-byte store each.  Within a
-// pass the chunks' dword order is fixed ((2G / 8) mod 4 = q mod 4), four lanes
-// store 64 contiguous bytes of a row, and the sixteen rows a wave reads have
-// different pswz (no bank conflicts).
+// threads).  Pass q (0..15) takes column group G = 8 (q % 2) + t % 8 of row 32 (q
+// / 2) + t / 8 (thread t): pair chunks 2G and 2G + 1, i.e. columns 8 G .. 8 G + 7
+// (low halves) and 128 + 8 G .. (high halves), one 16-byte store each, so eight
+// lanes store one whole 128-byte line of a row; the two rows a 16-lane group
+// reads differ in pswz's low bit, so its reads hit sixteen chunk positions.
 __device__ __forceinline__ void store_tile_pairs(const MainArgs &a, const uint8_t *smem, int m0, int n0, int tid) {
   constexpr int PITCH = 512;
-  // columns 8 G .. + 7 (lo) and 128 + 8 G .. + 7 (hi) of row r for pass q
-  auto fetch = [&](int q, int r, int G, v4i &lo, v4i &hi) __attribute__((always_inline)) {
-    v4i d[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = 2 * G + h;
-      const v4i v = *(const v4i *)(smem + r * PITCH + ((c ^ pswz(r)) << 4));
-      switch (q & 3) {  // pair 4 c + j is stored at dword j ^ (q % 4)
-        case 0: d[h] = v; break;
-        case 1: d[h] = v4i{v[1], v[0], v[3], v[2]}; break;
-        case 2: d[h] = v4i{v[2], v[3], v[0], v[1]}; break;
-        default: d[h] = v4i{v[3], v[2], v[1], v[0]}; break;
-      }
-    }
-    const uint32_t p[8] = {(uint32_t)d[0][0], (uint32_t)d[0][1], (uint32_t)d[0][2], (uint32_t)d[0][3],
-                           (uint32_t)d[1][0], (uint32_t)d[1][1], (uint32_t)d[1][2], (uint32_t)d[1][3]};
+  auto grp = [&](int q) __attribute__((always_inline)) { return 8 * (q & 1) + (tid & 7); };
+  auto row = [&](int q) __attribute__((always_inline)) { return 32 * (q >> 1) + (tid >> 3); };
+  // columns 8 G .. + 7 (lo) and 128 + 8 G .. + 7 (hi) of row r
+  auto fetch = [&](int r, int G, v4i &lo, v4i &hi) __attribute__((always_inline)) {
+    const v4i d0 = *(const v4i *)(smem + r * PITCH + (((2 * G) ^ pswz(r)) << 4));
+    const v4i d1 = *(const v4i *)(smem + r * PITCH + (((2 * G + 1) ^ pswz(r)) << 4));
+    const uint32_t p[8] = {(uint32_t)d0[0], (uint32_t)d0[1], (uint32_t)d0[2], (uint32_t)d0[3],
+                           (uint32_t)d1[0], (uint32_t)d1[1], (uint32_t)d1[2], (uint32_t)d1[3]};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       lo[k] = (int)__builtin_amdgcn_perm(p[2 * k + 1], p[2 * k], 0x05040100u);  // low halves
@@ -1529,34 +1519,29 @@ __device__ __forceinline__ void store_tile_pairs(const MainArgs &a, const uint8_
     for (int q0 = 0; q0 < 16; q0 += 4) {
       v4i lo[4], hi[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int q = q0 + b;
-        fetch(q, 64 * (q >> 2) + (tid >> 2), 4 * (q & 3) + (tid & 3), lo[b], hi[b]);
-      }
+      for (int b = 0; b < 4; ++b) fetch(row(q0 + b), grp(q0 + b), lo[b], hi[b]);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int q = q0 + b, r = 64 * (q >> 2) + (tid >> 2), G = 4 * (q & 3) + (tid & 3);
-        uint16_t *row = a.y + (size_t)(m0 + r) * a.N + n0;
-        __builtin_nontemporal_store(lo[b], (v4i *)(row + 8 * G));
-        __builtin_nontemporal_store(hi[b], (v4i *)(row + 128 + 8 * G));
+        uint16_t *yr = a.y + (size_t)(m0 + row(q0 + b)) * a.N + n0;
+        __builtin_nontemporal_store(lo[b], (v4i *)(yr + 8 * grp(q0 + b)));
+        __builtin_nontemporal_store(hi[b], (v4i *)(yr + 128 + 8 * grp(q0 + b)));
       }
     }
     return;
   }
-#pragma unroll 4
   for (int q = 0; q < 16; ++q) {
-    const int r = 64 * (q >> 2) + (tid >> 2), G = 4 * (q & 3) + (tid & 3);
+    const int r = row(q), G = grp(q);
     const int m = m0 + r;
     if (m >= a.M || n0 + 8 * G >= a.N) continue;
     v4i lo, hi;
-    fetch(q, r, G, lo, hi);
-    uint16_t *row = a.y + (size_t)m * a.N + n0;
+    fetch(r, G, lo, hi);
+    uint16_t *yr = a.y + (size_t)m * a.N + n0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int n = n0 + 128 * h + 8 * G;
       if (n >= a.N) continue;
       const v4i v = h ? hi : lo;
-      uint16_t *dst = row + 128 * h + 8 * G;
+      uint16_t *dst = yr + 128 * h + 8 * G;
       if (a.ystore == 16) {  // N % 8 == 0 and y 16-byte aligned: the chunk is whole
         __builtin_nontemporal_store(v, (v4i *)dst);
       } else if (a.ystore == 8) {  // N % 4 == 0 and y 8-byte aligned
@@ -1590,9 +1575,7 @@ __device__ __forceinline__ void main_epilogue_perm_t(const v4f (&acc)[8][8], con
     return activation<ACT>(z);
   };
   // byte offset of pair p within its row, before the row's chunk swizzle
-  auto at = [](int p) __attribute__((always_inline)) {
-    return ((uint32_t)(p >> 2) << 4) | ((uint32_t)((p & 3) ^ ((p >> 5) & 3)) << 2);
-  };
+  auto at = [](int p) __attribute__((always_inline)) { return (uint32_t)p << 2; };
   // Every scale (and bias) this lane needs is read before the first write: LDS
   // operations complete in order, so a read behind writes waits for all of them.
   float sc[8][4], bi[8][4];
