@@ -209,6 +209,9 @@ def main() -> int:
                     help="only sum a float32 buffer of this many bytes (cold, 5 times): one launch that "
                          "reads that much from HBM and writes almost nothing, the reference rate for a "
                          "memory-bound shape of the same size")
+    ap.add_argument("--shape", default="",
+                    help="only time the default plan on one M,N,K (cold, events on the kernel, 20 calls): "
+                         "e.g. the decode weight stream at M=1 beside M=32")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -249,6 +252,28 @@ def main() -> int:
             t.append(e0.elapsed_time(e1) * 1e3)
         assert float(total) == float(args.read_bytes // 4)
         print(json.dumps({"read_bytes": args.read_bytes, "launches": 5, "marker_median_us": float(np.median(t))}),
+              flush=True)
+        return 0
+
+    if args.shape:
+        M, N, K = (int(v) for v in args.shape.split(","))
+        x, w, s = synth.fp8_inputs(M, N, K, seed=42)
+        xd, wd, sd = (torch.from_numpy(a).to(dev) for a in (x, w, s))
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t = []
+        for i in range(20):
+            flush.fill_(i)
+            fg.fp8_gemm(xd, wd, sd, out=y, events=(e0, e1))
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e3)
+        plan = fg.fp8_gemm_plan(M, N, K)
+        nbytes = M * K + N * K + 4 * N + 2 * M * N
+        med = float(np.median(t[2:]))
+        print(json.dumps({"shape": [M, N, K], "plan": {k: plan[k] for k in ("path_name", "variant", "split_k", "grid")},
+                          "calls": 20, "median_us": round(med, 2), "algorithmic_bytes": nbytes,
+                          "GB_per_s": round(nbytes / med / 1e3, 1), "TFLOP_per_s": round(2 * M * N * K / med / 1e6, 1)}),
               flush=True)
         return 0
 
