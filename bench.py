@@ -194,6 +194,64 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+STREAM_MODES = {0: "LDS-DMA, decode pattern (48 rows x 8 waves, 2 slots a wave)",
+                1: "LDS-DMA, 24 rows x 8 waves, 3 slots a wave (512 workgroups)",
+                2: "16-byte loads into registers (1024 x 256 threads, 8 in flight)"}
+
+
+def stream_reference(spec: str, fg, synth, torch, dev, stream) -> int:
+    """bench.py --stream N,K: the default plan at M = 32 and the reference
+    streams of libfp8g_stream.so over the same N x K weight, interleaved, cold
+    (512 MiB rewritten before every call), events attached to each kernel.
+    Each stream's XOR checksum is checked against the weight's."""
+    import ctypes
+
+    N, K = (int(v) for v in spec.split(","))
+    path = os.path.join(ROOT, "fp8_gemm_channel_amd", "libfp8g_stream.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: python fp8_gemm_channel_amd/build.py --stream")
+    lib = ctypes.CDLL(path)
+    lib.fp8g_stream_out_words.restype = ctypes.c_longlong
+    lib.fp8g_stream_out_words.argtypes = [ctypes.c_int] * 3
+    lib.fp8g_stream_launch.restype = ctypes.c_int
+    lib.fp8g_stream_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
+    M = 32
+    x, w, s = synth.fp8_inputs(M, N, K, seed=42)
+    xd, wd, sd = (torch.from_numpy(a).to(dev) for a in (x, w, s))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    want = int(np.bitwise_xor.reduce(np.ascontiguousarray(w).view(np.uint32), axis=None))
+    outs = {m: torch.empty(int(lib.fp8g_stream_out_words(m, N, K)), dtype=torch.int32, device=dev) for m in STREAM_MODES}
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream), e1.record(stream)
+    torch.cuda.synchronize()
+    t = {k: [] for k in ["gemm"] + list(STREAM_MODES)}
+    for i in range(20):
+        for k in t:
+            flush.fill_(i)
+            if k == "gemm":
+                fg.fp8_gemm(xd, wd, sd, out=y, events=(e0, e1))
+            else:
+                rc = lib.fp8g_stream_launch(k, wd.data_ptr(), N, K, outs[k].data_ptr(), stream.cuda_stream,
+                                            e0.cuda_event, e1.cuda_event)
+                if rc != 0:
+                    raise RuntimeError(f"fp8g_stream_launch(mode {k}) returned {rc}")
+            e1.synchronize()
+            t[k].append(e0.elapsed_time(e1) * 1e3)
+    for k in STREAM_MODES:
+        got = int(np.bitwise_xor.reduce(outs[k].cpu().numpy().view(np.uint32), axis=None))
+        if got != want:
+            raise RuntimeError(f"stream mode {k}: checksum {got:#x}, weight {want:#x}")
+    wbytes = N * K
+    plan = fg.fp8_gemm_plan(M, N, K)
+    for k, v in t.items():
+        med = float(np.median(v[2:]))
+        name = f"default plan, M={M} (variant {plan['variant']})" if k == "gemm" else STREAM_MODES[k]
+        print(json.dumps({"stream": k, "what": name, "N": N, "K": K, "calls": 20, "median_us": round(med, 2),
+                          "weight_bytes": wbytes, "TB_per_s": round(wbytes / med / 1e6, 3)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +270,10 @@ def main() -> int:
     ap.add_argument("--shape", default="",
                     help="only time the default plan on one M,N,K (cold, events on the kernel, 20 calls): "
                          "e.g. the decode weight stream at M=1 beside M=32")
+    ap.add_argument("--stream", default="",
+                    help="only time, on one N,K weight (cold, events on the kernel, 20 rounds interleaved), the "
+                         "default plan at M=32 beside the reference streams of libfp8g_stream.so that read the "
+                         "same bytes and compute nothing: e.g. 12288,4096 for the decode weight")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -254,6 +316,9 @@ def main() -> int:
         print(json.dumps({"read_bytes": args.read_bytes, "launches": 5, "marker_median_us": float(np.median(t))}),
               flush=True)
         return 0
+
+    if args.stream:
+        return stream_reference(args.stream, fg, synth, torch, dev, stream)
 
     if args.shape:
         M, N, K = (int(v) for v in args.shape.split(","))

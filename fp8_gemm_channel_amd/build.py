@@ -7,6 +7,10 @@ LDS-DMA is preceded by a NaN fill of its destination (FP8G_LDS_POISON), so a
 read that runs ahead of its DMA shows up as NaN outputs.  Load it by setting
 FP8G_LIBRARY to its path before importing the package.
 
+--stream builds libfp8g_stream.so instead: the reference HBM streams that
+bench.py --stream times beside the memory-bound shapes (csrc/fp8g_stream.hip;
+no part of the GEMM interface).
+
 (run as a file: importing the package loads the library this builds)
 
 hipcc cross-compiles the device code for gfx950 without a GPU present.
@@ -22,6 +26,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libfp8g.so")
 POISON_LIBRARY = os.path.join(PKG, "libfp8g_lds_poison.so")
+STREAM_LIBRARY = os.path.join(PKG, "libfp8g_stream.so")
+STREAM_SOURCE = os.path.join(CSRC, "fp8g_stream.hip")
 SOURCES = [os.path.join(CSRC, f) for f in ("fp8g_api.cpp", "fp8g_kernels.hip", "fp8g_noalloc.hip")] + sorted(
     os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.startswith("fp8g_launch_") and f.endswith(".hip"))
 
@@ -82,5 +88,29 @@ def build(verbose: bool = False, jobs: int = 0, lds_poison: bool = False) -> str
     return target
 
 
+def build_stream(verbose: bool = False) -> str:
+    """Compile and link libfp8g_stream.so (the reference streams) in-tree."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = STREAM_LIBRARY + ".tmp%d" % os.getpid()
+    cmd = [hipcc, *HIPCC_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, STREAM_SOURCE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        out = _filter(res.stdout + res.stderr)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed on fp8g_stream.hip:\n" + out)
+        if verbose and out.strip():
+            print(out)
+        os.replace(tmp, STREAM_LIBRARY)
+    finally:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+    return STREAM_LIBRARY
+
+
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv, lds_poison="--lds-poison" in sys.argv))
+    if "--stream" in sys.argv:
+        print(build_stream(verbose="--verbose" in sys.argv))
+    else:
+        print(build(verbose="--verbose" in sys.argv, lds_poison="--lds-poison" in sys.argv))
