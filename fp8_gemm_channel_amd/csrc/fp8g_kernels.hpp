@@ -1256,7 +1256,7 @@ __device__ __forceinline__ void splitk_finish(const SkinnyArgs &a, int n0, int *
 // several: unscaled fp32 partials, which the column tile's last workgroup adds.
 template <int RB, int MB, bool EPI, int NW = 4>
 __device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const SkinnyArgs &a, float *red, int n0,
-                                              int s, int wave, int lane) {
+                                              int s, int wave, int lane, const v4f *esc, const v4f *ebi) {
   const int g = lane >> 4, lr = lane & 15;
   __syncthreads();
 #pragma unroll
@@ -1266,9 +1266,10 @@ __device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const Sk
 #pragma unroll
       for (int e = 0; e < 4; ++e) red[(((wave * RB + rb) * MB + mb) * 4 + e) * 64 + lane] = acc[rb][mb][e];
   __syncthreads();
-  const v4i rsrc_s = make_rsrc(a.scale, (uint32_t)a.N * 4u);
-  const v4i rsrc_b = make_rsrc(a.bias, a.bias ? (uint32_t)a.N * 4u : 0u);
-  for (int b = wave; b < RB * MB; b += NW) {
+#pragma unroll
+  for (int i = 0; i < (RB * MB + NW - 1) / NW; ++i) {
+    const int b = wave + i * NW;
+    if (b >= RB * MB) break;
     const int rb = b / MB, mb = b % MB;
     float v[4];
 #pragma unroll
@@ -1292,9 +1293,9 @@ __device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const Sk
       uint32_t bits[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float z = v[e] * llvm_buffer_load_f32(rsrc_s, (uint32_t)(n + e) * 4u, 0, 0);
+        float z = v[e] * esc[i][e];
         if constexpr (EPI) {
-          if (a.bias) z += llvm_buffer_load_f32(rsrc_b, (uint32_t)(n + e) * 4u, 0, 0);
+          if (a.bias) z += ebi[i][e];
           z = activation_rt(z, a.act);
         }
         bits[e] = bf16_rne(z);
@@ -1331,6 +1332,26 @@ __global__ __launch_bounds__(64 * NW, 1) void fp8g_splitk_partial_kernel(SkinnyA
 
   const v4i rsrc_w = make_rsrc(a.w + (size_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
   const v4i rsrc_x = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)K);
+
+  // With one K slice, the epilogue's scales (and biases) for the blocks this
+  // wave finishes -- columns n .. n+3 of block b = wave + i NW, n = n0 + 16 (b /
+  // MB) + 4 (lane / 16) -- requested before any DMA, so the kernel's end does
+  // not wait for a cold read (columns at or past N read as zero).  With several
+  // slices the column tile's last workgroup scales in splitk_finish.
+  constexpr int BPW = (RB * MB + NW - 1) / NW;
+  v4f esc[BPW], ebi[BPW];
+  {
+    const bool one = gridDim.y == 1;
+    const v4i rsrc_s = make_rsrc(a.scale, one ? (uint32_t)a.N * 4u : 0u);
+    const v4i rsrc_b = make_rsrc(a.bias, EPI && one && a.bias ? (uint32_t)a.N * 4u : 0u);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int b = wave + i * NW;
+      const uint32_t at = b < RB * MB ? (uint32_t)(n0 + 16 * (b / MB) + 4 * (lane >> 4)) * 4u : kOut;
+      esc[i] = llvm_buffer_load_v4f32(rsrc_s, at, 0, 0);
+      ebi[i] = EPI ? llvm_buffer_load_v4f32(rsrc_b, at, 0, 0) : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  }
 
   // DMA instruction t moves rows 8t .. 8t+7 of a slot (w rows, then x rows).
   uint32_t src_off[OPS], src_chunk[OPS];
@@ -1408,7 +1429,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fp8g_splitk_partial_kernel(SkinnyA
       for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = mfma16<FMT>(af[rb], bf[mb], acc[rb][mb]);
   }
 
-  skinny_finish<RB, MB, EPI, NW>(acc, a, (float *)smem, n0, s, wave, lane);
+  skinny_finish<RB, MB, EPI, NW>(acc, a, (float *)smem, n0, s, wave, lane, esc, ebi);
 }
 
 // Epilogue for accumulators of V_MFMA_F32_16X16X128_F8F6F4 (A = w, B = x):
