@@ -467,6 +467,7 @@ int run(const void *x, const void *w, const float *scale, const float *bias, voi
     l.bias = bias;
     l.act = act;
     l.fmt = fmt;
+    l.ywb = cdiv(M, p.tile_m) * cdiv(N, p.tile_n) > kNumCUs ? 1 : 0;
     l.ev = events;
     void *ws = nullptr;
     if (p.workspace_bytes > 0) {

@@ -26,6 +26,7 @@ struct MainLaunch {
   int variant;   // main-path configuration id
   bool k_tail;   // K % tile_k != 0
   int ystore;    // widest y store: 16 (N % 8 == 0, y 16-byte aligned), 8 (N % 4 == 0, y 8-byte aligned) or 2
+  int ywb = 0;   // y stores write-back (more tiles than compute units) or non-temporal
   const float *bias = nullptr;  // per-column bias [N], or null
   int act = 0;                  // epilogue activation (FP8G_ACT_*)
   int fmt = 0;                  // (w format << 1) | x format, 0 = E4M3, 1 = E5M2
