@@ -85,6 +85,23 @@ def test_main_cache_line_rows(shape):
     assert np.array_equal(a, b), "variant 20 differs from variant 10"
 
 
+# ---------------------- launches with more tiles than compute units (write-back y) --
+# More tiles than the GPU's 256 compute units switch the 16-byte y stores from
+# non-temporal to write-back: whole tiles, ragged edge tiles (M or N past the
+# last whole tile), the column-pair stores of variant 20 and the 128-row tiles.
+MULTIWAVE_CASES = [((4100, 4352, 512), 19), ((4352, 4352, 1001), 20), ((4100, 4352, 1001), 10),
+                   ((4352, 4104, 300), 18)]
+
+
+@pytest.mark.parametrize("shape,variant", MULTIWAVE_CASES, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else f"v{v}")
+def test_multiwave_write_back_stores(shape, variant):
+    M, N, K = shape
+    p = fg.fp8_gemm_plan_ex(M, N, K, path=fg.PATH_MAIN, variant=variant)
+    assert p["variant"] == variant
+    assert -(-M // p["tile_m"]) * -(-N // p["tile_n"]) > 256, "the case must have more tiles than compute units"
+    _full_case(M, N, K, seed=5, path=fg.PATH_MAIN, variant=variant)
+
+
 def test_odd_k_operands_inside_larger_buffers():
     """K = 4127 (every row start offset mod 128 over 128 rows) with the operands
     starting 0, 16 and 80 rows into larger buffers (128-byte aligned, then 112
