@@ -1271,12 +1271,12 @@ __device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const Sk
                                               int s, int wave, int lane, const v4f *esc, const v4f *ebi) {
   const int g = lane >> 4, lr = lane & 15;
   __syncthreads();
+  // red[wave][block][lane] holds the lane's four sums of a block (16 bytes):
+  // one 16-byte write per block, one 16-byte read per wave and block below.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[(((wave * RB + rb) * MB + mb) * 4 + e) * 64 + lane] = acc[rb][mb][e];
+    for (int mb = 0; mb < MB; ++mb) *(v4f *)&red[(((wave * RB + rb) * MB + mb) * 64 + lane) * 4] = acc[rb][mb];
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < (RB * MB + NW - 1) / NW; ++i) {
@@ -1284,12 +1284,14 @@ __device__ __forceinline__ void skinny_finish(const v4f (&acc)[RB][MB], const Sk
     if (b >= RB * MB) break;
     const int rb = b / MB, mb = b % MB;
     float v[4];
+    {
+      v4f t = *(const v4f *)&red[(b * 64 + lane) * 4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float t = red[((b) * 4 + e) * 64 + lane];
-#pragma unroll
-      for (int o = 1; o < NW; ++o) t += red[((o * RB * MB + b) * 4 + e) * 64 + lane];
-      v[e] = t;
+      for (int o = 1; o < NW; ++o) {
+        const v4f u = *(const v4f *)&red[((o * RB * MB + b) * 64 + lane) * 4];
+        t[0] += u[0]; t[1] += u[1]; t[2] += u[2]; t[3] += u[3];
+      }
+      v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
     }
     const int n = n0 + 16 * rb + 4 * g;
     const int m = 16 * mb + lr;
