@@ -223,7 +223,8 @@ def stream_reference(spec: str, fg, synth, torch, dev, stream) -> int:
     outs = {m: torch.empty(int(lib.fp8g_stream_out_words(m, N, K)), dtype=torch.int32, device=dev) for m in STREAM_MODES}
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream), e1.record(stream)
+    e0.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     t = {k: [] for k in ["gemm"] + list(STREAM_MODES)}
     for i in range(20):
