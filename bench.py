@@ -199,22 +199,82 @@ STREAM_MODES = {0: "LDS-DMA, decode pattern (48 rows x 8 waves, 2 slots a wave)"
                 2: "16-byte loads into registers (1024 x 256 threads, 8 in flight)"}
 
 
-def stream_reference(spec: str, fg, synth, torch, dev, stream) -> int:
-    """bench.py --stream N,K: the default plan at M = 32 and the reference
-    streams of libfp8g_stream.so over the same N x K weight, interleaved, cold
-    (512 MiB rewritten before every call), events attached to each kernel.
-    Each stream's XOR checksum is checked against the weight's."""
+REF_LIBRARY = os.path.join(ROOT, "fp8_gemm_channel_amd", "libfp8g_ref.so")
+
+
+def load_ref_library():
+    """libfp8g_ref.so (reference kernels, built by __graft_entry__.build() or
+    `python fp8_gemm_channel_amd/build.py --ref`) through ctypes."""
     import ctypes
 
-    N, K = (int(v) for v in spec.split(","))
-    path = os.path.join(ROOT, "fp8_gemm_channel_amd", "libfp8g_stream.so")
-    if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: python fp8_gemm_channel_amd/build.py --stream")
-    lib = ctypes.CDLL(path)
+    if not os.path.exists(REF_LIBRARY):
+        raise RuntimeError(f"{REF_LIBRARY} is missing: python fp8_gemm_channel_amd/build.py --ref")
+    lib = ctypes.CDLL(REF_LIBRARY)
     lib.fp8g_stream_out_words.restype = ctypes.c_longlong
     lib.fp8g_stream_out_words.argtypes = [ctypes.c_int] * 3
     lib.fp8g_stream_launch.restype = ctypes.c_int
     lib.fp8g_stream_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
+    lib.fp8g_mfma_ref_launch.restype = ctypes.c_int
+    lib.fp8g_mfma_ref_launch.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_uint] + [ctypes.c_void_p] * 3
+    return lib
+
+
+def attainable(torch, dev, stream, flush, weight) -> dict:
+    """What this GPU attains on the two resources the shapes are bound by,
+    measured by the reference kernels of libfp8g_ref.so right after the timed
+    steps: back-to-back fp8 MFMAs on random E4M3 operands from registers (256
+    workgroups of four waves, no memory traffic; median of 5 launches of ~2 ms),
+    and one launch reading a cold 48 MiB weight with 16-byte non-temporal loads
+    (median of 5, 512 MiB rewritten before each).  Null fields if the library
+    is missing."""
+    try:
+        lib = load_ref_library()
+    except RuntimeError as e:
+        return {"error": str(e)}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    e1.record(stream)
+    grid, iters = 256, 2000
+    out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    t = []
+    for i in range(8):
+        rc = lib.fp8g_mfma_ref_launch(out.data_ptr(), grid, iters, 1 + i, stream.cuda_stream, e0.cuda_event,
+                                      e1.cuda_event)
+        if rc != 0:
+            raise RuntimeError(f"fp8g_mfma_ref_launch returned {rc}")
+        e1.synchronize()
+        if i >= 3:
+            t.append(e0.elapsed_time(e1) * 1e-3)
+    mfma_flops = grid * 4 * iters * 64 * 2 * 16 * 16 * 128
+    mfma = mfma_flops / float(np.median(t)) / 1e12
+    N, K = weight.shape
+    words = torch.empty(int(lib.fp8g_stream_out_words(2, N, K)), dtype=torch.int32, device=dev)
+    t = []
+    for i in range(7):
+        flush.fill_(i)
+        rc = lib.fp8g_stream_launch(2, weight.data_ptr(), N, K, words.data_ptr(), stream.cuda_stream, e0.cuda_event,
+                                    e1.cuda_event)
+        if rc != 0:
+            raise RuntimeError(f"fp8g_stream_launch returned {rc}")
+        e1.synchronize()
+        if i >= 2:
+            t.append(e0.elapsed_time(e1) * 1e-3)
+    hbm = N * K / float(np.median(t)) / 1e12
+    return {"mfma_fp8_tflops": round(mfma, 1),
+            "mfma_kernel": "fp8g_mfma_ref_kernel: back-to-back V_MFMA_F32_16X16X128_F8F6F4 on random E4M3 codes "
+                           "from registers, 256 workgroups x 4 waves, events on the kernel",
+            "hbm_read_tb_s": round(hbm, 3),
+            "hbm_kernel": f"fp8g_stream_vgpr_kernel: one launch reading a cold {N}x{K} byte weight with 16-byte "
+                          "non-temporal loads, events on the kernel"}
+
+
+def stream_reference(spec: str, fg, synth, torch, dev, stream) -> int:
+    """bench.py --stream N,K: the default plan at M = 32 and the reference
+    streams of libfp8g_ref.so over the same N x K weight, interleaved, cold
+    (512 MiB rewritten before every call), events attached to each kernel.
+    Each stream's XOR checksum is checked against the weight's."""
+    N, K = (int(v) for v in spec.split(","))
+    lib = load_ref_library()
     M = 32
     x, w, s = synth.fp8_inputs(M, N, K, seed=42)
     xd, wd, sd = (torch.from_numpy(a).to(dev) for a in (x, w, s))
@@ -275,7 +335,7 @@ def main() -> int:
                          "e.g. the decode weight stream at M=1 beside M=32")
     ap.add_argument("--stream", default="",
                     help="only time, on one N,K weight (cold, events on the kernel, 20 rounds interleaved), the "
-                         "default plan at M=32 beside the reference streams of libfp8g_stream.so that read the "
+                         "default plan at M=32 beside the reference streams of libfp8g_ref.so that read the "
                          "same bytes and compute nothing: e.g. 12288,4096 for the decode weight")
     args = ap.parse_args()
 
@@ -448,6 +508,15 @@ def main() -> int:
         roofline["peak_at_sclk"] = round(256 * 8192 * clk["sclk_mhz_median"] * 1e6 / 1e12, 1)
         roofline["frac_at_sclk"] = round(roofline["achieved"] / roofline["peak_at_sclk"], 4)
 
+    # the decode weight when it is one of the shapes, else a 48 MiB buffer of its size
+    dec = [w for w in workloads if w.name == "decode-m32"]
+    weight = dev_bufs[dec[0].name][1] if dec else torch.zeros((12288, 4096), dtype=torch.uint8, device=dev)
+    att = attainable(torch, dev, stream, flush, weight)
+    if att.get("mfma_fp8_tflops") and roofline["unit"] == "TFLOP/s":
+        roofline["attainable_peak"] = att["mfma_fp8_tflops"]
+        roofline["frac_of_attainable"] = round(roofline["achieved"] / att["mfma_fp8_tflops"], 4)
+    log(f"attainable: {att}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: the oracle on each full shape ...")
@@ -470,6 +539,7 @@ def main() -> int:
         "value_marker_timed": round(geo_marker, 4),
         "per_config": per,
         "roofline": roofline,
+        "attainable": att,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

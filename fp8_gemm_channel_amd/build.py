@@ -7,9 +7,9 @@ LDS-DMA is preceded by a NaN fill of its destination (FP8G_LDS_POISON), so a
 read that runs ahead of its DMA shows up as NaN outputs.  Load it by setting
 FP8G_LIBRARY to its path before importing the package.
 
---stream builds libfp8g_stream.so instead: the reference HBM streams that
-bench.py --stream times beside the memory-bound shapes (csrc/fp8g_stream.hip;
-no part of the GEMM interface).
+--ref builds libfp8g_ref.so instead: the reference kernels (HBM streams and
+an MFMA loop) that bench.py times beside the GEMM (csrc/fp8g_ref.hip; no part
+of the GEMM interface).
 
 (run as a file: importing the package loads the library this builds)
 
@@ -26,8 +26,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libfp8g.so")
 POISON_LIBRARY = os.path.join(PKG, "libfp8g_lds_poison.so")
-STREAM_LIBRARY = os.path.join(PKG, "libfp8g_stream.so")
-STREAM_SOURCE = os.path.join(CSRC, "fp8g_stream.hip")
+REF_LIBRARY = os.path.join(PKG, "libfp8g_ref.so")
+REF_SOURCE = os.path.join(CSRC, "fp8g_ref.hip")
 SOURCES = [os.path.join(CSRC, f) for f in ("fp8g_api.cpp", "fp8g_kernels.hip", "fp8g_noalloc.hip")] + sorted(
     os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.startswith("fp8g_launch_") and f.endswith(".hip"))
 
@@ -88,29 +88,29 @@ def build(verbose: bool = False, jobs: int = 0, lds_poison: bool = False) -> str
     return target
 
 
-def build_stream(verbose: bool = False) -> str:
-    """Compile and link libfp8g_stream.so (the reference streams) in-tree."""
+def build_ref(verbose: bool = False) -> str:
+    """Compile and link libfp8g_ref.so (the reference kernels) in-tree."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = STREAM_LIBRARY + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *HIPCC_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, STREAM_SOURCE]
+    tmp = REF_LIBRARY + ".tmp%d" % os.getpid()
+    cmd = [hipcc, *HIPCC_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, REF_SOURCE]
     if verbose:
         print(" ".join(cmd), flush=True)
     try:
         res = subprocess.run(cmd, capture_output=True, text=True)
         out = _filter(res.stdout + res.stderr)
         if res.returncode != 0:
-            raise RuntimeError("hipcc failed on fp8g_stream.hip:\n" + out)
+            raise RuntimeError("hipcc failed on fp8g_ref.hip:\n" + out)
         if verbose and out.strip():
             print(out)
-        os.replace(tmp, STREAM_LIBRARY)
+        os.replace(tmp, REF_LIBRARY)
     finally:
         if os.path.exists(tmp):
             os.remove(tmp)
-    return STREAM_LIBRARY
+    return REF_LIBRARY
 
 
 if __name__ == "__main__":
-    if "--stream" in sys.argv:
-        print(build_stream(verbose="--verbose" in sys.argv))
+    if "--ref" in sys.argv:
+        print(build_ref(verbose="--verbose" in sys.argv))
     else:
         print(build(verbose="--verbose" in sys.argv, lds_poison="--lds-poison" in sys.argv))

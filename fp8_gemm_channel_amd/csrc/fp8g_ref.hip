@@ -1,10 +1,12 @@
-// fp8g_stream.hip -- reference streams for the memory-bound GEMM shapes
-// (libfp8g_stream.so, separate from libfp8g.so and not part of its interface).
+// fp8g_ref.hip -- reference kernels that measure what MI355X attains on the two
+// resources the GEMM is bound by (libfp8g_ref.so, separate from libfp8g.so and
+// not part of its interface): HBM streams for the memory-bound shapes, and a
+// loop of back-to-back fp8 MFMAs from registers for the compute-bound ones.
 //
-// They read an N x K byte matrix -- a decode weight -- once from HBM and compute
-// nothing but an XOR checksum of what they read, so a profile of the split-K
-// kernel can be set beside the rate at which one launch streams the same bytes
-// with nothing else to do:
+// The streams read an N x K byte matrix -- a decode weight -- once from HBM and
+// compute nothing but an XOR checksum of what they read, so a profile of the
+// split-K kernel can be set beside the rate at which one launch streams the
+// same bytes with nothing else to do:
 //
 //   mode 0  the split-K kernel's weight stream alone: 48 rows per workgroup,
 //           eight waves taking 128-byte K chunks round-robin, each through a
@@ -85,6 +87,50 @@ __global__ __launch_bounds__(256) void fp8g_stream_vgpr_kernel(const uint8_t *w,
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+
+// Back-to-back V_MFMA_F32_16X16X128_F8F6F4 from registers, one wave per SIMD
+// (256 threads, one workgroup per compute unit at most): each wave runs `iters`
+// rounds of 64 independent MFMAs over eight A and eight B operand sets of
+// pseudo-random E4M3 codes (bit 3 of every byte cleared: no NaN codes), the
+// data the GEMM's operands look like.  No memory traffic in the loop; out gets
+// one float per thread (a sum of its accumulators) so nothing is dead.  The
+// MFMA rate sustained on random operands is data dependent and below the
+// published peak (the chip's clock drops under this load).
+__device__ __forceinline__ uint32_t ref_mix(uint32_t h) {
+  h ^= h >> 16; h *= 0x7feb352dU; h ^= h >> 15; h *= 0x846ca68bU; h ^= h >> 16;  // a 32-bit integer finalizer
+  return h;
+}
+template <typename F, int... I>
+__device__ __forceinline__ void ref_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void ref_for(F &&f) { ref_for_impl(f, std::make_integer_sequence<int, N>{}); }
+
+__global__ __launch_bounds__(256, 1) void fp8g_mfma_ref_kernel(float *out, int iters, uint32_t seed) {
+  v8i A[8], B[8];
+  for (int s = 0; s < 8; ++s)
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ha = ref_mix(seed * 977u + threadIdx.x * 131u + blockIdx.x * 7919u + (uint32_t)(s * 17 + i));
+      const uint32_t hb = ref_mix(ha ^ 0x9e3779b9u);
+      A[s][i] = (int)(ha & 0xF7F7F7F7u);
+      B[s][i] = (int)(hb & 0xF7F7F7F7u);
+    }
+  v4f acc[64];
+  ref_for<64>([&](auto jc) __attribute__((always_inline)) { acc[decltype(jc)::value] = v4f{0.f, 0.f, 0.f, 0.f}; });
+  for (int it = 0; it < iters; ++it)
+    ref_for<64>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      acc[j] = mfma16<0>(A[j & 7], B[(j >> 3) & 7], acc[j]);
+    });
+  float t = 0.f;
+  ref_for<64>([&](auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  });
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = t;
+}
+
 }  // namespace fp8g
 
 // Launch stream `mode` over the N x K matrix w (device pointer, row-major,
@@ -123,5 +169,19 @@ extern "C" int fp8g_stream_launch(int mode, const void *w, int N, int K, unsigne
     default:
       return -2;
   }
+  return (int)hipGetLastError();
+}
+
+// Launch the MFMA loop: `grid` workgroups of 256 threads, `iters` rounds of 64
+// MFMAs per wave (2 * 16 * 16 * 128 FLOPs each); out: device buffer of grid *
+// 256 floats.  Events e0/e1 (may be null) are recorded around the dispatch.
+// Returns 0, -1 for grid outside 1..65536 or iters outside 1..1000000, or the
+// HIP error of the launch.
+extern "C" int fp8g_mfma_ref_launch(float *out, int grid, int iters, unsigned int seed, void *stream, void *e0,
+                                    void *e1) {
+  using namespace fp8g;
+  if (grid < 1 || grid > 65536 || iters < 1 || iters > 1000000) return -1;
+  hipExtLaunchKernelGGL(fp8g_mfma_ref_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (hipEvent_t)e0,
+                        (hipEvent_t)e1, 0, out, iters, (uint32_t)seed);
   return (int)hipGetLastError();
 }
