@@ -1767,6 +1767,22 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
     const uint4 v = *(const uint4 *)(smem + at + (hf ? c1 : c0));
     f[4 * hf + 0] = (int)v.x; f[4 * hf + 1] = (int)v.y; f[4 * hf + 2] = (int)v.z; f[4 * hf + 3] = (int)v.w;
   };
+  // The same read in the K loop: one VALU add of the unit's base (an SGPR) to
+  // the lane's loop-invariant row and chunk offset per quadrant and chunk half,
+  // the block as the instruction's immediate offset.  The add is written out so
+  // the compiler cannot reassociate it: left to itself it spread the k % 3 of
+  // the rotating units over the lane offsets, 30 VALU instructions a step, each
+  // taking issue cycles from the MFMAs of this one wave per SIMD.
+  const uint32_t oa[2] = {ra + c0, ra + c1}, ob[2] = {rb + c0, rb + c1};
+  auto lane_at = [](uint32_t unit, uint32_t off) __attribute__((always_inline)) {
+    uint32_t r;
+    asm("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(unit), "v"(off));
+    return r;
+  };
+  auto rd16 = [&](uint32_t unit, const uint32_t (&o)[2], int blk, int hf, v8i &f) __attribute__((always_inline)) {
+    const uint4 v = *(const uint4 *)(smem + lane_at(unit, o[hf]) + blk * 16 * BK);
+    f[4 * hf + 0] = (int)v.x; f[4 * hf + 1] = (int)v.y; f[4 * hf + 2] = (int)v.z; f[4 * hf + 3] = (int)v.w;
+  };
 
   v4f acc[FN][FM];
 #pragma unroll
@@ -1821,7 +1837,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
     for (int q = 0; q < 16; ++q) {
       const int mb = q >> 2, nb = q & 3;
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
-      if (q < 8) half16(u_xh(s) + rb + (q >> 1) * 16 * BK, q & 1, B[4 + (q >> 1)]);
+      if (q < 8) rd16(u_xh(s), ob, q >> 1, q & 1, B[4 + (q >> 1)]);
       if ((q & 3) == 1 && more2) issue_l(s + 2, q >> 2);
       __builtin_amdgcn_sched_barrier(0);  // keep the spread as written
     }
@@ -1831,7 +1847,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
     for (int q = 0; q < 16; ++q) {
       const int mb = 4 + (q >> 2), nb = q & 3;
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
-      if (q < 8) half16(u_wh(s) + ra + (q >> 1) * 16 * BK, q & 1, A[4 + (q >> 1)]);
+      if (q < 8) rd16(u_wh(s), oa, q >> 1, q & 1, A[4 + (q >> 1)]);
       if ((q & 3) == 1 && more2) issue_l(s + 2, 4 + (q >> 2));
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1849,7 +1865,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
     for (int q = 0; q < 16; ++q) {
       const int nb = 4 + (q >> 2), mb = q & 3;
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
-      if (more && q < 8) half16(u_wl(s + 1) + ra + (q >> 1) * 16 * BK, q & 1, A[q >> 1]);
+      if (more && q < 8) rd16(u_wl(s + 1), oa, q >> 1, q & 1, A[q >> 1]);
       if ((q & 3) == 1 && more3) issue_h(s + 3, q >> 2);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1859,7 +1875,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
     for (int q = 0; q < 16; ++q) {
       const int nb = 4 + (q >> 2), mb = 4 + (q & 3);
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
-      if (more && q < 8) half16(u_xl(s + 1) + rb + (q >> 1) * 16 * BK, q & 1, B[q >> 1]);
+      if (more && q < 8) rd16(u_xl(s + 1), ob, q >> 1, q & 1, B[q >> 1]);
       if ((q & 3) == 1 && more3) issue_h(s + 3, 4 + (q >> 2));
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1900,14 +1916,14 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
     for (int q = 0; q < 16; ++q) {
       const int mb = q >> 2, nb = q & 3;
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
-      if (q < 8) half16(u_xh(s) + rb + (q >> 1) * 16 * BK, q & 1, B[4 + (q >> 1)]);
+      if (q < 8) rd16(u_xh(s), ob, q >> 1, q & 1, B[4 + (q >> 1)]);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int mb = 4 + (q >> 2), nb = q & 3;
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
-      if (q < 8) half16(u_wh(s) + ra + (q >> 1) * 16 * BK, q & 1, A[4 + (q >> 1)]);
+      if (q < 8) rd16(u_wh(s), oa, q >> 1, q & 1, A[4 + (q >> 1)]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // every wave has read its operands: the units hold the bf16 tile from here
