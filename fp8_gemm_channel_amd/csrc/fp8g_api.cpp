@@ -347,18 +347,19 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
   if (variant == 19 && p->k_tail)
     return fail(FP8G_ERR_INVALID_ARG, "main variant 19 needs K %% 128 == 0 (K=%lld)", (long long)K);
   // Variant 20 (rows fetched as whole cache lines, realigned in registers) needs
-  // odd K, the last row of each operand to end on a 16-byte boundary (M K and N
-  // K multiples of 16) and 128-byte-aligned operands (checked by the call, which
-  // runs variant 10 instead when the plan was the planner's choice).  Where it
+  // odd K above 128 (two K steps at least), the last row of each operand to end
+  // on a 16-byte boundary (M K and N K multiples of 16) and 128-byte-aligned
+  // operands (checked by the call, which runs variant 10 instead when the plan
+  // was the planner's choice).  Where it
   // applies it replaces variant 10 for odd K: measured on MI355X at 4096^2 x
   // 4127, 74.6 us against 89.2 us for variant 10 streaming the rows as they lie.
   const bool lines_ok = (M * K) % 16 == 0 && (N * K) % 16 == 0;
-  if (auto_variant && variant == 10 && K % 2 == 1 && lines_ok) {
+  if (auto_variant && variant == 10 && K % 2 == 1 && K > 128 && lines_ok) {
     variant = 20;
     p->variant = 20;
   }
-  if (variant == 20 && K % 2 == 0)
-    return fail(FP8G_ERR_INVALID_ARG, "main variant 20 needs odd K (K=%lld)", (long long)K);
+  if (variant == 20 && (K % 2 == 0 || K <= 128))
+    return fail(FP8G_ERR_INVALID_ARG, "main variant 20 needs odd K above 128 (K=%lld)", (long long)K);
   if (variant == 20 && !lines_ok)
     return fail(FP8G_ERR_INVALID_ARG, "main variant 20 needs M*K and N*K multiples of 16 (M=%lld N=%lld K=%lld)",
                 (long long)M, (long long)N, (long long)K);

@@ -2022,7 +2022,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
 // block's first MFMA; in the last step the bytes at or past K are cleared in
 // both operands.
 //
-// Requirements (checked by the host): K odd; x and w 128-byte aligned, so no
+// Requirements (checked by the host): K odd and above 128; x and w 128-byte aligned, so no
 // line starts before an operand; M K and N K multiples of 16, so the last row
 // of either operand ends on a 16-byte boundary and a tile's buffer range never
 // cuts a chunk (bytes past the range read as zero; bytes of the next row that a
@@ -2131,11 +2131,20 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
     lpw[k] = (uint32_t)wave_n * 64u * BK + pos;
     sel[k] = (l16 >> 1) + v >= 8 ? ~0u : 0u;
   }
-  // The three addresses of a window read from units S0 (line t) and S1 (line t + 1).
+  // The three addresses of a window read from units S0 (line t) and S1 (line t + 1):
+  // two VALU instructions each, written out so the compiler cannot reassociate
+  // the wave-uniform unit bases into the lane offsets (it spent about three more
+  // a window that way, and each VALU instruction takes issue cycles from the
+  // MFMAs of this one wave per SIMD).
   auto win = [&](uint32_t S0, uint32_t S1, const uint32_t (&lp)[3], uint32_t (&at)[3])
       __attribute__((always_inline)) {
+    const uint32_t d = S1 - S0;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) at[k] = lp[k] + S0 + (sel[k] & (S1 - S0));
+    for (int k = 0; k < 3; ++k) {
+      uint32_t m;
+      asm("v_and_b32 %0, %1, %2" : "=v"(m) : "s"(d), "v"(sel[k]));
+      asm("v_add3_u32 %0, %1, %2, %3" : "=v"(at[k]) : "v"(lp[k]), "s"(S0), "v"(m));
+    }
   };
   // Read k of block b mod 4 = bl: chunks 0 and 1 into f, chunk 2 into x3.
   auto read_blk = [&](const uint32_t (&at)[3], int bl, int k, v8i &f, v4i &x3) __attribute__((always_inline)) {
@@ -2341,9 +2350,24 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
                   (int)group_exists(2, s) + (int)group_exists(3, s) + (int)group_exists(4, s));
     __syncthreads();
   };
+  // K > 128 (checked by the host), so the steady steps end at s = nk - 2 and
+  // exactly two guarded steps follow.  In the plain kernel they are written out
+  // as steps nk - 2 and nk - 1, so every guard in them folds at compile time:
+  // with a loop (or a conditional step) there, the compiler routed eight
+  // accumulators through AGPR copies inside the steady loop, 40 VALU
+  // instructions and extra wait states a step, and with the guards left to run
+  // time the two written-out steps were long branchy code (slower for small K).
+  // The cost is two register spills outside the K loop (20 bytes of scratch a
+  // lane).  The kernels with a bias or an activation keep the loop (written
+  // out, their larger epilogue spilled more).
   int s = 0;
   for (; s + 3 <= nk; ++s) step(s, std::true_type{});
-  for (; s < nk; ++s) step(s, std::false_type{});
+  if constexpr (EPI) {
+    for (; s < nk; ++s) step(s, std::false_type{});
+  } else {
+    step(nk - 2, std::false_type{});
+    step(nk - 1, std::false_type{});
+  }
 
   // Every DMA has landed and every wave is done with the units: scales (and
   // biases) go into LDS past the bf16 tile.
@@ -2441,6 +2465,8 @@ static hipError_t launch_main4w_t(const MainLaunch &l, hipStream_t stream) {
 // The cache-line-row kernel (variant 20; the host checks its requirements).
 template <bool EPI>
 static hipError_t launch_main4wr_t(const MainLaunch &l, hipStream_t stream) {
+  // two K steps at least: the kernel runs its last two steps unconditionally
+  if (l.K <= 128 || l.K % 2 == 0) return hipErrorInvalidValue;
   const MainArgs a = main_args(l);
   const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(256);
   return with_format(l.fmt, [&](auto fmt) {

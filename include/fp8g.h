@@ -122,9 +122,9 @@ int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y,
  *             17 = 128x256 and 18 = 128x128 (mid M); 3 = 64x64 (small
  *             problems); 16 = variant 10 with stream-K (opt-in); 20 = variant
  *             19's tiles on rows fetched as whole 128-byte cache lines and
- *             realigned in registers (the default for odd K; needs odd K, M*K
- *             and N*K multiples of 16 and x, w 128-byte aligned, else
- *             FP8G_ERR_INVALID_ARG).  Split-K
+ *             realigned in registers (the default for odd K above 128;
+ *             needs odd K > 128, M*K and N*K multiples of 16 and x, w
+ *             128-byte aligned, else FP8G_ERR_INVALID_ARG).  Split-K
  *             path: 1-5 = 16*v w rows per workgroup through per-wave LDS
  *             rings, 4 waves (the default for M > 32); 21-24 = 16*(v-20)
  *             rows with 8 waves (the default for M <= 32).  Row counts are

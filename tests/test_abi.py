@@ -174,9 +174,13 @@ def test_plan_main_kernel_choice():
     # the whole-line variant (opt-in) needs odd K and M K, N K multiples of 16
     assert fg.fp8_gemm_plan_ex(4096, 4096, 4127, fg.PATH_MAIN, 20, 0)["variant"] == 20
     assert fg.fp8_gemm_plan_ex(48, 560, 3001, fg.PATH_MAIN, 20, 0)["variant"] == 20
-    for shape in [(4097, 4096, 4127), (4096, 4104, 4127), (4096, 4104, 4128), (256, 256, 1000), (256, 256, 4096)]:
+    for shape in [(4097, 4096, 4127), (4096, 4104, 4127), (4096, 4104, 4128), (256, 256, 1000), (256, 256, 4096),
+                  (256, 256, 127), (256, 512, 17), (16, 16, 1)]:
         with pytest.raises(fg.Fp8gError):
             fg.fp8_gemm_plan_ex(*shape, fg.PATH_MAIN, 20, 0)
+    # one K step (odd K up to 127) runs on the eight-wave kernel
+    assert fg.fp8_gemm_plan(4096, 4096, 127)["variant"] == 10
+    assert fg.fp8_gemm_plan(4096, 4096, 129)["variant"] == 20
     assert fg.fp8_gemm_plan(3072, 3072, 3072)["variant"] == 19      # 144 tiles
     forced = fg.fp8_gemm_plan_ex(300, 300, 384, fg.PATH_MAIN, 19, 0)
     assert forced["variant"] == 19 and forced["grid"] == 4 and forced["tile_k"] == 128

@@ -63,13 +63,13 @@ def test_main_one_wave_per_simd_matches_eight_wave():
 
 
 # ------------- main path, rows fetched as whole cache lines (variant 20, odd K) --
-# K from one byte (a single step) to several steps with every kind of tail
-# (1, 17, 127 bytes past the last whole step, ...); M, N multiples of 16 (the
-# variant needs M K and N K multiples of 16) with rows past M and N in the edge
-# tiles.
-V20_SHAPES = [(256, 256, 4127), (272, 400, 4127), (512, 768, 1001), (256, 512, 1), (304, 256, 17),
+# K from two steps (129, the smallest K the variant takes) to many, with every
+# kind of tail (1, 3, 17, 127 bytes past the last whole step, ...); M, N
+# multiples of 16 (the variant needs M K and N K multiples of 16) with rows past
+# M and N in the edge tiles.
+V20_SHAPES = [(256, 256, 4127), (272, 400, 4127), (512, 768, 1001), (256, 512, 131), (304, 256, 145),
               (256, 256, 129), (528, 272, 257), (256, 256, 383), (256, 256, 4113), (256, 256, 4225),
-              (256, 256, 4095), (48, 560, 3001), (768, 256, 8191), (272, 288, 641), (16, 16, 3)]
+              (256, 256, 4095), (48, 560, 3001), (768, 256, 8191), (272, 288, 641), (16, 16, 259)]
 
 
 @pytest.mark.parametrize("shape", V20_SHAPES, ids=lambda s: "x".join(map(str, s)))
