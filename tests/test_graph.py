@@ -3,7 +3,8 @@
 Callers that replay work through graphs capture a call once and replay it.
 Every path that uses a workspace is captured here: split-K with several
 slices (partials and call-id tickets: the ticket words must not need zeroing
-between replays) and stream-K, plus a main-path call with a K tail.  Each graph is replayed several times with the program's own eager
+between replays) and stream-K, plus main-path calls with a K tail (one on the
+whole-line odd-K kernel, which uses scratch memory for two spilled registers).  Each graph is replayed several times with the program's own eager
 work (a different GEMM, a synchronisation) in between, and every replay is
 compared with the eager result bit for bit, after the inputs were rewritten in
 place, so that a replay that reused stale data would show.
@@ -22,6 +23,9 @@ CASES = [
     ("splitk-S4", (32, 1000, 4127), dict(path=fg.PATH_SPLITK, split_k=4)),
     ("splitk-S8-bias-silu", (17, 777, 3000), dict(path=fg.PATH_SPLITK, split_k=8)),
     ("main-odd-k", (700, 520, 3001), dict(path=fg.PATH_MAIN, variant=10)),
+    # the default odd-K kernel (rows as whole cache lines; it keeps two spilled
+    # registers in scratch memory), edge tiles in both dimensions
+    ("main-odd-k-lines", (528, 304, 3001), dict(path=fg.PATH_MAIN, variant=20)),
     ("stream-k", (513, 520, 1000), dict(path=fg.PATH_MAIN, variant=16, split_k=40)),
     ("main-v18-gelu", (300, 520, 1000), dict(path=fg.PATH_MAIN, variant=18)),
 ]

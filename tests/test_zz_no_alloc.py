@@ -23,6 +23,8 @@ CASES = [
     ("splitk-many-slices", (64, 1536, 4096), (40, 264, 2000), (fg.PATH_SPLITK, 1, 7)),
     ("stream-k", (513, 520, 1000), (300, 300, 384), (fg.PATH_MAIN, 16, 40)),
     ("no-workspace", (256, 256, 256), (64, 72, 100), (0, 0, 0)),
+    # the whole-line odd-K kernel: no workspace, two spilled registers in scratch
+    ("odd-k-lines", (528, 304, 3001), (272, 288, 641), (fg.PATH_MAIN, 20, 0)),
 ]
 
 
