@@ -69,7 +69,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "fp8_gemm_channel_amd", "csrc", f)
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_main4w_kernel_square-8192_traffic.md")
 TRACE_SUMMARY = os.path.join(ROOT, "profiles", "fp8g_5shape_bench_kernel_trace.md")
 MAIN_KERNEL_NAMES = {10: "fp8g_main5_kernel", 16: "fp8g_main5_kernel", 19: "fp8g_main4w_kernel",
-                     20: "fp8g_main4wr_kernel"}
+                     20: "fp8g_main4wr_kernel", 27: "fp8g_direct_kernel"}
 
 
 def kernel_source_hash() -> str:

@@ -118,6 +118,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Threads per workgroup of each kernel configuration.
 int64_t block_threads(int32_t path, int32_t variant) {
   if (path == FP8G_PATH_SPLITK) return variant > 20 ? 512 : 256;
+  if (variant == 27) return 64;
   return (variant == 3 || variant == 19 || variant == 20) ? 256 : 512;
 }
 
@@ -151,6 +152,12 @@ int check_dims(int64_t M, int64_t N, int64_t K) {
 // 4096^3, 8192^3, 3072^3 -> 10; 1024 x 8192^2, 1536 x 4096^2, 512 x 12288 x
 // 4096 -> 17; 512 x 8192^2, 768 x 4096^2, 2048^3 -> 18; 128 x 8192^2 -> 3.
 int auto_main_variant(int64_t M, int64_t N, int64_t K) {
+  // Tiny problems (at most 256 blocks of 16 x 16 and two K steps): the
+  // register-tile kernel, one memory round trip with nothing staged in LDS.
+  // Measured on MI355X against variant 3 (interleaved, cold, outputs
+  // identical): 256^3 -2.9%, 240^2 x 256 -11.5%, 144 x 256 x 256 -3.9%, level at
+  // K = 128 and 256 x 384 x 256; slower from K = 384 (+6%) or 320^2 (+4%) on.
+  if (K <= 256 && K % 16 == 0 && cdiv(M, 16) * cdiv(N, 16) <= 256) return 27;
   if (cdiv(M, 128) * cdiv(N, 128) < kNumCUs / 2) return 3;
   struct Cand {
     int variant, bm, bn;
@@ -358,6 +365,8 @@ int plan_impl(int64_t M, int64_t N, int64_t K, int32_t path, int32_t variant, in
     variant = 20;
     p->variant = 20;
   }
+  if (variant == 27 && K % 16 != 0)
+    return fail(FP8G_ERR_INVALID_ARG, "main variant 27 needs K %% 16 == 0 (K=%lld)", (long long)K);
   if (variant == 20 && (K % 2 == 0 || K <= 128))
     return fail(FP8G_ERR_INVALID_ARG, "main variant 20 needs odd K above 128 (K=%lld)", (long long)K);
   if (variant == 20 && !lines_ok)

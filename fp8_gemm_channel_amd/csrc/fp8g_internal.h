@@ -101,6 +101,7 @@ hipError_t launch_main4wr(const MainLaunch &l, hipStream_t stream);          // 
 hipError_t launch_main4wr_epi(const MainLaunch &l, hipStream_t stream);      // variant 20, bias / activation
 hipError_t launch_main_tiles(const MainLaunch &l, hipStream_t stream);       // variants 3, 17, 18
 hipError_t launch_main_tiles_epi(const MainLaunch &l, hipStream_t stream);   // the same, bias / activation
+hipError_t launch_direct(const MainLaunch &l, hipStream_t stream);           // variant 27 (register tiles)
 hipError_t launch_skinny_epi(const SkinnyLaunch &l, hipStream_t stream);     // bias / activation
 hipError_t launch_skinny(const SkinnyLaunch &l, hipStream_t stream);
 hipError_t launch_zero(uint16_t *y, int64_t count, hipStream_t stream, const DispatchEvents &ev);

@@ -66,6 +66,7 @@ static const MainConfig kMainConfigs[] = {
     {18, 128, 128, 128, 4}, // 8 waves, wave tile 64 (m) x 32 (n): grids of 128 x 128 tiles (mid M)
     {19, 256, 256, 128, 2}, // 4 waves, wave tile 128 x 128, ten 16 KiB LDS units (K % 128 == 0)
     {20, 256, 256, 128, 2}, // variant 19 on rows fetched as whole cache lines and realigned (K % 128 != 0)
+    {27, 16, 16, 128, 1},   // one wave per 16 x 16 block, operands straight into registers (tiny problems)
 };
 // ids 1-5: LDS-ring kernel with 4 waves, 21-24: with 8 waves; 16 * row_blocks
 // w rows per workgroup
@@ -98,6 +99,7 @@ hipError_t launch_main(const MainLaunch &l, hipStream_t stream) {
     case 16: return launch_main5(l, stream);
     case 19: return launch_main4w(l, stream);
     case 20: return launch_main4wr(l, stream);
+    case 27: return launch_direct(l, stream);
     case 3:
     case 17:
     case 18: return launch_main_tiles(l, stream);

@@ -2389,6 +2389,78 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4wr_kernel(MainArgs a) {
   main_epilogue_perm<EPI>(acc, a, smem, s_lds, b_lds, m0, n0, mrow, pa, pb, tid);
 }
 
+// ------------------------------------------ main path, register tiles (tiny problems)
+//
+// One wave per 16 x 16 block of y and no LDS: each lane loads its operand bytes
+// straight into the registers V_MFMA_F32_16X16X128_F8F6F4 takes them from (w row
+// n0 + l % 16 as the A operand, x row m0 + l % 16 as the B operand, K bytes
+// [32 (l / 16), + 32) of each 128-byte step: two 16-byte loads per operand and
+// step), up to eight K steps in flight at once, and writes its four results of
+// a row (columns n0 + 4 (l / 16) .. + 3 of row m0 + l % 16, the accumulator
+// layout) as one 8-byte store.  For problems that 64 x 64 tiles cannot spread
+// over the GPU, where a call is a memory round trip plus the launch: nothing is
+// staged in LDS on either side of the MFMAs.  The K steps are added in the same
+// order as in every other main kernel.  Requires K % 16 == 0 (checked by the
+// host): a 16-byte piece of a row then lies wholly before K or wholly past it,
+// and the pieces past it are read as zeros (offset out of range); rows past M
+// or N lie past the tile's buffer range and read as zeros too.
+template <int FMT, bool EPI>
+__global__ __launch_bounds__(64) void fp8g_direct_kernel(MainArgs a) {
+  constexpr int D = 8;  // K steps in flight
+  const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
+  const int tm = (int)blockIdx.x % a.tiles_m, tn = (int)blockIdx.x / a.tiles_m;
+  const int m0 = 16 * tm, n0 = 16 * tn, K = a.K;
+  const v4i rx = make_rsrc(a.x + (size_t)m0 * K, (uint32_t)min(16, a.M - m0) * (uint32_t)K);
+  const v4i rw = make_rsrc(a.w + (size_t)n0 * K, (uint32_t)min(16, a.N - n0) * (uint32_t)K);
+  const v4i rs = make_rsrc(a.scale + n0, (uint32_t)(a.N - n0) * 4u);
+  const uint32_t row = (uint32_t)l16 * (uint32_t)K;
+  const int nk = (K + 127) / 128;
+  // piece h of this lane's K group in step s, from the operand of descriptor r
+  auto piece = [&](const v4i &r, int s, int h) __attribute__((always_inline)) {
+    const int k = 128 * s + 32 * g + 16 * h;
+    return llvm_buffer_load_v4i32(r, k < K ? row + (uint32_t)k : kOut, 0, 0);
+  };
+  // the epilogue's scales (and biases), requested with the first operands
+  const v4f sc = llvm_buffer_load_v4f32(rs, 16u * (uint32_t)g, 0, 0);
+  v4f bi = v4f{0.f, 0.f, 0.f, 0.f};
+  if (EPI && a.bias) bi = llvm_buffer_load_v4f32(make_rsrc(a.bias + n0, (uint32_t)(a.N - n0) * 4u), 16u * (uint32_t)g, 0, 0);
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nk; s0 += D) {
+    v8i A[D], B[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (s0 + i < nk) {
+        const v4i w0 = piece(rw, s0 + i, 0), w1 = piece(rw, s0 + i, 1);
+        const v4i x0 = piece(rx, s0 + i, 0), x1 = piece(rx, s0 + i, 1);
+        A[i] = v8i{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        B[i] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (s0 + i < nk) acc = mfma16<FMT>(A[i], B[i], acc);
+  }
+  const int m = m0 + l16, n = n0 + 4 * g;
+  if (m >= a.M || n >= a.N) return;
+  float z[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    z[e] = acc[e] * sc[e];
+    if constexpr (EPI) {
+      if (a.bias) z[e] += bi[e];  // (no +0 without a bias: it would turn -0 into +0)
+      z[e] = activation_rt(z[e], a.act);
+    }
+  }
+  uint16_t *yr = a.y + (size_t)m * a.N + n;
+  if (a.ystore >= 8 && n + 4 <= a.N) {  // N % 4 == 0 and y 8-byte aligned: the four are one 8-byte piece
+    *(uint2 *)yr = make_uint2(bf16x2_rne(z[0], z[1]), bf16x2_rne(z[2], z[3]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < a.N) yr[e] = (uint16_t)bf16_rne(z[e]);
+  }
+}
+
 // ------------------------------------------------------- launch templates
 // Instantiated by the fp8g_launch_*.hip units.  EPI = the call has a bias or
 // an activation (kernels built without it compile only the plain epilogue).
@@ -2472,6 +2544,16 @@ static hipError_t launch_main4wr_t(const MainLaunch &l, hipStream_t stream) {
   return with_format(l.fmt, [&](auto fmt) {
     constexpr int F = decltype(fmt)::value;
     return dispatch(fp8g_main4wr_kernel<F, EPI>, grid, block, stream, l.ev, a);
+  });
+}
+template <bool EPI>
+static hipError_t launch_direct_t(const MainLaunch &l, hipStream_t stream) {
+  if (l.K % 16 != 0) return hipErrorInvalidValue;
+  const MainArgs a = main_args(l);
+  const dim3 grid((unsigned)(l.tiles_m * l.tiles_n)), block(64);
+  return with_format(l.fmt, [&](auto fmt) {
+    constexpr int F = decltype(fmt)::value;
+    return dispatch(fp8g_direct_kernel<F, EPI>, grid, block, stream, l.ev, a);
   });
 }
 template <bool EPI>

@@ -124,7 +124,10 @@ int fp8_gemm_scaled(const void *x, const void *w, const float *scale, void *y,
  *             19's tiles on rows fetched as whole 128-byte cache lines and
  *             realigned in registers (the default for odd K above 128;
  *             needs odd K > 128, M*K and N*K multiples of 16 and x, w
- *             128-byte aligned, else FP8G_ERR_INVALID_ARG).  Split-K
+ *             128-byte aligned, else FP8G_ERR_INVALID_ARG); 27 = one wave
+ *             per 16x16 block of y with the operands loaded straight into
+ *             the MFMA registers, no LDS (the default for tiny problems: at
+ *             most 256 such blocks and K <= 256; needs K % 16 == 0).  Split-K
  *             path: 1-5 = 16*v w rows per workgroup through per-wave LDS
  *             rings, 4 waves (the default for M > 32); 21-24 = 16*(v-20)
  *             rows with 8 waves (the default for M <= 32).  Row counts are

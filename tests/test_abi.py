@@ -182,6 +182,14 @@ def test_plan_main_kernel_choice():
     assert fg.fp8_gemm_plan(4096, 4096, 127)["variant"] == 10
     assert fg.fp8_gemm_plan(4096, 4096, 129)["variant"] == 20
     assert fg.fp8_gemm_plan(3072, 3072, 3072)["variant"] == 19      # 144 tiles
+    # tiny problems (at most 256 blocks of 16 x 16, K <= 256, K % 16 == 0): register tiles
+    tiny = fg.fp8_gemm_plan(256, 256, 256)
+    assert tiny["variant"] == 27 and (tiny["tile_m"], tiny["tile_n"], tiny["grid"]) == (16, 16, 256)
+    assert fg.fp8_gemm_plan(240, 240, 256)["variant"] == 27
+    for shape in [(256, 256, 384), (320, 320, 256), (256, 256, 255)]:
+        assert fg.fp8_gemm_plan(*shape)["variant"] == 3, shape
+    with pytest.raises(fg.Fp8gError):
+        fg.fp8_gemm_plan_ex(256, 256, 255, fg.PATH_MAIN, 27, 0)     # K % 16 != 0
     forced = fg.fp8_gemm_plan_ex(300, 300, 384, fg.PATH_MAIN, 19, 0)
     assert forced["variant"] == 19 and forced["grid"] == 4 and forced["tile_k"] == 128
     assert fg.fp8_gemm_plan_ex(4096, 4096, 4096, fg.PATH_MAIN, 10, 0)["variant"] == 10

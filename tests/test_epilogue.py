@@ -78,6 +78,16 @@ def test_main_cache_line_rows_all_formats(fmts):
     _case(256, 256, 4127, fg.ACT_RELU, *fmts, path=fg.PATH_MAIN, variant=20)
 
 
+# the register-tile kernel (K % 16 == 0), every format and activation, with and
+# without a bias, ragged edges and partial row pieces
+@pytest.mark.parametrize("fmts", FORMATS, ids=lambda f: f"x{f[0]}w{f[1]}")
+def test_main_register_tiles_all_formats(fmts):
+    _case(300, 520, 256, fg.ACT_GELU_TANH, *fmts, path=fg.PATH_MAIN, variant=27)
+    _case(129, 70, 1040, fg.ACT_SILU, *fmts, path=fg.PATH_MAIN, variant=27)
+    _case(33, 301, 48, fg.ACT_RELU, *fmts, path=fg.PATH_MAIN, variant=27)
+    _case(64, 64, 128, fg.ACT_RELU, *fmts, path=fg.PATH_MAIN, variant=27, with_bias=False)
+
+
 # the one-wave-per-SIMD kernel (K % 128 == 0), every format and activation
 @pytest.mark.parametrize("fmts", FORMATS, ids=lambda f: f"x{f[0]}w{f[1]}")
 def test_main_one_wave_per_simd_all_formats(fmts):

@@ -12,7 +12,7 @@ from tests.gpu_util import compare, run, say
 
 pytestmark = pytest.mark.gpu
 
-MAIN_VARIANTS = [0, 3, 10, 16, 17, 18, 19, 20]
+MAIN_VARIANTS = [0, 3, 10, 16, 17, 18, 19, 20, 27]
 SPLITK_VARIANTS = [0, 1, 2, 3, 4, 5, 21, 22, 23, 24]
 
 

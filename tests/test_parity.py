@@ -38,6 +38,29 @@ def test_main_variants_full(variant, shape):
     _full_case(*shape, path=fg.PATH_MAIN, variant=variant)
 
 
+# ------------------------------- main path, register tiles (variant 27, K % 16 == 0) --
+# One wave per 16 x 16 block, operands loaded straight into the MFMA registers:
+# one K piece (16), a part step, one to many steps (more than the eight kept in
+# flight: 2048 is sixteen), ragged M and N (partial 8-byte row pieces, N odd),
+# single rows and columns.
+V27_SHAPES = [(256, 256, 256), (1, 1, 16), (17, 33, 48), (16, 16, 128), (300, 520, 1024), (65, 70, 2048),
+              (255, 257, 144), (64, 1000, 1040), (33, 7, 4096), (128, 130, 272)]
+
+
+@pytest.mark.parametrize("shape", V27_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_main_register_tiles(shape):
+    """Variant 27 against the oracle, every element, and bit for bit against
+    variant 3 (both add the same 128-byte K steps with the same instruction in
+    the same order)."""
+    M, N, K = shape
+    x, w, s = synth.fp8_inputs(M, N, K, seed=27)
+    say(f"v27 {shape}")
+    a = run(x, w, s, path=fg.PATH_MAIN, variant=27)
+    compare(a, oracle.gemm_scaled(x, w, s), f"{shape} v27")
+    b = run(x, w, s, path=fg.PATH_MAIN, variant=3)
+    assert np.array_equal(a, b), "variant 27 differs from variant 3"
+
+
 # ------------------------- main path, one wave per SIMD (variant 19, K % 128 == 0) --
 # One to five 128-byte K steps (the guarded last three steps alone, then with
 # the branch-free body before them), rows past M and N, a long K.
