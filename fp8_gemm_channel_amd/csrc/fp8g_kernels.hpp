@@ -1823,9 +1823,10 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
   // so the body has no branches; the last three steps take the guarded body.
   // In each quadrant the eight reads go out with its first eight MFMAs (so they
   // have landed by the barrier that retires their unit) and its four DMAs with
-  // MFMAs 1, 5, 9, 13; the MFMAs take their blocks in the order the previous
-  // quadrant read them, so every block is read at least eight MFMAs before its
-  // first use.
+  // MFMAs 2, 6, 10, 14 (measured on MI355X, interleaved: 0.2-1.0% faster than
+  // with MFMAs 1, 5, 9, 13 on five shapes); the MFMAs take their blocks in the
+  // order the previous quadrant read them, so every block is read at least
+  // eight MFMAs before its first use.
   auto step = [&](const int s, auto steady) __attribute__((always_inline)) {
     constexpr bool STEADY = decltype(steady)::value;
     const bool more = STEADY || s + 1 < nk;
@@ -1838,7 +1839,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
       const int mb = q >> 2, nb = q & 3;
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
       if (q < 8) rd16(u_xh(s), ob, q >> 1, q & 1, B[4 + (q >> 1)]);
-      if ((q & 3) == 1 && more2) issue_l(s + 2, q >> 2);
+      if ((q & 3) == 2 && more2) issue_l(s + 2, q >> 2);
       __builtin_amdgcn_sched_barrier(0);  // keep the spread as written
     }
     // Q2: w L x x H (x block-major); read w H (s) into A[4..7]; DMA the other
@@ -1848,7 +1849,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
       const int mb = 4 + (q >> 2), nb = q & 3;
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
       if (q < 8) rd16(u_wh(s), oa, q >> 1, q & 1, A[4 + (q >> 1)]);
-      if ((q & 3) == 1 && more2) issue_l(s + 2, 4 + (q >> 2));
+      if ((q & 3) == 2 && more2) issue_l(s + 2, 4 + (q >> 2));
       __builtin_amdgcn_sched_barrier(0);
     }
     if (more) {
@@ -1866,7 +1867,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
       const int nb = 4 + (q >> 2), mb = q & 3;
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
       if (more && q < 8) rd16(u_wl(s + 1), oa, q >> 1, q & 1, A[q >> 1]);
-      if ((q & 3) == 1 && more3) issue_h(s + 3, q >> 2);
+      if ((q & 3) == 2 && more3) issue_h(s + 3, q >> 2);
       __builtin_amdgcn_sched_barrier(0);
     }
     // Q4: w H x x H; read x L (s + 1) into B[0..3]; DMA the other half of the
@@ -1876,7 +1877,7 @@ __global__ __launch_bounds__(256, 1) void fp8g_main4w_kernel(MainArgs a) {
       const int nb = 4 + (q >> 2), mb = 4 + (q & 3);
       acc[nb][mb] = mfma16<FMT>(A[nb], B[mb], acc[nb][mb]);
       if (more && q < 8) rd16(u_xl(s + 1), ob, q >> 1, q & 1, B[q >> 1]);
-      if ((q & 3) == 1 && more3) issue_h(s + 3, 4 + (q >> 2));
+      if ((q & 3) == 2 && more3) issue_h(s + 3, 4 + (q >> 2));
       __builtin_amdgcn_sched_barrier(0);
     }
     if (more) {
