@@ -438,6 +438,11 @@ def main() -> int:
             if not args.no_flush:
                 flush.fill_(i)
             fg.fp8_gemm(xd, wd, sd, out=yd, stream=stream, events=(k0, k1))
+            # wait for the attached stop event before queuing more work: with the
+            # next 512 MiB rewrite already queued behind the call, the stop
+            # timestamp came out later than the kernel's end (256^3: 4.74 us
+            # against 4.12-4.20 with the wait; rocprofv3 puts the kernel at 3.9)
+            k1.synchronize()
             if not args.no_flush:
                 flush.fill_(i + 1)
             e0.record(stream)
